@@ -1,0 +1,226 @@
+"""CPU oracle for one rank's share of context-parallel (Ring / Ulysses) attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports, calls or links
+this package; only the tests, ``__graft_entry__.smoke()`` and the benchmark's
+CPU-baseline leg use it. It shares no code with the HIP path (no kernels,
+headers, helpers or constants); the two meet only in the seeded inputs of the
+``workloads`` module, which holds none of the method's arithmetic.
+
+Everything here is plain numpy in float64 on exactly the values the GPU sees
+(bfloat16 inputs are upcast losslessly). It is written for a reader to check
+against the pages by eye: no blocking, fusion or reordering beyond what each
+definition states.
+
+Sources (diffusers v0.43.0 documentation pages):
+  * "Paralelismo de contexto" (context-parallelism guide, Portuguese),
+    sections "Atenção em Anel", "Atenção Ulysses", "Ring Anything Attention";
+  * "Paralelismo" (parallelism API reference, Spanish), section
+    "ContextParallelConfig", parameters ``ring_degree``, ``convert_to_fp32``,
+    ``rotate_method``, ``ring_anything``;
+  * "Inferencia distribuida" (distributed-inference guide, Spanish), sections
+    "Ring Attention", "Ulysses Attention".
+
+Readings taken where the pages are silent (each is listed in the design doc too):
+  * the merge of per-block partials is the exact log-sum-exp recombination,
+    the only merge under which a full ring equals full attention;
+  * the softmax scale is 1/sqrt(D) and LSE is the natural log of
+    sum_j exp(scale * q.k_j);
+  * the Ulysses regroup sends head group g to token slot g (contiguous head
+    groups, token chunks concatenated in rank order).
+
+Pins: every function here is checked by the CPU tests against something other
+than itself -- a pure-Python brute force, closed forms, a library attention
+routine, hand-computed golden values under ``tests/golden/`` and invariants
+(ring over any split == single pass, shift/permutation invariance, regroup
+round trip, a multi-rank Ulysses simulation). No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "attention",
+    "block_attention",
+    "lse_merge",
+    "ring_attention",
+    "ulysses_regroup",
+    "ulysses_regroup_inv",
+    "brute_attention",
+]
+
+_F64 = np.float64
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+              row_chunk: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+    """Full non-causal softmax attention, plus the log-sum-exp of each row.
+
+    Layout is [B, S, H, D] for q (Sq rows), k and v (Skv rows); returns
+    O [B, Sq, H, D] and LSE [B, H, Sq], both float64.
+
+    Definition (one (b, h) pair, one query row q_i):
+        x_ij  = scale * <q_i, k_j>
+        LSE_i = ln sum_j exp(x_ij)
+        O_i   = sum_j exp(x_ij - LSE_i) * v_j
+    evaluated with the row maximum subtracted before exponentiating, which is
+    the same value up to rounding. Each rank of a ring computes exactly this
+    between its local Q and one K/V block ("Paralelismo" API reference,
+    ContextParallelConfig, ``ring_degree``), and a full ring must reproduce
+    it over all tokens ("Paralelismo de contexto", "Atenção em Anel").
+
+    An empty key set (Skv == 0) gives O = 0 and LSE = -inf: the sum over no
+    terms is zero, so its log is -inf and it carries no weight in a merge.
+    """
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    assert k.shape == (B, Skv, H, D) and v.shape == (B, Skv, H, D), (q.shape, k.shape, v.shape)
+    out = np.zeros((B, Sq, H, D), dtype=_F64)
+    lse = np.empty((B, H, Sq), dtype=_F64)
+    if Skv == 0:
+        lse[...] = -np.inf
+        return out, lse
+    for b in range(B):
+        for h in range(H):
+            kh = np.asarray(k[b, :, h, :], dtype=_F64)  # [Skv, D]
+            vh = np.asarray(v[b, :, h, :], dtype=_F64)
+            for r0 in range(0, Sq, row_chunk):
+                r1 = min(Sq, r0 + row_chunk)
+                qh = np.asarray(q[b, r0:r1, h, :], dtype=_F64)  # [rows, D]
+                x = scale * (qh @ kh.T)                       # scores [rows, Skv]
+                m = x.max(axis=1, keepdims=True)
+                e = np.exp(x - m)
+                l = e.sum(axis=1, keepdims=True)
+                out[b, r0:r1, h, :] = (e @ vh) / l
+                lse[b, h, r0:r1] = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def block_attention(q: np.ndarray, k_block: np.ndarray, v_block: np.ndarray,
+                    scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Partial attention of the local Q against one K/V block.
+
+    Each block yields a partial output and its LSE; ``convert_to_fp32`` keeps
+    both in float32 on the GPU so that the merge is stable ("Paralelismo",
+    ContextParallelConfig, ``convert_to_fp32``). Here both are float64.
+    A Ring Anything block is first cut back to its true length
+    ("Paralelismo de contexto", "Ring Anything Attention"); callers pass the
+    already-cut block, whose length may be zero.
+    """
+    return attention(q, k_block, v_block, scale)
+
+
+def lse_merge(o_a: np.ndarray, lse_a: np.ndarray, o_b: np.ndarray,
+              lse_b: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge two partial results of the same queries over disjoint key sets.
+
+    With O in [B, S, H, D] and LSE in [B, H, S]:
+        M   = max(LSE_a, LSE_b)
+        w_a = exp(LSE_a - M),  w_b = exp(LSE_b - M)
+        LSE = M + ln(w_a + w_b)
+        O   = (w_a * O_a + w_b * O_b) / (w_a + w_b)
+    which is attention over the union of the two key sets. The pages name
+    the merged quantities (partial output and LSE, kept in float32) but do
+    not print the formula; this is the exact recombination
+    ("Paralelismo", ContextParallelConfig, ``convert_to_fp32``).
+
+    A side with LSE = -inf (no keys) gets weight 0. If both are -inf the
+    result is O = 0, LSE = -inf.
+    """
+    lse_a = np.asarray(lse_a, dtype=_F64)
+    lse_b = np.asarray(lse_b, dtype=_F64)
+    m = np.maximum(lse_a, lse_b)
+    both_empty = np.isneginf(m)
+    m_safe = np.where(both_empty, 0.0, m)
+    w_a = np.where(np.isneginf(lse_a), 0.0, np.exp(lse_a - m_safe))
+    w_b = np.where(np.isneginf(lse_b), 0.0, np.exp(lse_b - m_safe))
+    tot = w_a + w_b
+    with np.errstate(divide="ignore"):
+        lse = np.where(both_empty, -np.inf, m_safe + np.log(np.where(both_empty, 1.0, tot)))
+    # weights are [B, H, S]; outputs are [B, S, H, D]
+    wa = np.transpose(w_a, (0, 2, 1))[..., None]
+    wb = np.transpose(w_b, (0, 2, 1))[..., None]
+    den = np.transpose(np.where(both_empty, 1.0, tot), (0, 2, 1))[..., None]
+    o = (wa * np.asarray(o_a, dtype=_F64) + wb * np.asarray(o_b, dtype=_F64)) / den
+    return o, lse
+
+
+def ring_attention(q: np.ndarray, k_blocks: Sequence[np.ndarray], v_blocks: Sequence[np.ndarray],
+                   scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One rank's share of Ring Attention with all K/V blocks resident.
+
+    The rank attends its local Q to each K/V block in turn and folds the
+    partials into an accumulator, block 0 first ("Paralelismo de contexto",
+    "Atenção em Anel": after a full loop every rank has seen the K/V of all
+    tokens; "Paralelismo", ContextParallelConfig, ``rotate_method`` --
+    all-gather, so every block is present before the loop).
+    """
+    assert len(k_blocks) == len(v_blocks) and len(k_blocks) >= 1
+    o, lse = block_attention(q, k_blocks[0], v_blocks[0], scale)
+    for kb, vb in zip(k_blocks[1:], v_blocks[1:]):
+        o_i, lse_i = block_attention(q, kb, vb, scale)
+        o, lse = lse_merge(o, lse, o_i, lse_i)
+    return o, lse
+
+
+def ulysses_regroup(x: np.ndarray, degree: int) -> np.ndarray:
+    """Sequence-sharded -> head-sharded layout of one rank (all-to-all, loopback).
+
+    x is [B, S_local, H, D]. The first all-to-all leaves each rank with every
+    token for a subset of heads ("Paralelismo de contexto", "Atenção Ulysses").
+    With the exchange replaced by a loopback, head group g (heads
+    g*H/P .. (g+1)*H/P - 1) of this rank's tokens becomes token chunk g:
+        out[b, g*S_local + s, h, d] = x[b, s, g*(H/P) + h, d]
+    Result: [B, P*S_local, H/P, D]. A pure permutation: bit-exact.
+    """
+    B, S_l, H, D = x.shape
+    assert H % degree == 0
+    Hl = H // degree
+    return np.ascontiguousarray(
+        x.reshape(B, S_l, degree, Hl, D).transpose(0, 2, 1, 3, 4).reshape(B, degree * S_l, Hl, D))
+
+
+def ulysses_regroup_inv(y: np.ndarray, degree: int) -> np.ndarray:
+    """Head-sharded -> sequence-sharded: the second all-to-all, regrouping by token.
+
+    y is [B, P*S_local, H/P, D]; inverse of ``ulysses_regroup``:
+        out[b, s, g*(H/P) + h, d] = y[b, g*S_local + s, h, d]
+    """
+    B, S, Hl, D = y.shape
+    assert S % degree == 0
+    S_l = S // degree
+    return np.ascontiguousarray(
+        y.reshape(B, degree, S_l, Hl, D).transpose(0, 2, 1, 3, 4).reshape(B, S_l, degree * Hl, D))
+
+
+def brute_attention(q, k, v, scale: float):
+    """Pure-Python attention with math.exp / math.log, for tiny shapes only.
+
+    Same definition as ``attention`` with nothing vectorised and no max
+    subtraction (tiny inputs cannot overflow), so it shares no evaluation
+    order with the numpy version. Returns nested lists O[b][s][h][d],
+    LSE[b][h][s].
+    """
+    B, Sq, H, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Skv = len(k[0])
+    O = [[[[0.0] * D for _ in range(H)] for _ in range(Sq)] for _ in range(B)]
+    L = [[[0.0] * Sq for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            for i in range(Sq):
+                w = []
+                for j in range(Skv):
+                    dot = 0.0
+                    for d in range(D):
+                        dot += float(q[b][i][h][d]) * float(k[b][j][h][d])
+                    w.append(math.exp(scale * dot))
+                tot = sum(w)
+                L[b][h][i] = math.log(tot) if Skv else -math.inf
+                for d in range(D):
+                    acc = 0.0
+                    for j in range(Skv):
+                        acc += w[j] * float(v[b][j][h][d])
+                    O[b][i][h][d] = acc / tot if Skv else 0.0
+    return O, L
