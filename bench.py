@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark: one rank's share of ring-block attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: for a ring workload, attention of the local Q
+against every K/V block with each float32 partial merged by LSE rescaling
+(cp_ring_attention); for the Ulysses workload, the head/token regroup of Q, K
+and V, attention over all tokens for the local heads, and the inverse regroup
+of the output.
+
+Prints ONE JSON line on stdout. ``value`` is attention TFLOP/s over the whole
+step, counting 4*B*H*Sq*Skv*D flops; ``roofline`` prices the dominant kernel
+(block attention) from its per-launch duration measured with HIP events on
+the launch stream; ``cpu_baseline`` times the float64 CPU oracle on a bounded
+sample of the same workload on this host.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "ring-block attention TFLOP/s (fwd+LSE merge) and % of MI355X bf16 MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA bf16; fp32 vector ALU
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "flux1024_ring2_bf16"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=[w.name for w in workloads.WORKLOADS])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle baseline sample (0 disables it)")
+    ap.add_argument("--separate-merge", action="store_true",
+                    help="merge partials with the standalone merge kernel instead of the fused epilogue")
+    return ap.parse_args()
+
+
+class Problem:
+    """Device-resident inputs and outputs of one workload, and its step."""
+
+    def __init__(self, w: workloads.Workload, separate_merge: bool):
+        import torch
+        import context_attention_dits_amd as cp
+        self.cp, self.torch, self.w = cp, torch, w
+        inp = workloads.make_inputs(w)
+        self.inp = inp
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        to = lambda x: torch.from_numpy(x).to(tdt).cuda()  # noqa: E731
+        self.q, self.k, self.v = to(inp.q), to(inp.k), to(inp.v)
+        B, D = w.B, w.D
+        self.flags = cp.CP_RING_SEPARATE_MERGE if separate_merge else 0
+        if len(set(w.block_lens)) > 1:
+            self.flags |= cp.CP_RING_ANYTHING
+        if w.ulysses_degree > 1:
+            P = w.ulysses_degree
+            shp = (B, P * w.S_local, w.H // P, D)
+            self.qr = torch.empty(shp, dtype=tdt, device="cuda")
+            self.kr = torch.empty(shp, dtype=tdt, device="cuda")
+            self.vr = torch.empty(shp, dtype=tdt, device="cuda")
+            self.back = torch.empty((B, w.S_local, w.H, D), dtype=torch.float32, device="cuda")
+            q_att, k_att, v_att = self.qr, self.kr, self.vr
+        else:
+            q_att, k_att, v_att = self.q, self.k, self.v
+        self.q_att = q_att
+        offs = workloads.block_offsets(w.block_lens)
+        self.kb = [k_att[:, o:o + L] for o, L in zip(offs, w.block_lens)]
+        self.vb = [v_att[:, o:o + L] for o, L in zip(offs, w.block_lens)]
+        H = w.attn_H
+        self.out = torch.empty((B, w.Sq, H, D), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((B, H, w.Sq), dtype=torch.float32, device="cuda")
+        nbytes = cp.cp_ring_attention_workspace_size(B, H, w.Sq, D, self.flags)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+
+    def step(self):
+        cp, w = self.cp, self.w
+        if w.ulysses_degree > 1:
+            P = w.ulysses_degree
+            cp.cp_ulysses_regroup(self.q, self.qr, P, cp.CP_REGROUP_SEQ_TO_HEAD)
+            cp.cp_ulysses_regroup(self.k, self.kr, P, cp.CP_REGROUP_SEQ_TO_HEAD)
+            cp.cp_ulysses_regroup(self.v, self.vr, P, cp.CP_REGROUP_SEQ_TO_HEAD)
+        cp.cp_ring_attention(self.q_att, self.kb, self.vb, self.out, self.lse, scale=w.scale,
+                             flags=self.flags, workspace=self.ws)
+        if w.ulysses_degree > 1:
+            cp.cp_ulysses_regroup(self.out, self.back, w.ulysses_degree, cp.CP_REGROUP_HEAD_TO_SEQ)
+
+    def time_block_kernels(self, reps: int):
+        """Average duration of one block-attention launch, as the ring issues them.
+
+        Block 0 is written, later blocks are merged in by the kernel epilogue;
+        each launch is bracketed by HIP events on the stream it runs on.
+        """
+        torch, cp, w = self.torch, self.cp, self.w
+        stream = torch.cuda.current_stream()
+        durs, flops = [], []
+        for _ in range(reps):
+            for i, (kb, vb) in enumerate(zip(self.kb, self.vb)):
+                if kb.shape[1] == 0:
+                    continue
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                cp.cp_attn_block_fwd(self.q_att, kb, vb, self.out, self.lse, scale=w.scale,
+                                     flags=cp.CP_BLOCK_ACCUMULATE if i > 0 else 0)
+                e1.record(stream)
+                durs.append((e0, e1))
+                flops.append(4 * w.B * w.attn_H * w.Sq * kb.shape[1] * w.D)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in durs]
+        return sum(ms) / len(ms), sum(flops) / len(flops)
+
+
+def cpu_baseline(w: workloads.Workload, inp, target_s: float):
+    """Time the float64 oracle on whole heads of the same workload, ~target_s of CPU work."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001 - threadpoolctl is optional
+        cores = 1
+    if w.ulysses_degree > 1:
+        P = w.ulysses_degree
+        q, k, v = (oracle.ulysses_regroup(x, P) for x in (inp.q, inp.k, inp.v))
+    else:
+        q, k, v = inp.q, inp.k, inp.v
+    offs = workloads.block_offsets(w.block_lens)
+    H = w.attn_H
+
+    def run(h0, h1):
+        kb = [k[:, o:o + L, h0:h1] for o, L in zip(offs, w.block_lens)]
+        vb = [v[:, o:o + L, h0:h1] for o, L in zip(offs, w.block_lens)]
+        t = time.perf_counter()
+        oracle.ring_attention(q[:, :, h0:h1], kb, vb, w.scale)
+        return time.perf_counter() - t
+
+    t1 = run(0, 1)  # one head to size the sample
+    n_heads = int(max(1, min(H, math.floor(target_s / max(t1, 1e-6)))))
+    t = run(0, n_heads) if n_heads > 1 else t1
+    flops = 4 * w.B * n_heads * w.Sq * w.Skv * w.D
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_heads} of {H} heads x B={w.B} x Sq={w.Sq} x Skv={w.Skv} (all blocks, merged), "
+                      f"numpy float64, {t:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    w = workloads.by_name(args.workload)
+    log(f"[bench] workload {w.name}: B={w.B} H={w.attn_H} D={w.D} Sq={w.Sq} blocks={list(w.block_lens)}")
+    prob = Problem(w, args.separate_merge)
+
+    for _ in range(args.warmup):
+        prob.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        prob.step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step)")
+    tflops = w.flops / (ms_step * 1e-3) / 1e12
+
+    k_ms, k_flops = prob.time_block_kernels(max(5, min(args.steps, 50)))
+    achieved = k_flops / (k_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log(f"[bench] block kernel: {k_ms * 1e3:.1f} us/launch, {achieved:.1f} TFLOP/s ({achieved / peak:.1%} of {peak})")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("[bench] timing the CPU oracle ...")
+        cpu = cpu_baseline(w, prob.inp, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded i.i.d. N(0,1) Q/K/V (bf16-rounded), FLUX-like shapes",
+        "config": {"workload": w.name, "B": w.B, "H": w.attn_H, "D": w.D, "Sq": w.Sq,
+                   "block_lens": list(w.block_lens), "ring_degree": w.ring_degree,
+                   "ulysses_degree": w.ulysses_degree,
+                   "merge": "separate" if args.separate_merge else "fused",
+                   "pct_of_bf16_peak": round(100 * tflops / PEAK_TFLOPS["bf16"], 2)},
+        "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel",
+                     "us_per_launch": round(k_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

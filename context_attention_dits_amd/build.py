@@ -1,0 +1,88 @@
+"""Build the gfx950 HIP library ``libcpattn.so`` in-tree with hipcc.
+
+Usage: ``python -m context_attention_dits_amd.build [--out PATH] [-DNAME=VALUE ...]``.
+Every call compiles from source (no up-to-date check). Objects go to
+``context_attention_dits_amd/_build/``; the shared library lands next to this
+file unless ``--out`` says otherwise. ``-D`` definitions select kernel tile
+variants (e.g. ``-DCP_FWD_QB=2``) for a library built at another path.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+from typing import Dict, List, Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libcpattn.so"
+SOURCES = ["api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "lse_merge.hip", "regroup.hip"]
+ARCH = "gfx950"
+
+# Packed-fp32 VALU instructions are left out of the generated code on purpose.
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (expected /opt/rocm/bin/hipcc)")
+
+
+def build(out: Optional[str] = None, defines: Optional[Dict[str, str]] = None,
+          build_dir: Optional[str] = None, verbose: bool = False) -> str:
+    out = out or os.path.join(PKG, LIB_NAME)
+    tag = "_".join(f"{k}{v}" for k, v in sorted((defines or {}).items())) or "default"
+    build_dir = build_dir or os.path.join(PKG, "_build", tag)
+    os.makedirs(build_dir, exist_ok=True)
+    dflags: List[str] = [f"-D{k}={v}" for k, v in sorted((defines or {}).items())]
+    cc = hipcc()
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        cmd = [cc, *HIPCC_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = out + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--out", default=None)
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args(argv)
+    defs = {}
+    for d in a.defines:
+        k, _, v = d.partition("=")
+        defs[k] = v or "1"
+    path = build(a.out, defs, verbose=a.verbose)
+    print(path)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,276 @@
+// C-ABI of the library: host-side validation, launch selection and the ring
+// loop. Every check runs before anything is enqueued, so a failing call
+// launches nothing. See include/cp_attn.h for the contract of each entry point.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "cp_attn.h"
+#include "kernels.h"
+
+namespace {
+
+using cpattn::Strides;
+
+thread_local std::string g_err;
+
+cp_status_t fail(cp_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+cp_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return CP_OK;
+  return fail(CP_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+const char* kSupported = "supported: dtype CP_F32 (0) or CP_BF16 (1), head dim D = 64 or 128";
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Resolve a host stride triple (NULL = contiguous [B, S, H, D]).
+Strides resolve(const int64_t* s, int S, int H, int D) {
+  if (s == nullptr) return Strides{(int64_t)S * H * D, (int64_t)H * D, (int64_t)D};
+  return Strides{s[0], s[1], s[2]};
+}
+
+cp_status_t check_strides(const char* name, Strides st, int elem_bytes, int S, int H, int D) {
+  if (st.b < 0 || st.s < 0 || st.h < 0)
+    return fail(CP_ERR_INVALID_ARG, "%s: strides must be non-negative (got b=%lld s=%lld h=%lld)",
+                name, (long long)st.b, (long long)st.s, (long long)st.h);
+  if ((st.b * elem_bytes) % 16 || (st.s * elem_bytes) % 16 || (st.h * elem_bytes) % 16)
+    return fail(CP_ERR_UNSUPPORTED,
+                "%s: every stride times the element size must be a multiple of 16 bytes", name);
+  // Rows of one head must not overlap each other along D.
+  if (H > 1 && st.h < D)
+    return fail(CP_ERR_INVALID_ARG, "%s: head stride %lld smaller than D=%d", name, (long long)st.h, D);
+  if (S > 1 && st.s < D)
+    return fail(CP_ERR_INVALID_ARG, "%s: sequence stride %lld smaller than D=%d", name,
+                (long long)st.s, D);
+  return CP_OK;
+}
+
+int elem_size(int dtype) { return dtype == CP_BF16 ? 2 : 4; }
+
+// Arguments common to block attention and the ring; K/V lengths checked by callers.
+cp_status_t check_common(const void* q, Strides qs, Strides kvs, int dtype, int B, int H, int D,
+                         int Sq, float scale, const float* out, Strides os, const float* lse) {
+  if (dtype != CP_F32 && dtype != CP_BF16)
+    return fail(CP_ERR_UNSUPPORTED, "dtype %d is not supported; %s", dtype, kSupported);
+  if (D != 64 && D != 128)
+    return fail(CP_ERR_UNSUPPORTED, "head dim D=%d is not supported; %s", D, kSupported);
+  if (B < 0 || H < 0 || Sq < 0)
+    return fail(CP_ERR_INVALID_ARG, "sizes must be non-negative (B=%d H=%d Sq=%d)", B, H, Sq);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(CP_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (B == 0 || H == 0 || Sq == 0) return CP_OK;
+  if (q == nullptr || out == nullptr || lse == nullptr)
+    return fail(CP_ERR_INVALID_ARG, "q, out and lse must be non-null");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4))
+    return fail(CP_ERR_UNSUPPORTED, "q and out must be 16-byte aligned, lse 4-byte aligned");
+  const int es = elem_size(dtype);
+  cp_status_t st;
+  if ((st = check_strides("q", qs, es, Sq, H, D)) != CP_OK) return st;
+  if ((st = check_strides("k/v", kvs, es, 2, H, D)) != CP_OK) return st;
+  if ((st = check_strides("out", os, 4, Sq, H, D)) != CP_OK) return st;
+  return CP_OK;
+}
+
+cp_status_t check_kv(const void* k, const void* v, int Skv) {
+  if (Skv < 0) return fail(CP_ERR_INVALID_ARG, "K/V length must be non-negative (got %d)", Skv);
+  if (Skv == 0) return CP_OK;
+  if (k == nullptr || v == nullptr) return fail(CP_ERR_INVALID_ARG, "k and v must be non-null");
+  if (!aligned(k, 16) || !aligned(v, 16))
+    return fail(CP_ERR_UNSUPPORTED, "k and v must be 16-byte aligned");
+  return CP_OK;
+}
+
+// One validated block: launches the attention (overwrite or accumulate) or the empty fill.
+cp_status_t run_block(const void* q, Strides qs, const void* k, const void* v, Strides kvs, int dtype,
+                      int B, int H, int D, int Sq, int Skv, float scale, bool accumulate, float* out,
+                      Strides os, float* lse, hipStream_t stream) {
+  if (Skv == 0) {
+    if (accumulate) return CP_OK;
+    return hip_status(cpattn::launch_fill_empty(out, os, lse, B, H, Sq, D, stream), "fill_empty");
+  }
+  cpattn::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+  a.qs = qs; a.kvs = kvs; a.os = os;
+  a.B = B; a.H = H; a.D = D; a.Sq = Sq; a.Skv = Skv;
+  a.scale = scale;
+  a.accumulate = accumulate;
+  if (dtype == CP_BF16) return hip_status(cpattn::launch_attn_fwd_bf16(a, stream), "attn_fwd_bf16");
+  return hip_status(cpattn::launch_attn_fwd_f32(a, stream), "attn_fwd_f32");
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t partial_bytes(int B, int H, int Sq, int D) {
+  return align_up((size_t)B * Sq * H * D * sizeof(float), 256) + align_up((size_t)B * H * Sq * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+int cp_abi_version(void) { return CP_ATTN_ABI_VERSION; }
+
+const char* cp_last_error(void) { return g_err.c_str(); }
+
+cp_status_t cp_attn_block_fwd(const void* q, const int64_t* q_strides, const void* k, const void* v,
+                              const int64_t* kv_strides, int dtype, int B, int H, int D, int Sq,
+                              int Skv, float scale, unsigned flags, float* out,
+                              const int64_t* out_strides, float* lse, void* stream) {
+  if (flags & ~CP_BLOCK_ACCUMULATE)
+    return fail(CP_ERR_INVALID_ARG, "cp_attn_block_fwd: unknown flags 0x%x", flags);
+  const Strides qs = resolve(q_strides, Sq, H, D);
+  const Strides kvs = resolve(kv_strides, Skv, H, D);
+  const Strides os = resolve(out_strides, Sq, H, D);
+  cp_status_t st = check_common(q, qs, kvs, dtype, B, H, D, Sq, scale, out, os, lse);
+  if (st != CP_OK) return st;
+  if (B == 0 || H == 0 || Sq == 0) return CP_OK;
+  if ((st = check_kv(k, v, Skv)) != CP_OK) return st;
+  return run_block(q, qs, k, v, kvs, dtype, B, H, D, Sq, Skv, scale, (flags & CP_BLOCK_ACCUMULATE) != 0,
+                   out, os, lse, static_cast<hipStream_t>(stream));
+}
+
+cp_status_t cp_lse_merge(float* out_acc, float* lse_acc, const float* out_blk, const float* lse_blk,
+                         const int64_t* acc_strides, const int64_t* blk_strides, int B, int H, int Sq,
+                         int D, void* stream) {
+  if (D != 64 && D != 128)
+    return fail(CP_ERR_UNSUPPORTED, "cp_lse_merge: head dim D=%d is not supported (D = 64 or 128)", D);
+  if (B < 0 || H < 0 || Sq < 0)
+    return fail(CP_ERR_INVALID_ARG, "cp_lse_merge: sizes must be non-negative");
+  if (B == 0 || H == 0 || Sq == 0) return CP_OK;
+  if (!out_acc || !lse_acc || !out_blk || !lse_blk)
+    return fail(CP_ERR_INVALID_ARG, "cp_lse_merge: pointers must be non-null");
+  if (!aligned(out_acc, 16) || !aligned(out_blk, 16) || !aligned(lse_acc, 4) || !aligned(lse_blk, 4))
+    return fail(CP_ERR_UNSUPPORTED, "cp_lse_merge: outputs must be 16-byte aligned, LSE 4-byte");
+  if (out_acc == out_blk || lse_acc == lse_blk)
+    return fail(CP_ERR_INVALID_ARG, "cp_lse_merge: accumulator and block must be distinct buffers");
+  const Strides as = resolve(acc_strides, Sq, H, D);
+  const Strides bs = resolve(blk_strides, Sq, H, D);
+  cp_status_t st;
+  if ((st = check_strides("out_acc", as, 4, Sq, H, D)) != CP_OK) return st;
+  if ((st = check_strides("out_blk", bs, 4, Sq, H, D)) != CP_OK) return st;
+  return hip_status(cpattn::launch_lse_merge(out_acc, lse_acc, out_blk, lse_blk, as, bs, B, H, Sq, D,
+                                             static_cast<hipStream_t>(stream)),
+                    "lse_merge");
+}
+
+size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned flags) {
+  if (!(flags & CP_RING_SEPARATE_MERGE) || B <= 0 || H <= 0 || Sq <= 0 || D <= 0) return 0;
+  return partial_bytes(B, H, Sq, D);
+}
+
+cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const void* const* k_blocks,
+                              const void* const* v_blocks, const int64_t* kv_strides,
+                              const int* block_len, int ring_degree, int dtype, int B, int H, int D,
+                              int Sq, float scale, unsigned flags, float* out,
+                              const int64_t* out_strides, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (flags & ~(CP_RING_ANYTHING | CP_RING_SEPARATE_MERGE))
+    return fail(CP_ERR_INVALID_ARG, "cp_ring_attention: unknown flags 0x%x", flags);
+  if (ring_degree < 1)
+    return fail(CP_ERR_INVALID_ARG, "cp_ring_attention: ring_degree must be >= 1 (got %d)", ring_degree);
+  if (!k_blocks || !v_blocks || !block_len)
+    return fail(CP_ERR_INVALID_ARG, "cp_ring_attention: block arrays must be non-null");
+  const bool anything = (flags & CP_RING_ANYTHING) != 0;
+  int64_t total = 0;
+  for (int i = 0; i < ring_degree; ++i) {
+    if (block_len[i] < 0)
+      return fail(CP_ERR_INVALID_ARG, "cp_ring_attention: block %d has negative length %d", i, block_len[i]);
+    if (!anything && block_len[i] != block_len[0])
+      return fail(CP_ERR_INVALID_ARG,
+                  "cp_ring_attention: block lengths differ (block 0: %d, block %d: %d); plain ring "
+                  "attention needs the sequence to divide evenly by ring_degree -- pass "
+                  "CP_RING_ANYTHING for uneven blocks",
+                  block_len[0], i, block_len[i]);
+    total += block_len[i];
+  }
+  if (!anything && block_len[0] == 0)
+    return fail(CP_ERR_INVALID_ARG, "cp_ring_attention: empty blocks need CP_RING_ANYTHING");
+  const Strides qs = resolve(q_strides, Sq, H, D);
+  const Strides kvs = resolve(kv_strides, total > 0x7fffffff ? 0 : (int)total, H, D);
+  const Strides os = resolve(out_strides, Sq, H, D);
+  cp_status_t st = check_common(q, qs, kvs, dtype, B, H, D, Sq, scale, out, os, lse);
+  if (st != CP_OK) return st;
+  for (int i = 0; i < ring_degree; ++i)
+    if ((st = check_kv(k_blocks[i], v_blocks[i], block_len[i])) != CP_OK)
+      return fail(st, "cp_ring_attention: block %d: %s", i, g_err.c_str());
+  const bool separate = (flags & CP_RING_SEPARATE_MERGE) != 0;
+  float* ws_out = nullptr;
+  float* ws_lse = nullptr;
+  if (separate && B > 0 && H > 0 && Sq > 0) {
+    const size_t need = partial_bytes(B, H, Sq, D);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(CP_ERR_WORKSPACE, "cp_ring_attention: workspace of %zu bytes needed, %zu given", need,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (!aligned(workspace, 256))
+      return fail(CP_ERR_UNSUPPORTED, "cp_ring_attention: workspace must be 256-byte aligned");
+    ws_out = static_cast<float*>(workspace);
+    ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      align_up((size_t)B * Sq * H * D * sizeof(float), 256));
+  }
+  if (B == 0 || H == 0 || Sq == 0) return CP_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Strides ws_s = resolve(nullptr, Sq, H, D);
+  bool have = false;  // does (out, lse) hold a partial yet?
+  for (int i = 0; i < ring_degree; ++i) {
+    if (block_len[i] == 0) continue;  // a block over no keys has weight 0 in the merge
+    if (!have) {
+      st = run_block(q, qs, k_blocks[i], v_blocks[i], kvs, dtype, B, H, D, Sq, block_len[i], scale, false,
+                     out, os, lse, s);
+      have = true;
+    } else if (separate) {
+      st = run_block(q, qs, k_blocks[i], v_blocks[i], kvs, dtype, B, H, D, Sq, block_len[i], scale, false,
+                     ws_out, ws_s, ws_lse, s);
+      if (st == CP_OK)
+        st = hip_status(cpattn::launch_lse_merge(out, lse, ws_out, ws_lse, os, ws_s, B, H, Sq, D, s),
+                        "lse_merge");
+    } else {
+      st = run_block(q, qs, k_blocks[i], v_blocks[i], kvs, dtype, B, H, D, Sq, block_len[i], scale, true,
+                     out, os, lse, s);
+    }
+    if (st != CP_OK) return st;
+  }
+  if (!have) return hip_status(cpattn::launch_fill_empty(out, os, lse, B, H, Sq, D, s), "fill_empty");
+  return CP_OK;
+}
+
+cp_status_t cp_ulysses_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
+                               int D, int degree, int direction, void* stream) {
+  if (elem_bytes != 2 && elem_bytes != 4)
+    return fail(CP_ERR_UNSUPPORTED, "cp_ulysses_regroup: elem_bytes must be 2 or 4 (got %d)", elem_bytes);
+  if (B < 0 || S_local < 0 || H < 0 || D < 0)
+    return fail(CP_ERR_INVALID_ARG, "cp_ulysses_regroup: sizes must be non-negative");
+  if (degree < 1) return fail(CP_ERR_INVALID_ARG, "cp_ulysses_regroup: degree must be >= 1 (got %d)", degree);
+  if (H % degree != 0)
+    return fail(CP_ERR_INVALID_ARG,
+                "cp_ulysses_regroup: the number of heads H=%d must be divisible by the Ulysses degree %d",
+                H, degree);
+  if (direction != CP_REGROUP_SEQ_TO_HEAD && direction != CP_REGROUP_HEAD_TO_SEQ)
+    return fail(CP_ERR_INVALID_ARG, "cp_ulysses_regroup: unknown direction %d", direction);
+  const int64_t bytes = (int64_t)B * S_local * H * D * elem_bytes;
+  if (bytes == 0) return CP_OK;
+  if (!in || !out) return fail(CP_ERR_INVALID_ARG, "cp_ulysses_regroup: pointers must be non-null");
+  const uintptr_t a = reinterpret_cast<uintptr_t>(in), b = reinterpret_cast<uintptr_t>(out);
+  if (a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes)
+    return fail(CP_ERR_INVALID_ARG, "cp_ulysses_regroup: in and out overlap");
+  if (!aligned(in, elem_bytes) || !aligned(out, elem_bytes))
+    return fail(CP_ERR_UNSUPPORTED, "cp_ulysses_regroup: pointers must be aligned to elem_bytes");
+  return hip_status(cpattn::launch_regroup(in, out, elem_bytes, B, S_local, H, D, degree, direction,
+                                           static_cast<hipStream_t>(stream)),
+                    "ulysses_regroup");
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the gfx950
+// kernels. Arguments reaching these launchers have been validated already.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+// Element strides of a [B, S, H, D] tensor (D is unit-stride).
+struct Strides {
+  int64_t b, s, h;
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;
+  float* lse;
+  Strides qs, kvs, os;
+  int B, H, D, Sq, Skv;
+  float scale;
+  bool accumulate;  // merge into (out, lse) instead of overwriting
+};
+
+// Partial attention of Q against one K/V block (Skv >= 1), float32 out + LSE.
+hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
+
+// out = 0, lse = -inf for every (b, s, h): attention over an empty key set.
+hipError_t launch_fill_empty(float* out, Strides os, float* lse, int B, int H, int Sq, int D,
+                             hipStream_t stream);
+
+// (out_acc, lse_acc) <- (out_acc, lse_acc) (+) (out_blk, lse_blk).
+hipError_t launch_lse_merge(float* out_acc, float* lse_acc, const float* out_blk,
+                            const float* lse_blk, Strides as, Strides bs, int B, int H, int Sq,
+                            int D, hipStream_t stream);
+
+// Ulysses regroup bit copy; see cp_ulysses_regroup.
+hipError_t launch_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
+                          int D, int degree, int direction, hipStream_t stream);
+
+}  // namespace cpattn

@@ -1,0 +1,195 @@
+/*
+ * cp_attn.h -- one rank's share of context-parallel attention on one AMD
+ * Instinct MI355X (gfx950): blockwise non-causal softmax attention of a local
+ * Q slice against ring K/V blocks, float32 partial outputs with their
+ * log-sum-exp (LSE), the LSE merge of partials, and the Ulysses head/token
+ * regroup as a local permutation.
+ *
+ * Sources (diffusers v0.43.0 documentation pages):
+ *   [CP]  "Paralelismo de contexto" -- context-parallelism guide;
+ *         sections "Atencao em Anel" (Ring Attention), "Atencao Ulysses",
+ *         "Ring Anything Attention".
+ *   [API] "Paralelismo" -- parallelism API reference; section
+ *         "ContextParallelConfig" (ring_degree, ulysses_degree,
+ *         convert_to_fp32, rotate_method, ring_anything).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are [B, S, H, D] with the D axis unit-stride. Strides are given
+ *     as a host array int64_t[3] = {stride_b, stride_s, stride_h} in elements
+ *     of the tensor's own dtype; NULL means contiguous [B, S, H, D].
+ *   - LSE tensors are float32 [B, H, Sq], contiguous, natural log.
+ *   - Device pointers must be 16-byte aligned and every stride times the
+ *     element size must be a multiple of 16 bytes.
+ *   - The caller allocates and owns every buffer (inputs, outputs and any
+ *     workspace). The library keeps no pointer after a call returns and
+ *     allocates no device memory.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *     work on that stream and never synchronise the host; results are ready
+ *     once the stream has reached that point.
+ *   - Arguments are validated on the host before anything is enqueued. On
+ *     error nothing is launched, a non-zero status is returned and
+ *     cp_last_error() describes the problem. CP_ERR_HIP reports a failed
+ *     launch.
+ *   - Inputs and outputs must not overlap, except where an entry point says
+ *     it updates a buffer in place.
+ *   - Supported: dtype CP_BF16 or CP_F32 for Q/K/V, head dim D = 64 or 128.
+ *     Outputs are always float32: the partial output and LSE are kept in
+ *     float32 for a stable merge ([API] convert_to_fp32, default True).
+ */
+#ifndef CP_ATTN_H
+#define CP_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CP_ATTN_ABI_VERSION 1
+
+typedef enum cp_status {
+  CP_OK = 0,
+  CP_ERR_INVALID_ARG = 1, /* bad pointer, size, stride or combination */
+  CP_ERR_UNSUPPORTED = 2, /* valid request outside the supported set (dtype, D, alignment) */
+  CP_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  CP_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} cp_status_t;
+
+typedef enum cp_dtype { CP_F32 = 0, CP_BF16 = 1 } cp_dtype_t;
+
+/* cp_attn_block_fwd flag: merge this block into (out, lse) instead of overwriting them. */
+#define CP_BLOCK_ACCUMULATE 0x1u
+/* cp_ring_attention flag: allow unequal block lengths, zero included ([CP] Ring Anything). */
+#define CP_RING_ANYTHING 0x2u
+/* cp_ring_attention flag: write each block's partial into the workspace and merge it with
+ * a separate cp_lse_merge pass, instead of merging inside the attention kernel. */
+#define CP_RING_SEPARATE_MERGE 0x4u
+
+/* cp_ulysses_regroup directions. */
+#define CP_REGROUP_SEQ_TO_HEAD 0 /* first all-to-all: [B, S_local, H, D] -> [B, P*S_local, H/P, D] */
+#define CP_REGROUP_HEAD_TO_SEQ 1 /* second all-to-all: [B, P*S_local, H/P, D] -> [B, S_local, H, D] */
+
+/*
+ * cp_attn_block_fwd -- partial attention of the local Q against one K/V block.
+ *
+ * [CP] "Atencao em Anel": each GPU computes attention of its local Q against
+ * the K/V block it holds; [API] ring_degree: attention between the local Q
+ * and each K/V block passed around the ring; [API] convert_to_fp32: the
+ * block's output and LSE are float32.
+ *
+ * For every (b, h) and query row i (non-causal, no mask):
+ *   x_ij   = scale * <q_i, k_j>,  j = 0 .. Skv-1
+ *   lse_i  = ln sum_j exp(x_ij)
+ *   out_i  = sum_j exp(x_ij - lse_i) * v_j
+ *
+ *   q    [B, Sq, H, D]  dtype, strides q_strides
+ *   k, v [B, Skv, H, D] dtype, shared strides kv_strides (a block of a
+ *        larger resident buffer, e.g. a padded all-gather, is passed as a
+ *        base pointer plus that buffer's strides; rows >= Skv are never read)
+ *   out  [B, Sq, H, D]  float32, strides out_strides
+ *   lse  [B, H, Sq]     float32, contiguous
+ *   scale  > 0 and finite (the usual choice is 1/sqrt(D))
+ *   flags  0 or CP_BLOCK_ACCUMULATE. With CP_BLOCK_ACCUMULATE, (out, lse)
+ *          must already hold a partial result of the same queries over
+ *          other keys; they are updated in place to the merge of that
+ *          partial with this block (the cp_lse_merge formula).
+ *
+ * Skv == 0 is allowed: without CP_BLOCK_ACCUMULATE it writes out = 0 and
+ * lse = -inf (attention over no keys); with it, it leaves (out, lse) as they
+ * are. B, H or Sq == 0 enqueues nothing.
+ */
+cp_status_t cp_attn_block_fwd(const void* q, const int64_t* q_strides,
+                              const void* k, const void* v, const int64_t* kv_strides,
+                              int dtype, int B, int H, int D, int Sq, int Skv, float scale,
+                              unsigned flags, float* out, const int64_t* out_strides, float* lse,
+                              void* stream);
+
+/*
+ * cp_lse_merge -- (out_acc, lse_acc) <- (out_acc, lse_acc) (+) (out_blk, lse_blk), in place.
+ *
+ * [API] convert_to_fp32 (partials kept in float32 for the ring's merge) and
+ * [CP] "Atencao em Anel" (after a full loop every rank has seen every
+ * token's K/V). The pages name the merged quantities but print no formula;
+ * this is the exact recombination of two softmax partials over disjoint keys:
+ *   M   = max(lse_a, lse_b),  w_a = exp(lse_a - M),  w_b = exp(lse_b - M)
+ *   lse = M + ln(w_a + w_b),  out = (w_a*out_a + w_b*out_b) / (w_a + w_b)
+ * A side with lse = -inf has weight 0; if both are -inf the result is
+ * out = 0, lse = -inf.
+ *
+ *   out_acc, out_blk [B, Sq, H, D] float32 with strides acc_strides / blk_strides
+ *   lse_acc, lse_blk [B, H, Sq]    float32, contiguous
+ * out_blk/lse_blk are read only and must not overlap the accumulators.
+ */
+cp_status_t cp_lse_merge(float* out_acc, float* lse_acc, const float* out_blk, const float* lse_blk,
+                         const int64_t* acc_strides, const int64_t* blk_strides,
+                         int B, int H, int Sq, int D, void* stream);
+
+/*
+ * cp_ring_attention_workspace_size -- bytes of workspace cp_ring_attention
+ * needs for these sizes and flags: 0 unless CP_RING_SEPARATE_MERGE is set,
+ * then room for one float32 partial output [B, Sq, H, D] and its LSE.
+ */
+size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned flags);
+
+/*
+ * cp_ring_attention -- one rank's share of Ring Attention, all K/V blocks resident.
+ *
+ * [CP] "Atencao em Anel" and [API] ring_degree / rotate_method: the local Q
+ * attends to each of the ring_degree K/V blocks in turn (block 0 first) and
+ * the float32 partials are merged by LSE rescaling; with all blocks present
+ * after an all-gather (the only rotate method the pages support) the loop
+ * runs locally. The result equals attention of Q over the concatenation of
+ * all blocks.
+ *
+ *   k_blocks, v_blocks  host arrays of ring_degree device pointers; block i
+ *                       is [B, block_len[i], H, D] with the shared kv_strides
+ *   block_len           host array of ring_degree lengths
+ *   ring_degree         >= 1
+ *   flags               CP_RING_ANYTHING: lengths may differ and may be 0
+ *                       ([CP] "Ring Anything Attention": each padded block
+ *                       is cut back to its true length; pad rows are never
+ *                       read). Without it every length must be equal and
+ *                       >= 1 (plain ring attention needs the sequence to
+ *                       divide evenly by ring_degree).
+ *                       CP_RING_SEPARATE_MERGE: see above; needs workspace.
+ *   out, lse            as cp_attn_block_fwd; overwritten.
+ *   workspace           device buffer of workspace_bytes (may be NULL when
+ *                       cp_ring_attention_workspace_size() returns 0)
+ * If every block is empty the result is out = 0, lse = -inf.
+ */
+cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides,
+                              const void* const* k_blocks, const void* const* v_blocks,
+                              const int64_t* kv_strides, const int* block_len, int ring_degree,
+                              int dtype, int B, int H, int D, int Sq, float scale, unsigned flags,
+                              float* out, const int64_t* out_strides, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * cp_ulysses_regroup -- the Ulysses all-to-all's local permutation, loopback.
+ *
+ * [CP] "Atencao Ulysses": the first all-to-all leaves each GPU with every
+ * token for a subset of heads; the second regroups the results by token.
+ * With the exchange replaced by a loopback, head group g (heads g*H/P ..
+ * (g+1)*H/P - 1) of this rank's S_local tokens becomes token chunk g:
+ *   SEQ_TO_HEAD: out[b, g*S_local + s, h, d] = in[b, s, g*(H/P) + h, d]
+ *   HEAD_TO_SEQ: out[b, s, g*(H/P) + h, d] = in[b, g*S_local + s, h, d]
+ * A bit copy: elem_bytes is 2 (bf16/fp16) or 4 (float32); contiguous tensors.
+ * S_local and H always describe the sequence-sharded side [B, S_local, H, D];
+ * degree is the Ulysses degree P >= 1 and must divide H ([CP]: the number of
+ * heads must be divisible by ulysses_degree). in and out must not overlap.
+ */
+cp_status_t cp_ulysses_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
+                               int D, int degree, int direction, void* stream);
+
+/* Message for the last non-CP_OK status returned on the calling thread ("" if none). */
+const char* cp_last_error(void);
+
+/* CP_ATTN_ABI_VERSION of the loaded library. */
+int cp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_ATTN_H */

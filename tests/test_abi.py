@@ -1,0 +1,142 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+
+The pointers used here are fake host addresses; every call below fails
+validation, which happens before anything is enqueued, so none of them is
+ever dereferenced.
+"""
+import ctypes
+import os
+
+import pytest
+
+from context_attention_dits_amd import _lib
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.library_path()),
+                                reason="libcpattn.so not built (python -m context_attention_dits_amd.build)")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _lib.declared_symbols()
+    assert {"cp_attn_block_fwd", "cp_lse_merge", "cp_ring_attention", "cp_ring_attention_workspace_size",
+            "cp_ulysses_regroup", "cp_last_error", "cp_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.cp_abi_version() == 1
+
+
+def _block(lib, dtype=1, B=1, H=2, D=128, Sq=8, Skv=8, scale=0.1, flags=0, q=FAKE, k=FAKE, v=FAKE,
+           out=FAKE, lse=FAKE, qs=None, kvs=None, os_=None):
+    return lib.cp_attn_block_fwd(q, qs, k, v, kvs, dtype, B, H, D, Sq, Skv, scale, flags, out, os_, lse, None)
+
+
+def _err(lib):
+    return lib.cp_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=7), _lib.CP_ERR_UNSUPPORTED, "dtype"),
+    (dict(D=96), _lib.CP_ERR_UNSUPPORTED, "D=96"),
+    (dict(D=256), _lib.CP_ERR_UNSUPPORTED, "supported"),
+    (dict(B=-1), _lib.CP_ERR_INVALID_ARG, "non-negative"),
+    (dict(Skv=-3), _lib.CP_ERR_INVALID_ARG, "non-negative"),
+    (dict(scale=0.0), _lib.CP_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("nan")), _lib.CP_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("inf")), _lib.CP_ERR_INVALID_ARG, "scale"),
+    (dict(flags=0x80), _lib.CP_ERR_INVALID_ARG, "flags"),
+    (dict(q=0), _lib.CP_ERR_INVALID_ARG, "non-null"),
+    (dict(lse=0), _lib.CP_ERR_INVALID_ARG, "non-null"),
+    (dict(k=0), _lib.CP_ERR_INVALID_ARG, "non-null"),
+    (dict(q=FAKE + 8), _lib.CP_ERR_UNSUPPORTED, "aligned"),
+    (dict(v=FAKE + 2), _lib.CP_ERR_UNSUPPORTED, "aligned"),
+])
+def test_block_fwd_rejects(lib, kw, status, needle):
+    assert _block(lib, **kw) == status
+    assert needle in _err(lib)
+
+
+def test_block_fwd_rejects_bad_strides(lib):
+    bad = (ctypes.c_int64 * 3)(8 * 2 * 128, 2 * 128 + 4, 128)  # 4 bf16 = 8 bytes: not 16-B multiple
+    assert _block(lib, qs=bad) == _lib.CP_ERR_UNSUPPORTED
+    neg = (ctypes.c_int64 * 3)(-1, 256, 128)
+    assert _block(lib, kvs=neg) == _lib.CP_ERR_INVALID_ARG
+    overlap = (ctypes.c_int64 * 3)(8 * 2 * 128, 2 * 128, 64)  # heads overlap along D=128
+    assert _block(lib, os_=overlap) == _lib.CP_ERR_INVALID_ARG
+
+
+def test_empty_problem_is_a_no_op(lib):
+    # B, H or Sq == 0 enqueues nothing, so even null pointers are fine.
+    assert _block(lib, Sq=0, q=0, k=0, v=0, out=0, lse=0) == _lib.CP_OK
+    assert _block(lib, B=0, q=0, k=0, v=0, out=0, lse=0) == _lib.CP_OK
+
+
+def _ring(lib, lens, flags=0, dtype=1, ws=None, ws_bytes=0, kptrs=None):
+    P = len(lens)
+    karr = (ctypes.c_void_p * P)(*(kptrs or [FAKE] * P))
+    varr = (ctypes.c_void_p * P)(*([FAKE] * P))
+    L = (ctypes.c_int * P)(*lens)
+    return lib.cp_ring_attention(FAKE, None, karr, varr, None, L, P, dtype, 1, 2, 128, 8, 0.1, flags, FAKE, None,
+                                 FAKE, ws, ws_bytes, None)
+
+
+def test_ring_rejects_uneven_without_ring_anything(lib):
+    assert _ring(lib, [1536, 1536, 1535]) == _lib.CP_ERR_INVALID_ARG
+    assert "CP_RING_ANYTHING" in _err(lib)
+    assert _ring(lib, [0, 0]) == _lib.CP_ERR_INVALID_ARG
+    assert _ring(lib, [4, -1], flags=_lib.CP_RING_ANYTHING) == _lib.CP_ERR_INVALID_ARG
+
+
+def test_ring_rejects_degree_flags_and_null_blocks(lib):
+    assert _ring(lib, []) == _lib.CP_ERR_INVALID_ARG
+    assert "ring_degree" in _err(lib)
+    assert _ring(lib, [8, 8], flags=0x100) == _lib.CP_ERR_INVALID_ARG
+    assert _ring(lib, [8, 8], kptrs=[FAKE, 0]) == _lib.CP_ERR_INVALID_ARG
+    assert "block 1" in _err(lib)
+
+
+def test_ring_workspace_rules(lib):
+    need = lib.cp_ring_attention_workspace_size(1, 2, 8, 128, _lib.CP_RING_SEPARATE_MERGE)
+    assert need >= 4 * (1 * 8 * 2 * 128 + 1 * 2 * 8)
+    assert lib.cp_ring_attention_workspace_size(1, 2, 8, 128, 0) == 0
+    assert _ring(lib, [8, 8], flags=_lib.CP_RING_SEPARATE_MERGE) == _lib.CP_ERR_WORKSPACE
+    assert _ring(lib, [8, 8], flags=_lib.CP_RING_SEPARATE_MERGE, ws=FAKE, ws_bytes=need - 1) == _lib.CP_ERR_WORKSPACE
+    assert _ring(lib, [8, 8], flags=_lib.CP_RING_SEPARATE_MERGE, ws=FAKE + 16, ws_bytes=need) == _lib.CP_ERR_UNSUPPORTED
+
+
+def test_merge_rejects(lib):
+    f = lib.cp_lse_merge
+    assert f(FAKE, FAKE, FAKE + 4096, FAKE + 8192, None, None, 1, 2, 8, 80, None) == _lib.CP_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE + 8192, None, None, 1, 2, 8, 128, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(0, FAKE, FAKE, FAKE, None, None, 1, 2, 8, 128, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(0, 0, 0, 0, None, None, 1, 0, 8, 128, None) == _lib.CP_OK
+
+
+def test_regroup_rejects(lib):
+    f = lib.cp_ulysses_regroup
+    assert f(FAKE, FAKE + (1 << 30), 2, 1, 16, 24, 128, 5, 0, None) == _lib.CP_ERR_INVALID_ARG
+    assert "divisible" in _err(lib)
+    assert f(FAKE, FAKE + (1 << 30), 3, 1, 16, 24, 128, 2, 0, None) == _lib.CP_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE + (1 << 30), 2, 1, 16, 24, 128, 0, 0, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(FAKE, FAKE + (1 << 30), 2, 1, 16, 24, 128, 2, 9, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 64, 2, 1, 16, 24, 128, 2, 0, None) == _lib.CP_ERR_INVALID_ARG  # overlap
+    assert "overlap" in _err(lib)
+    assert f(0, 0, 2, 0, 16, 24, 128, 2, 0, None) == _lib.CP_OK
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    import context_attention_dits_amd as cp
+    q = torch.zeros(1, 8, 2, 128, dtype=torch.bfloat16)
+    out = torch.zeros(1, 8, 2, 128)
+    lse = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        cp.cp_attn_block_fwd(q, q, q, out, lse)
+    with pytest.raises(ValueError, match="GPU"):
+        cp.cp_ulysses_regroup(q, q.clone(), 2)

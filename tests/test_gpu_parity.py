@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path, called through the C-ABI, against the float64 oracle.
+
+Every case draws seeded inputs from ``workloads``, runs the library on the GPU
+and compares element by element with the oracle on the same values. Small
+shapes are compared in full (they span several tiles and a ragged tail); the
+full-size workloads are compared on sampled query rows, which the oracle
+computes one by one against every key, in the same launch configuration the
+benchmark times. Tolerances: float32 inputs 1e-5 (out and LSE), bfloat16
+inputs 1e-2 (out) and 1e-3 (LSE); the regroup is bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import TOL, assert_close, dev, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def cp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import context_attention_dits_amd as m
+    m.load()  # raises if the HIP library is missing: no fallback
+    return m
+
+
+def _ring_gpu(cp, inp, flags_extra=0, q_dev=None):
+    w = inp.workload
+    q = dev(inp.q, w.dtype) if q_dev is None else q_dev
+    k = dev(inp.k, w.dtype)
+    v = dev(inp.v, w.dtype)
+    offs = workloads.block_offsets(w.block_lens)
+    kb = [k[:, o:o + L] for o, L in zip(offs, w.block_lens)]
+    vb = [v[:, o:o + L] for o, L in zip(offs, w.block_lens)]
+    out, lse = cp.ring_attention(q, kb, vb, scale=w.scale, separate_merge=bool(flags_extra))
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def _check_rows(name, out, lse, q, k, v, scale, rows, dtype):
+    """Oracle full attention for the sampled query rows only."""
+    o_ref, l_ref = oracle.attention(q[:, rows], k, v, scale)
+    assert_close(f"{name} out", out[:, rows], o_ref, TOL[dtype]["o"])
+    assert_close(f"{name} lse", lse[:, :, rows], l_ref, TOL[dtype]["lse"])
+
+
+# ------------------------------------------------------------ small shapes ---
+
+SMALL = [
+    # B, H, D, Sq, block_lens, dtype
+    (1, 2, 64, 64, (64, 64, 64, 64), "f32"),
+    (2, 3, 128, 100, (77, 40), "f32"),
+    (2, 3, 128, 200, (300,), "bf16"),
+    (1, 4, 128, 257, (128, 128, 1), "bf16"),
+    (2, 2, 64, 130, (129, 200), "bf16"),
+    (1, 2, 128, 1, (5, 64, 33), "bf16"),
+    (1, 3, 64, 70, (3, 1), "f32"),
+]
+
+
+@pytest.mark.parametrize("B,H,D,Sq,lens,dtype", SMALL)
+def test_ring_small_full_compare(cp, B, H, D, Sq, lens, dtype):
+    say("ring small", B, H, D, Sq, lens, dtype)
+    inp = workloads.make_custom(B, H, D, Sq, lens, dtype, seed=1000 + B * 7 + H + D + Sq)
+    w = inp.workload
+    anything = len(set(lens)) > 1
+    q, k, v = dev(inp.q, dtype), dev(inp.k, dtype), dev(inp.v, dtype)
+    offs = workloads.block_offsets(lens)
+    kb = [k[:, o:o + L] for o, L in zip(offs, lens)]
+    vb = [v[:, o:o + L] for o, L in zip(offs, lens)]
+    for sep in (False, True):
+        out, lse = cp.ring_attention(q, kb, vb, scale=w.scale, ring_anything=anything, separate_merge=sep)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.ring_attention(inp.q, [inp.k_block(i) for i in range(len(lens))],
+                                             [inp.v_block(i) for i in range(len(lens))], w.scale)
+        assert_close(f"out sep={sep}", out.cpu().numpy(), o_ref, TOL[dtype]["o"])
+        assert_close(f"lse sep={sep}", lse.cpu().numpy(), l_ref, TOL[dtype]["lse"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_fwd_and_accumulate(cp, dtype):
+    """One block written, a second merged in by the kernel epilogue, versus oracle partials."""
+    B, H, D, Sq, lens = 2, 3, 128, 150, (96, 70)
+    say("block+accumulate", dtype)
+    inp = workloads.make_custom(B, H, D, Sq, lens, dtype, seed=77)
+    q = dev(inp.q, dtype)
+    k0, v0 = dev(inp.k_block(0), dtype), dev(inp.v_block(0), dtype)
+    k1, v1 = dev(inp.k_block(1), dtype), dev(inp.v_block(1), dtype)
+    out = torch.empty(B, Sq, H, D, device="cuda")
+    lse = torch.empty(B, H, Sq, device="cuda")
+    s = inp.workload.scale
+    cp.cp_attn_block_fwd(q, k0, v0, out, lse, scale=s)
+    torch.cuda.synchronize()
+    o0, l0 = oracle.block_attention(inp.q, inp.k_block(0), inp.v_block(0), s)
+    assert_close("block0 out", out.cpu().numpy(), o0, TOL[dtype]["o"])
+    assert_close("block0 lse", lse.cpu().numpy(), l0, TOL[dtype]["lse"])
+    cp.cp_attn_block_fwd(q, k1, v1, out, lse, scale=s, flags=cp.CP_BLOCK_ACCUMULATE)
+    torch.cuda.synchronize()
+    o, l = oracle.ring_attention(inp.q, [inp.k_block(0), inp.k_block(1)], [inp.v_block(0), inp.v_block(1)], s)
+    assert_close("merged out", out.cpu().numpy(), o, TOL[dtype]["o"])
+    assert_close("merged lse", lse.cpu().numpy(), l, TOL[dtype]["lse"])
+
+
+def test_lse_merge_kernel(cp):
+    say("lse_merge kernel")
+    rng = np.random.default_rng(5)
+    B, Sq, H, D = 2, 37, 5, 128
+    oa, ob = rng.standard_normal((B, Sq, H, D)).astype(np.float32), rng.standard_normal((B, Sq, H, D)).astype(np.float32)
+    la, lb = (rng.standard_normal((B, H, Sq)) * 4).astype(np.float32), (rng.standard_normal((B, H, Sq)) * 4).astype(np.float32)
+    la[0, 1, :5] = -np.inf   # accumulator empty
+    lb[1, 2, 3:9] = -np.inf  # block empty
+    la[1, 4, 10:12] = -np.inf
+    lb[1, 4, 10:12] = -np.inf  # both empty
+    oa[1, 10:12, 4] = np.nan  # an empty side's output must not leak
+    ga, gla = torch.from_numpy(oa).cuda(), torch.from_numpy(la).cuda()
+    cp.cp_lse_merge(ga, gla, torch.from_numpy(ob).cuda(), torch.from_numpy(lb).cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.lse_merge(np.nan_to_num(oa, nan=0.0), la, ob, lb)
+    got_l = gla.cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(l_ref))
+    fin = np.isfinite(l_ref)
+    assert_close("merge lse", got_l[fin], l_ref[fin], 1e-5)
+    assert_close("merge out", ga.cpu().numpy(), o_ref, 1e-5)
+
+
+# ----------------------------------------------------- degenerate / layout ---
+
+def test_ring_anything_nan_padded_gather(cp):
+    """K/V blocks as views of a padded [P, B, Lmax, H, D] gather whose pad rows are NaN."""
+    B, H, D, Sq, lens = 2, 3, 128, 90, (70, 64, 33)
+    say("ring anything padded NaN", lens)
+    inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=91)
+    Lmax = max(lens)
+    kpad = torch.full((len(lens), B, Lmax, H, D), float("nan"), dtype=torch.bfloat16)
+    vpad = torch.full((len(lens), B, Lmax, H, D), float("nan"), dtype=torch.bfloat16)
+    for i, L in enumerate(lens):
+        kpad[i, :, :L] = torch.from_numpy(inp.k_block(i)).to(torch.bfloat16)
+        vpad[i, :, :L] = torch.from_numpy(inp.v_block(i)).to(torch.bfloat16)
+    kpad, vpad = kpad.cuda(), vpad.cuda()
+    kb = [kpad[i, :, :L] for i, L in enumerate(lens)]
+    vb = [vpad[i, :, :L] for i, L in enumerate(lens)]
+    q = dev(inp.q, "bf16")
+    out, lse = cp.ring_attention(q, kb, vb, scale=inp.workload.scale, ring_anything=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.workload.scale)
+    assert_close("out", out.cpu().numpy(), o_ref, TOL["bf16"]["o"])
+    assert_close("lse", lse.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
+
+
+def test_zero_length_blocks(cp):
+    B, H, D, Sq = 1, 2, 128, 40
+    say("zero-length blocks")
+    inp = workloads.make_custom(B, H, D, Sq, (0, 50, 0, 30), "bf16", seed=12)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    kb = [k[:, 0:0], k[:, 0:50], k[:, 50:50], k[:, 50:80]]
+    vb = [v[:, 0:0], v[:, 0:50], v[:, 50:50], v[:, 50:80]]
+    out, lse = cp.ring_attention(q, kb, vb, scale=inp.workload.scale, ring_anything=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.workload.scale)
+    assert_close("out", out.cpu().numpy(), o_ref, TOL["bf16"]["o"])
+    assert_close("lse", lse.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
+    # every block empty: attention over no keys
+    out, lse = cp.ring_attention(q, [k[:, 0:0]] * 2, [v[:, 0:0]] * 2, ring_anything=True)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0).item() and torch.all(torch.isneginf(lse)).item()
+
+
+def test_strided_views(cp):
+    """Q, K/V and out as non-contiguous views (heads interleaved in wider buffers)."""
+    B, H, D, Sq, Skv = 2, 3, 128, 97, 130
+    say("strided views")
+    inp = workloads.make_custom(B, H, D, Sq, (Skv,), "bf16", seed=33)
+    qw = torch.zeros(B, Sq, 2 * H, D, dtype=torch.bfloat16, device="cuda")
+    kw = torch.zeros(B, Skv, 2 * H, D, dtype=torch.bfloat16, device="cuda")
+    vw = torch.zeros(B, Skv, 2 * H, D, dtype=torch.bfloat16, device="cuda")
+    qw[:, :, 1::2] = dev(inp.q, "bf16")
+    kw[:, :, 1::2] = dev(inp.k, "bf16")
+    vw[:, :, 1::2] = dev(inp.v, "bf16")
+    ow = torch.full((B, Sq, H, 2 * D), 7.0, device="cuda")
+    out = ow[..., D:]
+    lse = torch.empty(B, H, Sq, device="cuda")
+    cp.cp_ring_attention(qw[:, :, 1::2], [kw[:, :, 1::2]], [vw[:, :, 1::2]], out, lse, scale=inp.workload.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.workload.scale)
+    assert_close("out", out.cpu().numpy(), o_ref, TOL["bf16"]["o"])
+    assert_close("lse", lse.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
+    assert torch.all(ow[..., :D] == 7.0).item(), "write outside the output view"
+
+
+def test_wide_softmax_range(cp):
+    """Q scaled by 8: scores spread over a much wider range than N(0,1) gives."""
+    B, H, D, Sq, lens = 1, 4, 128, 192, (256, 250)
+    say("q*8 stress")
+    inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=8, q_scale=8.0)
+    out, lse = _ring_gpu(cp, inp)
+    o_ref, l_ref = oracle.ring_attention(inp.q, [inp.k_block(0), inp.k_block(1)],
+                                         [inp.v_block(0), inp.v_block(1)], inp.workload.scale)
+    assert_close("out", out, o_ref, TOL["bf16"]["o"])
+    assert_close("lse", lse, l_ref, TOL["bf16"]["lse"])
+
+
+# ----------------------------------------------------------------- regroup ---
+
+@pytest.mark.parametrize("B,S_l,H,D,P,dt", [(1, 2304, 24, 128, 2, "bf16"), (2, 33, 12, 64, 3, "bf16"),
+                                              (1, 50, 8, 128, 4, "f32"), (2, 7, 6, 128, 1, "bf16"),
+                                              (1, 5, 6, 4, 2, "bf16")])
+def test_regroup_bit_exact(cp, B, S_l, H, D, P, dt):
+    say("regroup", B, S_l, H, D, P, dt)
+    rng = np.random.default_rng(B * 100 + S_l + H)
+    x = rng.standard_normal((B, S_l, H, D)).astype(np.float32)
+    if dt == "bf16":
+        x = workloads.round_to_bf16(x)
+    t = dev(x, dt)
+    y = torch.empty(B, P * S_l, H // P, D, dtype=t.dtype, device="cuda")
+    cp.cp_ulysses_regroup(t, y, P, cp.CP_REGROUP_SEQ_TO_HEAD)
+    back = torch.empty_like(t)
+    cp.cp_ulysses_regroup(y, back, P, cp.CP_REGROUP_HEAD_TO_SEQ)
+    torch.cuda.synchronize()
+    want = oracle.ulysses_regroup(x, P)
+    got = y.float().cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32))
+    assert torch.equal(back, t)
+
+
+# -------------------------------------------------- the five workloads ---
+
+def _edges(n, tile=128):
+    e = []
+    for t in range(0, n, tile):
+        e += [t, t + tile - 1]
+    return e[:40] + [n - 1]
+
+
+def test_workload_tiny_ring4_f32(cp):
+    w = workloads.WORKLOADS[0]
+    say(w.name)
+    inp = workloads.make_inputs(w)
+    out, lse = _ring_gpu(cp, inp)
+    o_ref, l_ref = oracle.ring_attention(inp.q, [inp.k_block(i) for i in range(4)],
+                                         [inp.v_block(i) for i in range(4)], w.scale)
+    assert_close("out", out, o_ref, TOL["f32"]["o"])
+    assert_close("lse", lse, l_ref, TOL["f32"]["lse"])
+
+
+@pytest.mark.parametrize("idx", [1, 3, 4])
+def test_workload_ring_full_size_sampled(cp, idx):
+    w = workloads.WORKLOADS[idx]
+    say(w.name, "full size, sampled rows")
+    inp = workloads.make_inputs(w)
+    for sep in (False, True):
+        out, lse = _ring_gpu(cp, inp, flags_extra=sep)
+        assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+        rows = workloads.sample_rows(w.Sq, 48, seed=idx, must=_edges(w.Sq))
+        _check_rows(f"{w.name} sep={sep}", out, lse, inp.q, inp.k, inp.v, w.scale, rows, w.dtype)
+
+
+def test_workload_ulysses2(cp):
+    w = workloads.WORKLOADS[2]
+    say(w.name, "regroup + attention + inverse regroup")
+    inp = workloads.make_inputs(w)
+    P = w.ulysses_degree
+    regrouped = {}
+    for name, x in (("q", inp.q), ("k", inp.k), ("v", inp.v)):
+        t = dev(x, "bf16")
+        y = torch.empty(w.B, P * w.S_local, w.H // P, w.D, dtype=torch.bfloat16, device="cuda")
+        cp.cp_ulysses_regroup(t, y, P, cp.CP_REGROUP_SEQ_TO_HEAD)
+        regrouped[name] = y
+    torch.cuda.synchronize()
+    ref = {n: oracle.ulysses_regroup(x, P) for n, x in (("q", inp.q), ("k", inp.k), ("v", inp.v))}
+    for n in ref:
+        assert np.array_equal(regrouped[n].float().cpu().numpy(), ref[n]), f"regroup of {n} not bit-exact"
+    out, lse = cp.ring_attention(regrouped["q"], [regrouped["k"]], [regrouped["v"]], scale=w.scale)
+    back = torch.empty(w.B, w.S_local, w.H, w.D, dtype=torch.float32, device="cuda")
+    cp.cp_ulysses_regroup(out, back, P, cp.CP_REGROUP_HEAD_TO_SEQ)
+    torch.cuda.synchronize()
+    out_np, lse_np = out.cpu().numpy(), lse.cpu().numpy()
+    rows = workloads.sample_rows(w.Sq, 48, seed=2, must=_edges(w.Sq) + [w.S_local - 1, w.S_local])
+    _check_rows(w.name, out_np, lse_np, ref["q"], ref["k"], ref["v"], w.scale, rows, w.dtype)
+    assert np.array_equal(back.cpu().numpy(), oracle.ulysses_regroup_inv(out_np, P))
