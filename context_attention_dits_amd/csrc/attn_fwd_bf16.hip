@@ -9,31 +9,43 @@
 // by the exact LSE recombination instead of being stored on its own.
 //
 // Design (per workgroup: NW waves, each owning QB x 32 query rows of one
-// (b, h); the K/V block is streamed through LDS in tiles of BN keys):
+// (b, h); the K/V block is streamed through LDS in tiles of 64 keys):
 //   * Scores are computed transposed, S^T = K . Q^T, with
-//     v_mfma_f32_32x32x16_bf16: the A operand is a K tile read from LDS, the
-//     B operand is the wave's Q held in registers for the whole block. In the
-//     32x32 accumulator layout lane l holds query (l % 32) and 16 keys, so the
-//     row statistics of the online softmax are lane-local plus one swap of
+//     v_mfma_f32_32x32x16_bf16: the A operand is a K fragment read from LDS,
+//     the B operand is the wave's Q held in registers for the whole block. In
+//     the 32x32 accumulator layout lane l holds query (l % 32) and 16 keys, so
+//     the row statistics of the online softmax are lane-local plus one swap of
 //     the two 32-lane halves (v_permlane32_swap).
 //   * The output is accumulated transposed too, O^T += V^T . P^T: the B
-//     operand P^T is exactly the softmax'd score registers converted to bf16
-//     (no data movement); the contraction order over keys is permuted to
-//     match and the V^T tile is stored in LDS in that permuted key order.
-//     Each lane's O registers all belong to its own query row, so the
-//     rescale by exp(m_old - m_new) needs no cross-lane traffic.
-//   * V is transposed while it is written to LDS (four keys x eight dims per
-//     thread, 8-byte LDS stores), so every MFMA operand read is one 16-byte
-//     LDS load. Rows are XOR-swizzled in 16-byte units so the 16-byte reads
-//     of 8 (or 16) consecutive lanes land in distinct banks.
-//   * Two LDS stages: tile j+1 is fetched from global memory into registers
-//     while tile j is computed, then stored to the other stage; one barrier
-//     per tile.
+//     operand P^T is the softmax'd score registers converted to bf16 in place
+//     (no data movement), with the contraction over keys taken in the order
+//     the accumulator layout holds them. Each lane's O registers belong to its
+//     own query row, so rescaling needs no cross-lane traffic.
+//   * K and V tiles go from global memory straight into LDS
+//     (global_load_lds_dwordx4: lane i of a load fills bytes 16i..16i+15 of a
+//     1 KB LDS block), so staging costs no registers and no LDS-store
+//     instructions. K is laid out per MFMA fragment: each (32-key block,
+//     16-dim step) pair is one contiguous 1 KB block in exactly the lane
+//     order of the A operand, read back with one conflict-free ds_read_b128
+//     at an immediate offset. V stays row-major (one key per row) with its
+//     16-byte chunks XOR-swizzled by row, and the V^T operand is read with
+//     ds_read_b64_tr_b16, which transposes 4 keys x 16 dims across each
+//     16-lane group; the swizzle spreads the 8 rows one read touches over
+//     all LDS banks.
+//   * Lazy rescaling: the running row maximum is only raised (and O and the
+//     row sum rescaled) when a tile's maximum exceeds it by more than 2^8 in
+//     probability, so most tiles skip the rescale; exponentials stay <= 2^8.
+//     Row sums are accumulated in float32 from the unrounded probabilities
+//     (summing the bf16-rounded ones would cost up to 2^-9 relative in LSE
+//     when a few keys dominate a row).
+//   * Two LDS stages: the next tile's loads are issued before the current
+//     tile is computed; one barrier per tile.
 //   * The exponent uses base 2 with scale*log2(e) folded into one FMA.
 //   * Workgroups are remapped so that consecutive query tiles of one head run
 //     on the same XCD (each XCD has its own L2) and share its K/V reads.
-//   * Keys beyond Skv are never read (zero-filled in LDS) and get score
-//     -inf; query rows beyond Sq are computed on zeros and not stored.
+//   * Keys beyond Skv are never read: their loads are clamped to the last
+//     valid key and their scores set to -inf. Query rows beyond Sq are
+//     computed on zeros and not stored.
 #include <stdint.h>
 
 #include "kernels.h"
@@ -41,24 +53,28 @@
 #ifndef CP_FWD_QB
 #define CP_FWD_QB 1  // 32-query blocks per wave
 #endif
-#ifndef CP_FWD_BN
-#define CP_FWD_BN 64  // keys per LDS tile
-#endif
 #ifndef CP_FWD_NW
 #define CP_FWD_NW 4  // waves per workgroup
 #endif
 #ifndef CP_FWD_WPE
 #define CP_FWD_WPE 2  // minimum waves per SIMD the register budget must allow
 #endif
+#ifndef CP_FWD_LAZY
+#define CP_FWD_LAZY 8.0f  // rescale threshold on the row maximum, log2 units
+#endif
 
 namespace cpattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(1))) void global_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -77,19 +93,6 @@ struct Params {
   int n_wg;  // total workgroups
   float c;   // scale * log2(e)
 };
-
-// 16-byte-unit XOR swizzle for a row of NCH 16-byte chunks. For NCH >= 16
-// any 16 consecutive rows map one chunk index to 16 distinct chunks; for
-// NCH == 8 any 8 consecutive rows, and each parity class of 16 consecutive
-// rows, map to 8 distinct chunks.
-template <int NCH>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (NCH >= 16) {
-    return r & (NCH - 1);
-  } else {
-    return (r ^ (r >> 3)) & (NCH - 1);
-  }
-}
 
 // Both 32-lane halves of a wave64 end up with max/sum over the pair (l, l^32).
 __device__ __forceinline__ float half_max(float x) {
@@ -112,33 +115,50 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return (xcd < r) ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
 }
 
-template <int D, int QB, int BN, int NW>
+template <int D, int QB, int NW>
 struct Cfg {
-  static constexpr int BM = NW * QB * 32;    // query rows per workgroup
-  static constexpr int NT = NW * 64;         // threads per workgroup
-  static constexpr int DCH = D / 8;          // 16-byte chunks per K row
-  static constexpr int KROW = D * 2;         // bytes per K row in LDS
-  static constexpr int K_BYTES = BN * KROW;  // K tile
-  static constexpr int KCH = BN / 8;         // 16-byte chunks per V^T row
-  static constexpr int VROW = BN * 2;        // bytes per V^T row (one head dim)
-  static constexpr int V_BYTES = D * VROW;   // V^T tile
+  static constexpr int BN = 64;                   // keys per tile
+  static constexpr int BM = NW * QB * 32;         // query rows per workgroup
+  static constexpr int NT = NW * 64;              // threads per workgroup
+  static constexpr int KB = BN / 32;              // 32-key blocks per tile
+  static constexpr int KK = D / 16;               // 16-dim MFMA steps of QK^T
+  static constexpr int K_BYTES = KB * KK * 1024;  // one 1 KB block per (kb, kk)
+  static constexpr int VROW = D * 2;              // bytes per V row (one key)
+  static constexpr int V_BYTES = BN * VROW;
   static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int KL = BN * DCH / NT;             // K chunks per thread
-  static constexpr int VL = (BN / 4) * (D / 8) / NT;   // (4 keys x 8 dims) V tasks per thread
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert((BN * DCH) % NT == 0 && ((BN / 4) * (D / 8)) % NT == 0, "staging split");
-  static_assert(KL >= 1 && VL >= 1, "staging split");
+  static constexpr int V_RPI = 1024 / VROW;       // V rows per 1 KB direct load
+  static constexpr int V_LPR = VROW / 16;         // lanes per V row
+  static constexpr int K_PER_WAVE = KB * KK / NW;
+  static constexpr int V_PER_WAVE = (BN / V_RPI) / NW;
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert((KB * KK) % NW == 0 && (BN / V_RPI) % NW == 0, "load split");
 };
 
-template <int D, int QB, int BN, int NW, bool ACC>
+// XOR applied to a V row's 16-byte chunk index: the 8 rows that one
+// transposing read touches (4 consecutive keys, and the same 4 keys + 4)
+// cover every bank exactly twice.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  if constexpr (D == 128) {
+    return (r & 3) << 2;
+  } else {
+    return ((r >> 1) & 1) << 2;
+  }
+}
+
+template <int D, int QB, int NW, bool ACC>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
-                               amdgpu_waves_per_eu(D == 64 ? 1 : CP_FWD_WPE)))
+                               amdgpu_waves_per_eu(CP_FWD_WPE)))
 attn_fwd_bf16_kernel(Params p) {
-  using C = Cfg<D, QB, BN, NW>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  using C = Cfg<D, QB, NW>;
+  // One array per LDS stage, so the compiler can tell the stage being read
+  // from the stage the next tile is being loaded into.
+  __shared__ __attribute__((aligned(1024))) char smem0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[C::STAGE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
   const int tile = xcd_remap(blockIdx.x, p.n_wg);
@@ -151,13 +171,13 @@ attn_fwd_bf16_kernel(Params p) {
   const uint16_t* vbase = p.v + b * p.kv_sb + h * p.kv_sh;
 
   // ---- Q (B operand of S^T = K Q^T): lane holds query l32, dims kk*16 + hi*8 .. +7
-  bf16x8 qf[QB][D / 16];
+  bf16x8 qf[QB][C::KK];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qrow0 + qb * 32 + l32;
     const uint16_t* qp = p.q + b * p.q_sb + (int64_t)row * p.q_ss + h * p.q_sh + hi * 8;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
+    for (int kk = 0; kk < C::KK; ++kk) {
       if (row < p.Sq) {
         qf[qb][kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
       } else {
@@ -166,64 +186,36 @@ attn_fwd_bf16_kernel(Params p) {
     }
   }
 
-  // ---- global -> register staging of one K/V tile
-  u32x4 kreg[C::KL];
-  u32x4 vreg[C::VL][4];
-  auto gload = [&](int key0) {
+  // ---- global -> LDS for one tile (this wave's share of the 1 KB blocks)
+  auto issue_tile = [&](int key0, char* Ks) {
+    char* Vs = Ks + C::K_BYTES;
 #pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
-      const int cid = tid + i * C::NT;
-      const int n = cid / C::DCH, c = cid % C::DCH;
-      const int key = key0 + n;
-      kreg[i] = (key < p.Skv)
-                    ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * p.kv_ss + c * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < C::K_PER_WAVE; ++i) {
+      const int m = wave * C::K_PER_WAVE + i;  // K block = (kb, kk)
+      const int kb = m / C::KK, kk = m % C::KK;
+      const int key = min(key0 + kb * 32 + l32, p.Skv - 1);
+      const uint16_t* g = kbase + (int64_t)key * p.kv_ss + (2 * kk + hi) * 8;
+      __builtin_amdgcn_global_load_lds((global_void*)g, (lds_void*)(Ks + m * 1024), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < C::VL; ++i) {
-      const int task = tid + i * C::NT;
-      const int dq = task % (D / 8), kq = task / (D / 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = key0 + kq * 4 + e;
-        vreg[i][e] = (key < p.Skv)
-                         ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * p.kv_ss + dq * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < C::V_PER_WAVE; ++i) {
+      const int m = wave * C::V_PER_WAVE + i;  // V rows m*V_RPI ..
+      const int r = m * C::V_RPI + lane / C::V_LPR;
+      const int ch = (lane % C::V_LPR) ^ vswz<D>(r);
+      const int key = min(key0 + r, p.Skv - 1);
+      const uint16_t* g = vbase + (int64_t)key * p.kv_ss + ch * 8;
+      __builtin_amdgcn_global_load_lds((global_void*)g, (lds_void*)(Vs + m * 1024), 16, 0, 0);
     }
   };
 
-  // ---- register -> LDS: K row-major (swizzled); V transposed, keys in MFMA order
-  auto swrite = [&](int stage) {
-    char* Ks = smem + stage * C::STAGE;
-    char* Vs = Ks + C::K_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
-      const int cid = tid + i * C::NT;
-      const int n = cid / C::DCH, c = cid % C::DCH;
-      *reinterpret_cast<u32x4*>(Ks + n * C::KROW + ((c ^ swz<C::DCH>(n)) << 4)) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::VL; ++i) {
-      const int task = tid + i * C::NT;
-      const int dq = task % (D / 8), kq = task / (D / 8);
-      // Within each 16-key group the keys are stored in the order
-      // 0-3, 8-11, 4-7, 12-15: the key order of the P^T registers.
-      const int quad = kq & 3;
-      const int pos = (quad == 1) ? 2 : (quad == 2) ? 1 : quad;
-      const int p0 = (kq >> 2) * 16 + pos * 4;
-      const int ch = p0 >> 3, off = (p0 & 7) * 2;
-      const u32x4 v0 = vreg[i][0], v1 = vreg[i][1], v2 = vreg[i][2], v3 = vreg[i][3];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int de = dq * 8 + 2 * w, dodd = de + 1;
-        const u32x2 even = {(v0[w] & 0xffffu) | (v1[w] << 16), (v2[w] & 0xffffu) | (v3[w] << 16)};
-        const u32x2 odd = {(v0[w] >> 16) | (v1[w] & 0xffff0000u), (v2[w] >> 16) | (v3[w] & 0xffff0000u)};
-        *reinterpret_cast<u32x2*>(Vs + de * C::VROW + ((ch ^ swz<C::KCH>(de)) << 4) + off) = even;
-        *reinterpret_cast<u32x2*>(Vs + dodd * C::VROW + ((ch ^ swz<C::KCH>(dodd)) << 4) + off) = odd;
-      }
-    }
-  };
+  // Per-lane byte offset of the transposed V reads (see vswz): within a
+  // 16-lane group lane i supplies the address of key (i/4), dims 4*(i%4)..+3.
+  int vlane;
+  {
+    const int i16 = lane & 15, jq = i16 >> 2, q = i16 & 3, blk = (lane >> 4) & 1;
+    const int sw = (D == 128) ? jq : (jq >> 1);
+    vlane = (4 * hi + jq) * C::VROW + (sw << 6) + ((blk * 2 + (q >> 1)) << 4) + ((q & 1) << 3);
+  }
 
   f32x16 o[QB][D / 32];
   float m_run[QB], l_run[QB];
@@ -235,31 +227,28 @@ attn_fwd_bf16_kernel(Params p) {
     l_run[qb] = 0.f;
   }
 
-  const int n_tiles = (p.Skv + BN - 1) / BN;
-  gload(0);
-  swrite(0);
+  const int n_tiles = (p.Skv + C::BN - 1) / C::BN;
+  issue_tile(0, smem0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int key0 = j * BN;
-    const bool has_next = (j + 1) < n_tiles;
-    if (has_next) gload(key0 + BN);
-
-    const char* Ks = smem + (j & 1) * C::STAGE;
+  auto tile_step = [&](int j, const char* Ks, char* next) {
+    const int key0 = j * C::BN;
+    if (j + 1 < n_tiles) issue_tile(key0 + C::BN, next);
     const char* Vs = Ks + C::K_BYTES;
 
-    // ---- S^T = K Q^T for BN keys x (QB*32) queries
-    f32x16 s[QB][BN / 32];
+    // ---- S^T = K Q^T for 64 keys x (QB*32) queries
+    f32x16 s[QB][C::KB];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-      const int n = kb * 32 + l32;
-      const char* krow = Ks + n * C::KROW;
-      const int sw = swz<C::DCH>(n);
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
+      for (int kb = 0; kb < C::KB; ++kb) s[qb][kb] = f32x16{};
+    const char* kfrag = Ks + lane * 16;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((kk * 2 + hi) ^ sw) << 4));
+    for (int kk = 0; kk < C::KK; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kfrag + (kb * C::KK + kk) * 1024);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][kk], s[qb][kb], 0, 0, 0);
@@ -267,11 +256,11 @@ attn_fwd_bf16_kernel(Params p) {
     }
 
     // ---- tail mask: keys >= Skv get -inf (only the last tile can have them)
-    if (key0 + BN > p.Skv) {
+    if (key0 + C::BN > p.Skv) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
+        for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -279,62 +268,69 @@ attn_fwd_bf16_kernel(Params p) {
           }
     }
 
-    // ---- online softmax (base 2), P^T in bf16
-    bf16x8 pf[QB][BN / 32][2];
+    // ---- online softmax (base 2, lazy rescale), P^T in bf16
+    bf16x8 pf[QB][C::KB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = s[qb][0][0];
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-      mx = half_max(mx);
-      const float m_new = fmaxf(m_run[qb], mx * p.c);
-      const float alpha = fast_exp2(m_run[qb] - m_new);
-      m_run[qb] = m_new;
+      const float mt = half_max(mx) * p.c;
+      if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + CP_FWD_LAZY) != 0) {
+        const float m_new = fmaxf(m_run[qb], mt);
+        const float alpha = fast_exp2(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[qb][db] *= alpha;
+      }
+      const float mneg = -m_run[qb];
       float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(s[qb][kb][r], p.c, -m_new));
-          s[qb][kb][r] = e;
-          ls += e;
-        }
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int kk2 = 0; kk2 < 2; ++kk2) {
           bf16x8 t;
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) t[jj] = (__bf16)s[qb][kb][kk2 * 8 + jj];
+          for (int jj = 0; jj < 8; ++jj) {
+            const float e = fast_exp2(fmaf(s[qb][kb][kk2 * 8 + jj], p.c, mneg));
+            ls += e;  // float32 sum of the unrounded probabilities: LSE needs it
+            t[jj] = (__bf16)e;
+          }
           pf[qb][kb][kk2] = t;
         }
-      }
-      l_run[qb] = l_run[qb] * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) o[qb][db] *= alpha;
+      l_run[qb] += ls;
     }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T (V^T fragments via transposing LDS reads)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int d = db * 32 + l32;
-      const char* vrow = Vs + d * C::VROW;
-      const int sw = swz<C::KCH>(d);
+      const char* vb = Vs + (vlane ^ (db << 6));
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int kk2 = 0; kk2 < 2; ++kk2) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(vrow + (((kb * 4 + kk2 * 2 + hi) ^ sw) << 4));
+          const char* a0 = vb + (kb * 32 + kk2 * 16) * C::VROW;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
+          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * C::VROW));
+          const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                                   __builtin_bit_cast(bf16x4, hi4), 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][kk2], o[qb][db], 0, 0, 0);
         }
     }
 
-    if (has_next) swrite((j + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed in LDS
     __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile_step(j, smem0, smem1);
+    if (j + 1 < n_tiles) tile_step(j + 1, smem1, smem0);
   }
+
 
   // ---- epilogue: normalise, LSE, optional merge into the accumulator
 #pragma unroll
@@ -381,9 +377,8 @@ attn_fwd_bf16_kernel(Params p) {
 
 template <int D, bool ACC>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  // D = 64 uses 128-key tiles so that every thread has a (4 keys x 8 dims) V task.
-  constexpr int QB = CP_FWD_QB, NW = CP_FWD_NW, BN = (D == 64) ? 128 : CP_FWD_BN;
-  using C = Cfg<D, QB, BN, NW>;
+  constexpr int QB = CP_FWD_QB, NW = CP_FWD_NW;
+  using C = Cfg<D, QB, NW>;
   Params p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -399,8 +394,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
   p.n_wg = (int)n_wg;
   p.c = a.scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, BN, NW, ACC>), dim3(p.n_wg), dim3(C::NT), 0,
-                     stream, p);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, NW, ACC>), dim3(p.n_wg), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
