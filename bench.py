@@ -128,7 +128,12 @@ class Problem:
 
 
 def cpu_baseline(w: workloads.Workload, inp, target_s: float):
-    """Time the float64 oracle on whole heads of the same workload, ~target_s of CPU work."""
+    """Time the float64 oracle on the same workload for about target_s of CPU work.
+
+    Whole heads of the workload (all blocks, merged) are run through the oracle;
+    if the full workload takes less than target_s it is repeated, otherwise a
+    subset of heads is timed.
+    """
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -150,13 +155,41 @@ def cpu_baseline(w: workloads.Workload, inp, target_s: float):
         oracle.ring_attention(q[:, :, h0:h1], kb, vb, w.scale)
         return time.perf_counter() - t
 
-    t1 = run(0, 1)  # one head to size the sample
+    t1 = run(0, 1)  # one head, to size the sample
     n_heads = int(max(1, min(H, math.floor(target_s / max(t1, 1e-6)))))
-    t = run(0, n_heads) if n_heads > 1 else t1
-    flops = 4 * w.B * n_heads * w.Sq * w.Skv * w.D
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n_heads} of {H} heads x B={w.B} x Sq={w.Sq} x Skv={w.Skv} (all blocks, merged), "
-                      f"numpy float64, {t:.2f} s"}
+    passes, total = 0, 0.0
+    while True:
+        total += run(0, n_heads)
+        passes += 1
+        if n_heads < H or total >= 0.8 * target_s:
+            break
+    flops = 4 * w.B * n_heads * w.Sq * w.Skv * w.D * passes
+    what = f"{n_heads} of {H} heads" if n_heads < H else f"all {H} heads x {passes} passes"
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{what}, B={w.B} Sq={w.Sq} Skv={w.Skv} (every block, merged), numpy float64, "
+                      f"{total:.1f} s"}
+
+
+def hbm_traffic(w: workloads.Workload):
+    """HBM bytes per block-kernel launch from the committed counter summary.
+
+    profiles/attn_fwd_bf16_traffic.json holds FETCH_SIZE/WRITE_SIZE of one
+    launch (scaled by the same counters' reading for a copy of known size)
+    together with the SHA-256 of the kernel source they were taken from; the
+    figure is reported only while that source is unchanged.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json")
+    src = os.path.join(ROOT, "context_attention_dits_amd", "csrc", "attn_fwd_bf16.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(w.name)
+    if rec.get("kernel_source_sha256") != sha or not entry:
+        return None
+    return entry.get("hbm_bytes_per_launch")
 
 
 def main():
@@ -220,7 +253,7 @@ def main():
                    "merge": "separate" if args.separate_merge else "fused",
                    "pct_of_bf16_peak": round(100 * tflops / PEAK_TFLOPS["bf16"], 2)},
         "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": hbm_traffic(w),
                      "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel",
                      "us_per_launch": round(k_ms * 1e3, 2)},
         "cpu_baseline": cpu,

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import ctypes
 import os
 import shutil
 import subprocess
@@ -65,6 +66,12 @@ def build(out: Optional[str] = None, defines: Optional[Dict[str, str]] = None,
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # Resolve every symbol now (RTLD_NOW), so a missing kernel stub fails the build, not the first call.
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError(f"built library does not load: {e}") from e
     os.replace(tmp, out)
     return out
 

@@ -80,6 +80,9 @@ cp_status_t check_common(const void* q, Strides qs, Strides kvs, int dtype, int 
   cp_status_t st;
   if ((st = check_strides("q", qs, es, Sq, H, D)) != CP_OK) return st;
   if ((st = check_strides("k/v", kvs, es, 2, H, D)) != CP_OK) return st;
+  // K/V tiles are fetched through buffer descriptors with 32-bit offsets.
+  if (kvs.s > (int64_t(1) << 24))
+    return fail(CP_ERR_UNSUPPORTED, "k/v: sequence stride %lld exceeds 2^24 elements", (long long)kvs.s);
   if ((st = check_strides("out", os, 4, Sq, H, D)) != CP_OK) return st;
   return CP_OK;
 }

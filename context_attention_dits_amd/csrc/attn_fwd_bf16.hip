@@ -48,6 +48,8 @@
 //     computed on zeros and not stored.
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 #ifndef CP_FWD_QB
@@ -58,6 +60,12 @@
 #endif
 #ifndef CP_FWD_WPE
 #define CP_FWD_WPE 2  // minimum waves per SIMD the register budget must allow
+#endif
+#ifndef CP_FWD_SCHED
+#define CP_FWD_SCHED 7  // VALU ops scheduled between consecutive score MFMAs (0: no hints)
+#endif
+#ifndef CP_FWD_SCHED_PV
+#define CP_FWD_SCHED_PV 1  // pipeline the transposing V reads ahead of the PV MFMAs
 #endif
 #ifndef CP_FWD_LAZY
 #define CP_FWD_LAZY 8.0f  // rescale threshold on the row maximum, log2 units
@@ -74,10 +82,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(1))) void global_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Word 3 of a raw (unswizzled, untyped) buffer descriptor on gfx9-family GPUs.
+constexpr int kBufferFlags = 0x00020000;
 
 struct Params {
   const uint16_t* q;
@@ -107,6 +116,16 @@ __device__ __forceinline__ float half_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// 16 bytes per lane from global memory at base + voff into LDS at
+// lds + 16 * lane, through a raw buffer descriptor covering [base, base +
+// nbytes): lanes whose offset falls outside that range read nothing and
+// write zeros. base, nbytes and lds must be wave-uniform.
+__device__ __forceinline__ void buffer_to_lds16(const void* base, int nbytes, int voff, char* lds) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
 // Map the hardware workgroup id (dispatched round-robin over 8 XCDs) to a
 // logical tile id so that each XCD receives one contiguous range of tiles.
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
@@ -132,6 +151,7 @@ struct Cfg {
   static constexpr int V_PER_WAVE = (BN / V_RPI) / NW;
   static_assert(D == 64 || D == 128, "head dim");
   static_assert((KB * KK) % NW == 0 && (BN / V_RPI) % NW == 0, "load split");
+  static_assert(KK % K_PER_WAVE == 0, "a wave's K blocks share one key block");
 };
 
 // XOR applied to a V row's 16-byte chunk index: the 8 rows that one
@@ -151,10 +171,12 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                                amdgpu_waves_per_eu(CP_FWD_WPE)))
 attn_fwd_bf16_kernel(Params p) {
   using C = Cfg<D, QB, NW>;
-  // One array per LDS stage, so the compiler can tell the stage being read
-  // from the stage the next tile is being loaded into.
-  __shared__ __attribute__((aligned(1024))) char smem0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char smem1[C::STAGE];
+  // Separate arrays per buffer, so the compiler can tell the buffers being
+  // read from the ones the next tiles are being loaded into.
+  __shared__ __attribute__((aligned(1024))) char kbuf0[C::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[C::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[C::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[C::V_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -169,6 +191,7 @@ attn_fwd_bf16_kernel(Params p) {
 
   const uint16_t* kbase = p.k + b * p.kv_sb + h * p.kv_sh;
   const uint16_t* vbase = p.v + b * p.kv_sb + h * p.kv_sh;
+  const int n_tiles = (p.Skv + C::BN - 1) / C::BN;
 
   // ---- Q (B operand of S^T = K Q^T): lane holds query l32, dims kk*16 + hi*8 .. +7
   bf16x8 qf[QB][C::KK];
@@ -186,25 +209,44 @@ attn_fwd_bf16_kernel(Params p) {
     }
   }
 
-  // ---- global -> LDS for one tile (this wave's share of the 1 KB blocks)
-  auto issue_tile = [&](int key0, char* Ks) {
-    char* Vs = Ks + C::K_BYTES;
+  // ---- global -> LDS (this wave's share of a tile's 1 KB blocks) through
+  // buffer loads: a scalar descriptor based at the tile's first key whose
+  // range ends at key Skv, plus a per-lane byte offset that is the same for
+  // every tile. Keys past Skv fall outside the range, are never read and
+  // arrive in LDS as zeros. Tile indices past the end are clamped to the last
+  // tile so the pipeline can issue loads unconditionally; those copies are
+  // never used.
+  const int64_t row_bytes = p.kv_ss * 2;
+  int k_voff;  // K block m = (kb, kk): key kb*32 + l32, 16-byte chunk 2*kk + hi
+  {
+    const int kb = (wave * C::K_PER_WAVE) / C::KK;
+    k_voff = (int)((kb * 32 + l32) * row_bytes) + hi * 16;
+  }
+  int v_voff[C::V_PER_WAVE];  // V rows m*V_RPI + lane/V_LPR, swizzled chunks
+#pragma unroll
+  for (int i = 0; i < C::V_PER_WAVE; ++i) {
+    const int r = (wave * C::V_PER_WAVE + i) * C::V_RPI + lane / C::V_LPR;
+    v_voff[i] = (int)(r * row_bytes) + (((lane % C::V_LPR) ^ vswz<D>(r)) << 4);
+  }
+  auto issue_k = [&](int t, char* Ks) {
+    const int key0 = min(t, n_tiles - 1) * C::BN;
+    const uint16_t* base = kbase + (int64_t)key0 * p.kv_ss;
+    const int nbytes = (int)min((int64_t)(p.Skv - key0) * row_bytes, (int64_t)0x7fffffff);
 #pragma unroll
     for (int i = 0; i < C::K_PER_WAVE; ++i) {
-      const int m = wave * C::K_PER_WAVE + i;  // K block = (kb, kk)
-      const int kb = m / C::KK, kk = m % C::KK;
-      const int key = min(key0 + kb * 32 + l32, p.Skv - 1);
-      const uint16_t* g = kbase + (int64_t)key * p.kv_ss + (2 * kk + hi) * 8;
-      __builtin_amdgcn_global_load_lds((global_void*)g, (lds_void*)(Ks + m * 1024), 16, 0, 0);
+      const int m = wave * C::K_PER_WAVE + i;  // K block = (kb, kk); the wave's blocks share kb
+      const int kk = m % C::KK;
+      buffer_to_lds16(base, nbytes, k_voff + kk * 32, Ks + m * 1024);
     }
+  };
+  auto issue_v = [&](int t, char* Vs) {
+    const int key0 = min(t, n_tiles - 1) * C::BN;
+    const uint16_t* base = vbase + (int64_t)key0 * p.kv_ss;
+    const int nbytes = (int)min((int64_t)(p.Skv - key0) * row_bytes, (int64_t)0x7fffffff);
 #pragma unroll
     for (int i = 0; i < C::V_PER_WAVE; ++i) {
-      const int m = wave * C::V_PER_WAVE + i;  // V rows m*V_RPI ..
-      const int r = m * C::V_RPI + lane / C::V_LPR;
-      const int ch = (lane % C::V_LPR) ^ vswz<D>(r);
-      const int key = min(key0 + r, p.Skv - 1);
-      const uint16_t* g = vbase + (int64_t)key * p.kv_ss + ch * 8;
-      __builtin_amdgcn_global_load_lds((global_void*)g, (lds_void*)(Vs + m * 1024), 16, 0, 0);
+      const int m = wave * C::V_PER_WAVE + i;
+      buffer_to_lds16(base, nbytes, v_voff[i], Vs + m * 1024);
     }
   };
 
@@ -227,18 +269,8 @@ attn_fwd_bf16_kernel(Params p) {
     l_run[qb] = 0.f;
   }
 
-  const int n_tiles = (p.Skv + C::BN - 1) / C::BN;
-  issue_tile(0, smem0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  auto tile_step = [&](int j, const char* Ks, char* next) {
-    const int key0 = j * C::BN;
-    if (j + 1 < n_tiles) issue_tile(key0 + C::BN, next);
-    const char* Vs = Ks + C::K_BYTES;
-
-    // ---- S^T = K Q^T for 64 keys x (QB*32) queries
-    f32x16 s[QB][C::KB];
+  // S^T = K Q^T for one 64-key tile held in LDS.
+  auto scores = [&](const char* Ks, f32x16 (&s)[QB][C::KB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -254,38 +286,69 @@ attn_fwd_bf16_kernel(Params p) {
           s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][kk], s[qb][kb], 0, 0, 0);
       }
     }
+  };
 
-    // ---- tail mask: keys >= Skv get -inf (only the last tile can have them)
-    if (key0 + C::BN > p.Skv) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= p.Skv) s[qb][kb][r] = -INFINITY;
-          }
+  // One pipelined step over tile j: the scores of tile j+1 are computed on
+  // the matrix cores while tile j's softmax runs on the vector ALUs; then
+  // O += V_j^T P_j. On entry s_cur holds tile j's scores; on exit s_next
+  // holds tile j+1's. K runs one tile ahead of V in the LDS buffers.
+  auto step = [&](auto last_tag, int j, f32x16 (&s_cur)[QB][C::KB], f32x16 (&s_next)[QB][C::KB],
+                  const char* k_read, char* k_write, const char* v_read, char* v_write) {
+    constexpr bool LAST = decltype(last_tag)::value;  // the final tile: mask, no next tile
+    if constexpr (!LAST) {
+      issue_k(j + 2, k_write);
+      issue_v(j + 1, v_write);
     }
 
-    // ---- online softmax (base 2, lazy rescale), P^T in bf16
-    bf16x8 pf[QB][C::KB][2];
+    // tail mask: keys >= Skv get -inf (only the last tile can have them)
+    if constexpr (LAST) {
+      const int key0 = j * C::BN;
+      if (key0 + C::BN > p.Skv) {
+        // This lane holds keys key0 + 4*hi + (kb*32 + 8*(r/4) + r%4).
+        const int lim = p.Skv - key0 - 4 * hi;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_cur[qb][kb][r] = -INFINITY;
+      }
+    }
+
+    // row maxima of tile j; raise the running maximum only when a row's
+    // maximum grows by more than 2^CP_FWD_LAZY (then O and l are rescaled)
+    float alpha[QB];
+    bool rescale = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[qb][0][0];
+      float mx = s_cur[qb][0][0];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[qb][kb][r]);
       const float mt = half_max(mx) * p.c;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + CP_FWD_LAZY) != 0) {
-        const float m_new = fmaxf(m_run[qb], mt);
-        const float alpha = fast_exp2(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
+      const bool need = __builtin_amdgcn_ballot_w64(mt > m_run[qb] + CP_FWD_LAZY) != 0;
+      const float m_new = need ? fmaxf(m_run[qb], mt) : m_run[qb];
+      alpha[qb] = fast_exp2(m_run[qb] - m_new);  // 1 when the maximum is kept
+      rescale |= need;
+      m_run[qb] = m_new;
+    }
+    if (rescale) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[qb][db] *= alpha;
+      for (int qb = 0; qb < QB; ++qb) {
+        l_run[qb] *= alpha[qb];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[qb][db] *= alpha[qb];
       }
+    }
+
+    // Scores of tile j+1 on the matrix cores, interleaved with tile j's
+    // exponentials on the vector ALUs.
+    if constexpr (!LAST) scores(k_read, s_next);
+    bf16x8 pf[QB][C::KB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       const float mneg = -m_run[qb];
       float ls = 0.f;
 #pragma unroll
@@ -295,7 +358,7 @@ attn_fwd_bf16_kernel(Params p) {
           bf16x8 t;
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
-            const float e = fast_exp2(fmaf(s[qb][kb][kk2 * 8 + jj], p.c, mneg));
+            const float e = fast_exp2(fmaf(s_cur[qb][kb][kk2 * 8 + jj], p.c, mneg));
             ls += e;  // float32 sum of the unrounded probabilities: LSE needs it
             t[jj] = (__bf16)e;
           }
@@ -303,11 +366,24 @@ attn_fwd_bf16_kernel(Params p) {
         }
       l_run[qb] += ls;
     }
+#if CP_FWD_SCHED
+    if constexpr (!LAST) {
+    // 16*QB score MFMAs, their 16 fragment reads and ~112*QB VALU ops:
+    // keep two reads ahead and spread the VALU work between the MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < C::KB * C::KK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, CP_FWD_SCHED, 0);
+    }
+    }
+#endif
 
-    // ---- O^T += V^T P^T (V^T fragments via transposing LDS reads)
+    // O^T += V^T P^T (V^T fragments via transposing LDS reads)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const char* vb = Vs + (vlane ^ (db << 6));
+      const char* vb = v_read + (vlane ^ (db << 6));
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -323,12 +399,45 @@ attn_fwd_bf16_kernel(Params p) {
         }
     }
 
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed in LDS
-    __syncthreads();
+#if CP_FWD_SCHED_PV
+    // PV: keep four V^T fragments (eight transposing reads) ahead of the MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < (D / 32) * C::KB * 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#endif
+
+    if constexpr (!LAST) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads for the next steps have landed in LDS
+      __syncthreads();
+    }
   };
-  for (int j = 0; j < n_tiles; j += 2) {
-    tile_step(j, smem0, smem1);
-    if (j + 1 < n_tiles) tile_step(j + 1, smem1, smem0);
+
+  // prologue: K_0, V_0, K_1 in flight; scores of tile 0
+  issue_k(0, kbuf0);
+  issue_v(0, vbuf0);
+  issue_k(1, kbuf1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 sa[QB][C::KB], sb[QB][C::KB];
+  scores(kbuf0, sa);
+
+  // Steady state two tiles at a time (the buffers swap roles each tile), then
+  // the last one or two tiles, the final one masked.
+  using Mid = std::integral_constant<bool, false>;
+  using Last = std::integral_constant<bool, true>;
+  int j = 0;
+  for (; j + 2 < n_tiles; j += 2) {
+    step(Mid{}, j, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
+    step(Mid{}, j + 1, sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
+  }
+  if (j + 2 == n_tiles) {
+    step(Mid{}, j, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
+    step(Last{}, j + 1, sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
+  } else {
+    step(Last{}, j, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
   }
 
 

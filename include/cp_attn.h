@@ -19,7 +19,8 @@
  *     of the tensor's own dtype; NULL means contiguous [B, S, H, D].
  *   - LSE tensors are float32 [B, H, Sq], contiguous, natural log.
  *   - Device pointers must be 16-byte aligned and every stride times the
- *     element size must be a multiple of 16 bytes.
+ *     element size must be a multiple of 16 bytes. The K/V sequence stride
+ *     must not exceed 2^24 elements.
  *   - The caller allocates and owns every buffer (inputs, outputs and any
  *     workspace). The library keeps no pointer after a call returns and
  *     allocates no device memory.
