@@ -22,7 +22,8 @@ from ._lib import (CP_BF16, CP_BLOCK_ACCUMULATE, CP_ERR_HIP, CP_ERR_INVALID_ARG,
                    CP_REGROUP_SEQ_TO_HEAD, CP_RING_ANYTHING, CP_RING_SEPARATE_MERGE, STATUS_NAMES)
 
 __all__ = [
-    "CpAttnError", "load", "cp_abi_version", "cp_last_error", "cp_attn_block_fwd", "cp_lse_merge",
+    "CpAttnError", "load", "cp_abi_version", "cp_last_error", "cp_attn_set_fwd_waves", "cp_attn_block_fwd",
+    "cp_lse_merge",
     "cp_ring_attention", "cp_ring_attention_workspace_size", "cp_ulysses_regroup",
 ]
 
@@ -101,6 +102,14 @@ def cp_abi_version() -> int:
 
 def cp_last_error() -> str:
     return _lib.load().cp_last_error().decode()
+
+
+def cp_attn_set_fwd_waves(waves: int) -> int:
+    """Workgroup shape of the bfloat16 block kernel (0 auto, 4 or 8); returns the previous one."""
+    prev = _lib.load().cp_attn_set_fwd_waves(int(waves))
+    if prev < 0:
+        raise ValueError(f"cp_attn_set_fwd_waves: waves must be 0, 4 or 8, got {waves}")
+    return prev
 
 
 def cp_attn_block_fwd(q, k, v, out, lse, scale: Optional[float] = None, flags: int = 0, stream=None):

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "cp_attn.h"
@@ -16,6 +17,7 @@ namespace {
 using cpattn::Strides;
 
 thread_local std::string g_err;
+std::atomic<int> g_fwd_waves{0};  // cp_attn_set_fwd_waves
 
 cp_status_t fail(cp_status_t st, const char* fmt, ...) {
   char buf[512];
@@ -110,6 +112,7 @@ cp_status_t run_block(const void* q, Strides qs, const void* k, const void* v, S
   a.B = B; a.H = H; a.D = D; a.Sq = Sq; a.Skv = Skv;
   a.scale = scale;
   a.accumulate = accumulate;
+  a.waves = g_fwd_waves.load(std::memory_order_relaxed);
   if (dtype == CP_BF16) return hip_status(cpattn::launch_attn_fwd_bf16(a, stream), "attn_fwd_bf16");
   return hip_status(cpattn::launch_attn_fwd_f32(a, stream), "attn_fwd_f32");
 }
@@ -127,6 +130,11 @@ extern "C" {
 int cp_abi_version(void) { return CP_ATTN_ABI_VERSION; }
 
 const char* cp_last_error(void) { return g_err.c_str(); }
+
+int cp_attn_set_fwd_waves(int waves) {
+  if (waves != 0 && waves != 4 && waves != 8) return -1;
+  return g_fwd_waves.exchange(waves);
+}
 
 cp_status_t cp_attn_block_fwd(const void* q, const int64_t* q_strides, const void* k, const void* v,
                               const int64_t* kv_strides, int dtype, int B, int H, int D, int Sq,

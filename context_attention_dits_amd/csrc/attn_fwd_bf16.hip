@@ -56,7 +56,7 @@
 #define CP_FWD_QB 1  // 32-query blocks per wave
 #endif
 #ifndef CP_FWD_NW
-#define CP_FWD_NW 4  // waves per workgroup
+#define CP_FWD_NW 0  // default workgroup shape for D = 128: 4, 8 (ping-pong), or 0 to choose per launch
 #endif
 #ifndef CP_FWD_WPE
 #define CP_FWD_WPE 2  // minimum waves per SIMD the register budget must allow
@@ -147,6 +147,8 @@ struct Cfg {
   static constexpr int STAGE = K_BYTES + V_BYTES;
   static constexpr int V_RPI = 1024 / VROW;       // V rows per 1 KB direct load
   static constexpr int V_LPR = VROW / 16;         // lanes per V row
+  static constexpr bool PINGPONG = (NW == 8);     // two wave groups half a step apart
+  static constexpr int NBUF = PINGPONG ? 3 : 2;   // LDS buffers per operand
   static constexpr int K_PER_WAVE = KB * KK / NW;
   static constexpr int V_PER_WAVE = (BN / V_RPI) / NW;
   static_assert(D == 64 || D == 128, "head dim");
@@ -166,6 +168,23 @@ __device__ __forceinline__ int vswz(int r) {
   }
 }
 
+// A batch of global->LDS loads handed to a compute phase, with its
+// instruction count known at compile time (for the issue schedule).
+template <int N, typename F>
+struct Loads {
+  static constexpr int count = N;
+  F f;
+  __device__ __forceinline__ void operator()() const { f(); }
+};
+struct NoLoads {
+  static constexpr int count = 0;
+  __device__ __forceinline__ void operator()() const {}
+};
+template <int N, typename F>
+__device__ __forceinline__ Loads<N, F> make_loads(F f) {
+  return Loads<N, F>{f};
+}
+
 template <int D, int QB, int NW, bool ACC>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                                amdgpu_waves_per_eu(CP_FWD_WPE)))
@@ -177,6 +196,9 @@ attn_fwd_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char kbuf1[C::K_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[C::V_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf1[C::V_BYTES];
+  // third stage, ping-pong only
+  __shared__ __attribute__((aligned(1024))) char kbuf2[C::NBUF > 2 ? C::K_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char vbuf2[C::NBUF > 2 ? C::V_BYTES : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -213,39 +235,47 @@ attn_fwd_bf16_kernel(Params p) {
   // buffer loads: a scalar descriptor based at the tile's first key whose
   // range ends at key Skv, plus a per-lane byte offset that is the same for
   // every tile. Keys past Skv fall outside the range, are never read and
-  // arrive in LDS as zeros. Tile indices past the end are clamped to the last
-  // tile so the pipeline can issue loads unconditionally; those copies are
-  // never used.
+  // arrive in LDS as zeros.
   const int64_t row_bytes = p.kv_ss * 2;
+  const int lw = wave;
   int k_voff;  // K block m = (kb, kk): key kb*32 + l32, 16-byte chunk 2*kk + hi
   {
-    const int kb = (wave * C::K_PER_WAVE) / C::KK;
+    const int kb = (lw * C::K_PER_WAVE) / C::KK;
     k_voff = (int)((kb * 32 + l32) * row_bytes) + hi * 16;
   }
   int v_voff[C::V_PER_WAVE];  // V rows m*V_RPI + lane/V_LPR, swizzled chunks
 #pragma unroll
   for (int i = 0; i < C::V_PER_WAVE; ++i) {
-    const int r = (wave * C::V_PER_WAVE + i) * C::V_RPI + lane / C::V_LPR;
+    const int r = (lw * C::V_PER_WAVE + i) * C::V_RPI + lane / C::V_LPR;
     v_voff[i] = (int)(r * row_bytes) + (((lane % C::V_LPR) ^ vswz<D>(r)) << 4);
   }
+  // Source of tile t: a base pointer at its first key and the byte range up
+  // to key Skv. Tiles past the end get an empty range (nothing is read; the
+  // unused buffer they target receives zeros), so the pipeline can issue
+  // loads unconditionally.
+  auto tile_range = [&](int t, const uint16_t* head, const uint16_t*& base, int& nbytes) {
+    base = head + (int64_t)(min(t, n_tiles - 1) * C::BN) * p.kv_ss;
+    const int64_t avail = (int64_t)(p.Skv - t * C::BN) * row_bytes;  // <= 0 past the end
+    nbytes = (int)max((int64_t)0, min(avail, (int64_t)0x7fffffff));
+  };
   auto issue_k = [&](int t, char* Ks) {
-    const int key0 = min(t, n_tiles - 1) * C::BN;
-    const uint16_t* base = kbase + (int64_t)key0 * p.kv_ss;
-    const int nbytes = (int)min((int64_t)(p.Skv - key0) * row_bytes, (int64_t)0x7fffffff);
+    const uint16_t* base;
+    int nbytes;
+    tile_range(t, kbase, base, nbytes);
 #pragma unroll
     for (int i = 0; i < C::K_PER_WAVE; ++i) {
-      const int m = wave * C::K_PER_WAVE + i;  // K block = (kb, kk); the wave's blocks share kb
+      const int m = lw * C::K_PER_WAVE + i;  // K block = (kb, kk); the wave's blocks share kb
       const int kk = m % C::KK;
       buffer_to_lds16(base, nbytes, k_voff + kk * 32, Ks + m * 1024);
     }
   };
   auto issue_v = [&](int t, char* Vs) {
-    const int key0 = min(t, n_tiles - 1) * C::BN;
-    const uint16_t* base = vbase + (int64_t)key0 * p.kv_ss;
-    const int nbytes = (int)min((int64_t)(p.Skv - key0) * row_bytes, (int64_t)0x7fffffff);
+    const uint16_t* base;
+    int nbytes;
+    tile_range(t, vbase, base, nbytes);
 #pragma unroll
     for (int i = 0; i < C::V_PER_WAVE; ++i) {
-      const int m = wave * C::V_PER_WAVE + i;
+      const int m = lw * C::V_PER_WAVE + i;
       buffer_to_lds16(base, nbytes, v_voff[i], Vs + m * 1024);
     }
   };
@@ -288,17 +318,18 @@ attn_fwd_bf16_kernel(Params p) {
     }
   };
 
-  // One pipelined step over tile j: the scores of tile j+1 are computed on
-  // the matrix cores while tile j's softmax runs on the vector ALUs; then
-  // O += V_j^T P_j. On entry s_cur holds tile j's scores; on exit s_next
-  // holds tile j+1's. K runs one tile ahead of V in the LDS buffers.
-  auto step = [&](auto last_tag, int j, f32x16 (&s_cur)[QB][C::KB], f32x16 (&s_next)[QB][C::KB],
-                  const char* k_read, char* k_write, const char* v_read, char* v_write) {
+  // Probabilities of the tile whose PV product is pending, as the bf16 B
+  // operand of O^T += V^T P^T (key order as the score accumulators hold it).
+  bf16x8 pf[QB][C::KB][2];
+
+  // Softmax of tile j: tail mask, row maxima and lazy rescale, exponentials
+  // into pf and the row sums. Fused form: the scores of tile j+1 (from k_read
+  // into s_next) run on the matrix cores interleaved with the exponentials on
+  // the vector ALUs. On entry s_cur holds tile j's scores.
+  auto half_a = [&](auto last_tag, auto fuse_tag, int j, f32x16 (&s_cur)[QB][C::KB],
+                    f32x16 (&s_next)[QB][C::KB], const char* k_read, auto loads) {
     constexpr bool LAST = decltype(last_tag)::value;  // the final tile: mask, no next tile
-    if constexpr (!LAST) {
-      issue_k(j + 2, k_write);
-      issue_v(j + 1, v_write);
-    }
+    constexpr bool FUSE = decltype(fuse_tag)::value && !LAST;  // next tile's scores computed here
 
     // tail mask: keys >= Skv get -inf (only the last tile can have them)
     if constexpr (LAST) {
@@ -342,11 +373,9 @@ attn_fwd_bf16_kernel(Params p) {
         for (int db = 0; db < D / 32; ++db) o[qb][db] *= alpha[qb];
       }
     }
+    loads();
 
-    // Scores of tile j+1 on the matrix cores, interleaved with tile j's
-    // exponentials on the vector ALUs.
-    if constexpr (!LAST) scores(k_read, s_next);
-    bf16x8 pf[QB][C::KB][2];
+    if constexpr (FUSE) scores(k_read, s_next);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float mneg = -m_run[qb];
@@ -366,8 +395,21 @@ attn_fwd_bf16_kernel(Params p) {
         }
       l_run[qb] += ls;
     }
+    if constexpr (!decltype(fuse_tag)::value) {
+      // Split form: pin the probabilities and row sums here, so the compiler
+      // cannot sink their arithmetic past the barrier into the MFMA half.
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        asm volatile("" : "+v"(l_run[qb]));
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          asm volatile("" : "+v"(pf[qb][kb][0]));
+          asm volatile("" : "+v"(pf[qb][kb][1]));
+        }
+      }
+    }
 #if CP_FWD_SCHED
-    if constexpr (!LAST) {
+    if constexpr (FUSE) {
     // 16*QB score MFMAs, their 16 fragment reads and ~112*QB VALU ops:
     // keep two reads ahead and spread the VALU work between the MFMAs.
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -379,8 +421,11 @@ attn_fwd_bf16_kernel(Params p) {
     }
     }
 #endif
+  };
 
-    // O^T += V^T P^T (V^T fragments via transposing LDS reads)
+  // Second half: O^T += V^T P^T with the V tile in v_read (V^T fragments via
+  // transposing LDS reads).
+  auto half_b = [&](const char* v_read) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const char* vb = v_read + (vlane ^ (db << 6));
@@ -398,9 +443,8 @@ attn_fwd_bf16_kernel(Params p) {
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][kk2], o[qb][db], 0, 0, 0);
         }
     }
-
 #if CP_FWD_SCHED_PV
-    // PV: keep four V^T fragments (eight transposing reads) ahead of the MFMAs.
+    // keep four V^T fragments (eight transposing reads) ahead of the MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
     for (int i = 0; i < (D / 32) * C::KB * 2; ++i) {
@@ -408,38 +452,173 @@ attn_fwd_bf16_kernel(Params p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
 #endif
-
-    if constexpr (!LAST) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads for the next steps have landed in LDS
-      __syncthreads();
-    }
   };
 
-  // prologue: K_0, V_0, K_1 in flight; scores of tile 0
+  // Matrix-core half of a ping-pong step: O^T += V_j^T P_j^T from v_read and,
+  // unless tile j is the last, the scores of tile j+1 from k_read into s_next.
+  // Only LDS reads and MFMAs: the vector ALU work of the step is in half_a.
+  auto half_m = [&](auto last_tag, f32x16 (&s_next)[QB][C::KB], const char* k_read, const char* v_read) {
+    constexpr bool LAST = decltype(last_tag)::value;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const char* vb = v_read + (vlane ^ (db << 6));
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+          const char* a0 = vb + (kb * 32 + kk2 * 16) * C::VROW;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
+          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * C::VROW));
+          const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                                   __builtin_bit_cast(bf16x4, hi4), 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][kk2], o[qb][db], 0, 0, 0);
+        }
+    }
+    if constexpr (!LAST) scores(k_read, s_next);
+#if CP_FWD_SCHED_PV
+    // Keep the LDS reads ahead of the MFMAs: eight reads up front, then two
+    // per MFMA, then one, until the reads run out.
+    constexpr int n_mfma = QB * ((D / 32) * C::KB * 2 + (LAST ? 0 : C::KB * C::KK));
+    constexpr int n_rd = (D / 32) * C::KB * 4 + (LAST ? 0 : C::KB * C::KK);
+    constexpr int pre = n_rd < 8 ? n_rd : 8;
+    constexpr int two = (n_rd - pre) / 2 < n_mfma ? (n_rd - pre) / 2 : n_mfma;
+    constexpr int one = n_rd - pre - 2 * two;
+    __builtin_amdgcn_sched_group_barrier(0x100, pre, 0);
+#pragma unroll
+    for (int i = 0; i < n_mfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < two) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (i < two + one) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#endif
+  };
+
+  // Workgroup barrier after this wave's LDS reads have completed and all but
+  // its `pending` most recent global->LDS loads have landed (loads complete in
+  // issue order). The memory clobbers keep the compiler from moving LDS
+  // accesses across it.
+  auto sync = [&](auto pending_tag) {
+    constexpr int PENDING = decltype(pending_tag)::value;  // 63: no wait on loads
+    static_assert(PENDING >= 0 && PENDING < 64, "vmcnt field");
+    // s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
+    __builtin_amdgcn_s_waitcnt(0x0070 | (PENDING & 15) | ((PENDING >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  using Pend0 = std::integral_constant<int, 0>;
+  using PendAll = std::integral_constant<int, 63>;
+  using Mid = std::integral_constant<bool, false>;
+  using Last = std::integral_constant<bool, true>;
+
+  using Fused = std::integral_constant<bool, true>;
+  using Split = std::integral_constant<bool, false>;
+
+  // prologue: K_0, V_0, K_1 in flight; scores of tile 0. K_j always lives in
+  // kbuf(j % 2) and V_j in vbuf(j % 2).
   issue_k(0, kbuf0);
   issue_v(0, vbuf0);
   issue_k(1, kbuf1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  f32x16 sa[QB][C::KB], sb[QB][C::KB];
+  sync(Pend0{});
+  f32x16 sa[QB][C::KB];
   scores(kbuf0, sa);
 
-  // Steady state two tiles at a time (the buffers swap roles each tile), then
-  // the last one or two tiles, the final one masked.
-  using Mid = std::integral_constant<bool, false>;
-  using Last = std::integral_constant<bool, true>;
   int j = 0;
-  for (; j + 2 < n_tiles; j += 2) {
-    step(Mid{}, j, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
-    step(Mid{}, j + 1, sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
-  }
-  if (j + 2 == n_tiles) {
-    step(Mid{}, j, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
-    step(Last{}, j + 1, sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
+  if constexpr (!C::PINGPONG) {
+    sync(Pend0{});  // every wave is done with K_0 before K_2 overwrites it
+    f32x16 sb[QB][C::KB];
+    // One step over tile j: loads of K_{j+2} and V_{j+1} are issued, then
+    // the fused softmax / next scores and the PV product run, then one
+    // barrier. The score registers swap roles each tile, so the loop runs two
+    // tiles at a time; the final tile is masked.
+    auto step = [&](auto last_tag, int jj, f32x16 (&s_cur)[QB][C::KB], f32x16 (&s_next)[QB][C::KB],
+                    const char* k_read, char* k_write, const char* v_read, char* v_write) {
+      constexpr bool LAST = decltype(last_tag)::value;
+      if constexpr (!LAST) {
+        issue_k(jj + 2, k_write);
+        issue_v(jj + 1, v_write);
+      }
+      half_a(last_tag, Fused{}, jj, s_cur, s_next, k_read, NoLoads{});
+      half_b(v_read);
+      if constexpr (!LAST) sync(Pend0{});
+    };
+    for (; j + 2 < n_tiles; j += 2) {
+      step(Mid{}, j, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
+      step(Mid{}, j + 1, sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
+    }
+    if (j + 2 == n_tiles) {
+      step(Mid{}, j, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
+      step(Last{}, j + 1, sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
+    } else {
+      step(Last{}, j, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
+    }
   } else {
-    step(Last{}, j, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
+    // Ping-pong: waves [0, NW/2) (group A) and [NW/2, NW) (group B) share
+    // the SIMDs pairwise (wave w and w + NW/2 on one SIMD) and run the same
+    // program one interval apart, so that on each SIMD one wave's softmax
+    // (vector ALUs) runs while the other wave's matrix-core half (LDS reads
+    // and MFMAs only) runs. Intervals end with a workgroup barrier. Group A
+    // runs the softmax of tile j in interval 2j and its MFMA half (PV of tile
+    // j, scores of tile j+1) in 2j+1; group B one interval later. Three LDS
+    // stages per operand: tile t lives in buffer t % 3.
+    // During its softmax of tile j every wave issues its share of K_{j+2} and
+    // V_{j+1}, whose buffers were last read in interval 2j-2, and which are
+    // first read in interval 2j+3. Group A waits for its loads one softmax
+    // later (all but the newest at the end of interval 2j+2); group B, which
+    // issues in 2j+1, waits for all its loads at the end of its MFMA half in
+    // 2j+2.
+    using PendL = std::integral_constant<int, C::K_PER_WAVE + C::V_PER_WAVE>;
+    const bool grp_b = wave >= NW / 2;
+    if (grp_b) sync(Pend0{});  // group B idles in interval 0
+    char* const kb3[3] = {kbuf0, kbuf1, kbuf2};
+    char* const vb3[3] = {vbuf0, vbuf1, vbuf2};
+    // one tile; c = j % 3, known at compile time in the unrolled loop
+    auto step = [&](auto last_tag, auto c_tag, int jj) {
+      constexpr bool LAST = decltype(last_tag)::value;
+      constexpr int c = decltype(c_tag)::value;
+      const char* k_read = kb3[(c + 1) % 3];
+      const char* v_read = vb3[c];
+      if constexpr (!LAST) {
+        char* k_write = kb3[(c + 2) % 3];
+        char* v_write = vb3[(c + 1) % 3];
+        half_a(last_tag, Split{}, jj, sa, sa, k_read, make_loads<C::K_PER_WAVE + C::V_PER_WAVE>([&] {
+                 issue_k(jj + 2, k_write);
+                 issue_v(jj + 1, v_write);
+               }));
+        if (grp_b) sync(PendAll{});
+        else sync(PendL{});
+        half_m(last_tag, sa, k_read, v_read);
+        if (grp_b) sync(Pend0{});
+        else sync(PendAll{});
+      } else {
+        // The last barrier ends interval 2n-2: group A passes it after its
+        // last softmax, group B after its last MFMA half but one.
+        half_a(last_tag, Split{}, jj, sa, sa, k_read, NoLoads{});
+        if (!grp_b) sync(Pend0{});
+        half_m(last_tag, sa, k_read, v_read);
+      }
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    for (; j + 3 < n_tiles; j += 3) {
+      step(Mid{}, C0{}, j);
+      step(Mid{}, C1{}, j + 1);
+      step(Mid{}, C2{}, j + 2);
+    }
+    if (j + 3 == n_tiles) {
+      step(Mid{}, C0{}, j);
+      step(Mid{}, C1{}, j + 1);
+      step(Last{}, C2{}, j + 2);
+    } else if (j + 2 == n_tiles) {
+      step(Mid{}, C0{}, j);
+      step(Last{}, C1{}, j + 1);
+    } else {
+      step(Last{}, C0{}, j);
+    }
   }
-
 
   // ---- epilogue: normalise, LSE, optional merge into the accumulator
 #pragma unroll
@@ -484,9 +663,9 @@ attn_fwd_bf16_kernel(Params p) {
   }
 }
 
-template <int D, bool ACC>
+template <int D, int NW, bool ACC>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  constexpr int QB = CP_FWD_QB, NW = CP_FWD_NW;
+  constexpr int QB = CP_FWD_QB;
   using C = Cfg<D, QB, NW>;
   Params p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -509,9 +688,33 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Workgroup shape for one launch. The ping-pong kernel (8 waves, 256 query
+// rows, one workgroup per CU) is the faster one per workgroup; the 4-wave
+// kernel (128 rows, two workgroups per CU) drains a nearly empty last round
+// of workgroups faster, since a workgroup alone on a CU runs at full speed.
+// So: ping-pong unless its grid is under four rounds of 256 workgroups and
+// its last round is less than half full.
+int pick_waves(const FwdArgs& a) {
+  if (a.D != 128) return 4;
+  if (a.waves != 0) return a.waves;
+  if (CP_FWD_NW != 0) return CP_FWD_NW;
+  const int64_t n_wg8 = (int64_t)((a.Sq + 255) / 256) * a.H * a.B;
+  const int64_t rounds = (n_wg8 + 255) / 256, last = n_wg8 - (rounds - 1) * 256;
+  return (rounds < 4 && rounds > 1 && last < 128) ? 4 : 8;
+}
+
+template <int D>
+hipError_t launch_dn(const FwdArgs& a, hipStream_t stream) {
+  if constexpr (D == 128) {
+    if (pick_waves(a) == 8)
+      return a.accumulate ? launch_d<D, 8, true>(a, stream) : launch_d<D, 8, false>(a, stream);
+  }
+  return a.accumulate ? launch_d<D, 4, true>(a, stream) : launch_d<D, 4, false>(a, stream);
+}
+
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  if (a.D == 128) return a.accumulate ? launch_d<128, true>(a, stream) : launch_d<128, false>(a, stream);
-  if (a.D == 64) return a.accumulate ? launch_d<64, true>(a, stream) : launch_d<64, false>(a, stream);
+  if (a.D == 128) return launch_dn<128>(a, stream);
+  if (a.D == 64) return launch_dn<64>(a, stream);
   return hipErrorInvalidValue;
 }
 

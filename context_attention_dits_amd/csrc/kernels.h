@@ -22,6 +22,7 @@ struct FwdArgs {
   int B, H, D, Sq, Skv;
   float scale;
   bool accumulate;  // merge into (out, lse) instead of overwriting
+  int waves;        // bf16 workgroup shape: 4, 8, or 0 to choose per launch
 };
 
 // Partial attention of Q against one K/V block (Skv >= 1), float32 out + LSE.

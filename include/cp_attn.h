@@ -183,6 +183,15 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides,
 cp_status_t cp_ulysses_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
                                int D, int degree, int direction, void* stream);
 
+/* Workgroup shape of the bfloat16 block kernel, a process-wide tuning knob
+ * (no source passage; a property of this implementation). 0 = chosen per
+ * launch from the grid size (the default), 4 = four waves and 128 query rows
+ * per workgroup, 8 = eight waves and 256 rows in two ping-pong groups. Head
+ * dim 64 always uses 4. Results agree to rounding either way. Returns the
+ * previous setting; any other value is rejected with -1 and the setting is
+ * left unchanged. Launches already enqueued are not affected. */
+int cp_attn_set_fwd_waves(int waves);
+
 /* Message for the last non-CP_OK status returned on the calling thread ("" if none). */
 const char* cp_last_error(void);
 

@@ -1,5 +1,6 @@
 """Helpers for the GPU parity tests: move seeded inputs to the device, compare
 against the oracle, and report the worst element."""
+import contextlib
 import sys
 
 import numpy as np
@@ -37,3 +38,17 @@ def assert_close(name, got, want, tol):
     w = np.asarray(want)[i] if np.asarray(want).size else None
     say(f"{name}: max|err|={e:.3e} at {tuple(int(x) for x in i)} (got {g}, want {w}), tol {tol:g}")
     assert e <= tol, f"{name}: max abs error {e:.3e} > {tol:g} at {i}: got {g}, want {w}"
+
+
+# Both workgroup shapes of the bf16 block kernel (4 waves; 8 waves in ping-pong).
+SHAPES = (4, 8)
+
+
+@contextlib.contextmanager
+def fwd_waves(cp, waves):
+    """Force the bf16 block kernel's workgroup shape for the enclosed calls."""
+    prev = cp.cp_attn_set_fwd_waves(waves)
+    try:
+        yield
+    finally:
+        cp.cp_attn_set_fwd_waves(prev)

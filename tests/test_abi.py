@@ -130,6 +130,18 @@ def test_regroup_rejects(lib):
     assert f(0, 0, 2, 0, 16, 24, 128, 2, 0, None) == _lib.CP_OK
 
 
+def test_set_fwd_waves(lib):
+    """The bf16 workgroup-shape knob accepts 0, 4 and 8 only and returns the previous value."""
+    prev = lib.cp_attn_set_fwd_waves(4)
+    try:
+        assert prev in (0, 4, 8)
+        assert lib.cp_attn_set_fwd_waves(8) == 4
+        assert lib.cp_attn_set_fwd_waves(5) == -1
+        assert lib.cp_attn_set_fwd_waves(0) == 8
+    finally:
+        lib.cp_attn_set_fwd_waves(prev)
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     import context_attention_dits_amd as cp

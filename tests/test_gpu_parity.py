@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_util import TOL, assert_close, dev, say
+from tests.gpu_util import SHAPES, TOL, assert_close, dev, fwd_waves, say
 
 pytestmark = pytest.mark.gpu
 
@@ -75,13 +75,16 @@ def test_ring_small_full_compare(cp, B, H, D, Sq, lens, dtype):
     offs = workloads.block_offsets(lens)
     kb = [k[:, o:o + L] for o, L in zip(offs, lens)]
     vb = [v[:, o:o + L] for o, L in zip(offs, lens)]
-    for sep in (False, True):
-        out, lse = cp.ring_attention(q, kb, vb, scale=w.scale, ring_anything=anything, separate_merge=sep)
-        torch.cuda.synchronize()
-        o_ref, l_ref = oracle.ring_attention(inp.q, [inp.k_block(i) for i in range(len(lens))],
-                                             [inp.v_block(i) for i in range(len(lens))], w.scale)
-        assert_close(f"out sep={sep}", out.cpu().numpy(), o_ref, TOL[dtype]["o"])
-        assert_close(f"lse sep={sep}", lse.cpu().numpy(), l_ref, TOL[dtype]["lse"])
+    o_ref, l_ref = oracle.ring_attention(inp.q, [inp.k_block(i) for i in range(len(lens))],
+                                         [inp.v_block(i) for i in range(len(lens))], w.scale)
+    for wv in (SHAPES if dtype == "bf16" else (0,)):
+        for sep in (False, True):
+            say(f"waves={wv} separate_merge={sep}")
+            with fwd_waves(cp, wv):
+                out, lse = cp.ring_attention(q, kb, vb, scale=w.scale, ring_anything=anything, separate_merge=sep)
+                torch.cuda.synchronize()
+            assert_close(f"out sep={sep}", out.cpu().numpy(), o_ref, TOL[dtype]["o"])
+            assert_close(f"lse sep={sep}", lse.cpu().numpy(), l_ref, TOL[dtype]["lse"])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -93,19 +96,22 @@ def test_block_fwd_and_accumulate(cp, dtype):
     q = dev(inp.q, dtype)
     k0, v0 = dev(inp.k_block(0), dtype), dev(inp.v_block(0), dtype)
     k1, v1 = dev(inp.k_block(1), dtype), dev(inp.v_block(1), dtype)
-    out = torch.empty(B, Sq, H, D, device="cuda")
-    lse = torch.empty(B, H, Sq, device="cuda")
     s = inp.workload.scale
-    cp.cp_attn_block_fwd(q, k0, v0, out, lse, scale=s)
-    torch.cuda.synchronize()
     o0, l0 = oracle.block_attention(inp.q, inp.k_block(0), inp.v_block(0), s)
-    assert_close("block0 out", out.cpu().numpy(), o0, TOL[dtype]["o"])
-    assert_close("block0 lse", lse.cpu().numpy(), l0, TOL[dtype]["lse"])
-    cp.cp_attn_block_fwd(q, k1, v1, out, lse, scale=s, flags=cp.CP_BLOCK_ACCUMULATE)
-    torch.cuda.synchronize()
     o, l = oracle.ring_attention(inp.q, [inp.k_block(0), inp.k_block(1)], [inp.v_block(0), inp.v_block(1)], s)
-    assert_close("merged out", out.cpu().numpy(), o, TOL[dtype]["o"])
-    assert_close("merged lse", lse.cpu().numpy(), l, TOL[dtype]["lse"])
+    for wv in (SHAPES if dtype == "bf16" else (0,)):
+        say(f"waves={wv}")
+        out = torch.empty(B, Sq, H, D, device="cuda")
+        lse = torch.empty(B, H, Sq, device="cuda")
+        with fwd_waves(cp, wv):
+            cp.cp_attn_block_fwd(q, k0, v0, out, lse, scale=s)
+            torch.cuda.synchronize()
+            assert_close("block0 out", out.cpu().numpy(), o0, TOL[dtype]["o"])
+            assert_close("block0 lse", lse.cpu().numpy(), l0, TOL[dtype]["lse"])
+            cp.cp_attn_block_fwd(q, k1, v1, out, lse, scale=s, flags=cp.CP_BLOCK_ACCUMULATE)
+            torch.cuda.synchronize()
+        assert_close("merged out", out.cpu().numpy(), o, TOL[dtype]["o"])
+        assert_close("merged lse", lse.cpu().numpy(), l, TOL[dtype]["lse"])
 
 
 def test_lse_merge_kernel(cp):
@@ -172,10 +178,11 @@ def test_zero_length_blocks(cp):
     assert torch.all(out == 0).item() and torch.all(torch.isneginf(lse)).item()
 
 
-def test_strided_views(cp):
+@pytest.mark.parametrize("waves", SHAPES)
+def test_strided_views(cp, waves):
     """Q, K/V and out as non-contiguous views (heads interleaved in wider buffers)."""
     B, H, D, Sq, Skv = 2, 3, 128, 97, 130
-    say("strided views")
+    say("strided views, waves", waves)
     inp = workloads.make_custom(B, H, D, Sq, (Skv,), "bf16", seed=33)
     qw = torch.zeros(B, Sq, 2 * H, D, dtype=torch.bfloat16, device="cuda")
     kw = torch.zeros(B, Skv, 2 * H, D, dtype=torch.bfloat16, device="cuda")
@@ -186,20 +193,24 @@ def test_strided_views(cp):
     ow = torch.full((B, Sq, H, 2 * D), 7.0, device="cuda")
     out = ow[..., D:]
     lse = torch.empty(B, H, Sq, device="cuda")
-    cp.cp_ring_attention(qw[:, :, 1::2], [kw[:, :, 1::2]], [vw[:, :, 1::2]], out, lse, scale=inp.workload.scale)
-    torch.cuda.synchronize()
+    with fwd_waves(cp, waves):
+        cp.cp_ring_attention(qw[:, :, 1::2], [kw[:, :, 1::2]], [vw[:, :, 1::2]], out, lse,
+                             scale=inp.workload.scale)
+        torch.cuda.synchronize()
     o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.workload.scale)
     assert_close("out", out.cpu().numpy(), o_ref, TOL["bf16"]["o"])
     assert_close("lse", lse.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
     assert torch.all(ow[..., :D] == 7.0).item(), "write outside the output view"
 
 
-def test_wide_softmax_range(cp):
+@pytest.mark.parametrize("waves", SHAPES)
+def test_wide_softmax_range(cp, waves):
     """Q scaled by 8: scores spread over a much wider range than N(0,1) gives."""
     B, H, D, Sq, lens = 1, 4, 128, 192, (256, 250)
-    say("q*8 stress")
+    say("q*8 stress, waves", waves)
     inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=8, q_scale=8.0)
-    out, lse = _ring_gpu(cp, inp)
+    with fwd_waves(cp, waves):
+        out, lse = _ring_gpu(cp, inp)
     o_ref, l_ref = oracle.ring_attention(inp.q, [inp.k_block(0), inp.k_block(1)],
                                          [inp.v_block(0), inp.v_block(1)], inp.workload.scale)
     assert_close("out", out, o_ref, TOL["bf16"]["o"])
