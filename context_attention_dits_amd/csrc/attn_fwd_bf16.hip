@@ -21,14 +21,14 @@
 //     (no data movement), with the contraction over keys taken in the order
 //     the accumulator layout holds them. Each lane's O registers belong to its
 //     own query row, so rescaling needs no cross-lane traffic.
-//   * K and V tiles go from global memory straight into LDS
-//     (global_load_lds_dwordx4: lane i of a load fills bytes 16i..16i+15 of a
-//     1 KB LDS block), so staging costs no registers and no LDS-store
+//   * K and V tiles go from global memory straight into LDS (buffer loads
+//     with the LDS flag: lane i of a load fills bytes 16i..16i+15 of a 1 KB
+//     LDS block), so staging costs no registers and no LDS-store
 //     instructions. K is laid out per MFMA fragment: each (32-key block,
 //     16-dim step) pair is one contiguous 1 KB block in exactly the lane
 //     order of the A operand, read back with one conflict-free ds_read_b128
 //     at an immediate offset. V stays row-major (one key per row) with its
-//     16-byte chunks XOR-swizzled by row, and the V^T operand is read with
+//     16-byte chunks XOR-swizzled by row; V^T fragments are read from it with
 //     ds_read_b64_tr_b16, which transposes 4 keys x 16 dims across each
 //     16-lane group; the swizzle spreads the 8 rows one read touches over
 //     all LDS banks.
@@ -38,14 +38,25 @@
 //     Row sums are accumulated in float32 from the unrounded probabilities
 //     (summing the bf16-rounded ones would cost up to 2^-9 relative in LSE
 //     when a few keys dominate a row).
-//   * Two LDS stages: the next tile's loads are issued before the current
-//     tile is computed; one barrier per tile.
 //   * The exponent uses base 2 with scale*log2(e) folded into one FMA.
+//   * Two workgroup shapes, picked per launch:
+//     - 4 waves (128 query rows, two workgroups per CU): two LDS stages, one
+//       barrier per tile; each wave computes the next tile's scores on the
+//       matrix cores interleaved with the current tile's exponentials, then
+//       the PV product with V^T read by transposing LDS reads.
+//     - 8 waves (256 rows, one workgroup per CU, half the K/V traffic per
+//       row) in ping-pong: two groups of four waves, one wave of each group
+//       per SIMD, run one half-step apart. Each step is a softmax half
+//       (vector ALUs, plus the tile loads and a share of the V transposition)
+//       and a matrix-core half (PV and next scores, LDS reads and MFMAs
+//       only), separated by workgroup barriers, so each SIMD overlaps one
+//       wave's softmax with the other wave's MFMAs. Three LDS stages of K,
+//       raw V and V^T in fragment order (read with ds_read_b128).
 //   * Workgroups are remapped so that consecutive query tiles of one head run
 //     on the same XCD (each XCD has its own L2) and share its K/V reads.
-//   * Keys beyond Skv are never read: their loads are clamped to the last
-//     valid key and their scores set to -inf. Query rows beyond Sq are
-//     computed on zeros and not stored.
+//   * Keys beyond Skv are never read: the buffer descriptor's range ends at
+//     key Skv, so their LDS rows are zeros, and their scores are set to -inf.
+//     Query rows beyond Sq are computed on zeros and not stored.
 #include <stdint.h>
 
 #include <type_traits>
@@ -77,6 +88,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -168,22 +180,11 @@ __device__ __forceinline__ int vswz(int r) {
   }
 }
 
-// A batch of global->LDS loads handed to a compute phase, with its
-// instruction count known at compile time (for the issue schedule).
-template <int N, typename F>
-struct Loads {
-  static constexpr int count = N;
-  F f;
-  __device__ __forceinline__ void operator()() const { f(); }
+// A no-op hook for the memory-traffic slots of a compute phase.
+struct Nothing {
+  template <typename... A>
+  __device__ __forceinline__ void operator()(A...) const {}
 };
-struct NoLoads {
-  static constexpr int count = 0;
-  __device__ __forceinline__ void operator()() const {}
-};
-template <int N, typename F>
-__device__ __forceinline__ Loads<N, F> make_loads(F f) {
-  return Loads<N, F>{f};
-}
 
 template <int D, int QB, int NW, bool ACC>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
@@ -196,9 +197,12 @@ attn_fwd_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char kbuf1[C::K_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[C::V_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf1[C::V_BYTES];
-  // third stage, ping-pong only
+  // ping-pong only: third stage, and V^T in MFMA fragment order (three stages)
   __shared__ __attribute__((aligned(1024))) char kbuf2[C::NBUF > 2 ? C::K_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char vbuf2[C::NBUF > 2 ? C::V_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char vtb0[C::NBUF > 2 ? C::V_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char vtb1[C::NBUF > 2 ? C::V_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char vtb2[C::NBUF > 2 ? C::V_BYTES : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -213,7 +217,13 @@ attn_fwd_bf16_kernel(Params p) {
 
   const uint16_t* kbase = p.k + b * p.kv_sb + h * p.kv_sh;
   const uint16_t* vbase = p.v + b * p.kv_sb + h * p.kv_sh;
-  const int n_tiles = (p.Skv + C::BN - 1) / C::BN;
+  // Kernel arguments used inside the tile loop, pinned in SGPRs: reloading
+  // them from the argument segment there would make the next LDS wait also
+  // wait for that scalar load.
+  int skv = p.Skv;
+  float csc = p.c;
+  asm volatile("" : "+s"(skv), "+s"(csc));
+  const int n_tiles = (skv + C::BN - 1) / C::BN;
 
   // ---- Q (B operand of S^T = K Q^T): lane holds query l32, dims kk*16 + hi*8 .. +7
   bf16x8 qf[QB][C::KK];
@@ -255,7 +265,7 @@ attn_fwd_bf16_kernel(Params p) {
   // loads unconditionally.
   auto tile_range = [&](int t, const uint16_t* head, const uint16_t*& base, int& nbytes) {
     base = head + (int64_t)(min(t, n_tiles - 1) * C::BN) * p.kv_ss;
-    const int64_t avail = (int64_t)(p.Skv - t * C::BN) * row_bytes;  // <= 0 past the end
+    const int64_t avail = (int64_t)(skv - t * C::BN) * row_bytes;  // <= 0 past the end
     nbytes = (int)max((int64_t)0, min(avail, (int64_t)0x7fffffff));
   };
   auto issue_k = [&](int t, char* Ks) {
@@ -327,16 +337,17 @@ attn_fwd_bf16_kernel(Params p) {
   // into s_next) run on the matrix cores interleaved with the exponentials on
   // the vector ALUs. On entry s_cur holds tile j's scores.
   auto half_a = [&](auto last_tag, auto fuse_tag, int j, f32x16 (&s_cur)[QB][C::KB],
-                    f32x16 (&s_next)[QB][C::KB], const char* k_read, auto loads) {
+                    f32x16 (&s_next)[QB][C::KB], const char* k_read, auto pre, auto post) {
     constexpr bool LAST = decltype(last_tag)::value;  // the final tile: mask, no next tile
     constexpr bool FUSE = decltype(fuse_tag)::value && !LAST;  // next tile's scores computed here
+    pre();  // memory traffic first, so its latency hides behind the arithmetic
 
     // tail mask: keys >= Skv get -inf (only the last tile can have them)
     if constexpr (LAST) {
       const int key0 = j * C::BN;
-      if (key0 + C::BN > p.Skv) {
+      if (key0 + C::BN > skv) {
         // This lane holds keys key0 + 4*hi + (kb*32 + 8*(r/4) + r%4).
-        const int lim = p.Skv - key0 - 4 * hi;
+        const int lim = skv - key0 - 4 * hi;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -358,7 +369,7 @@ attn_fwd_bf16_kernel(Params p) {
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[qb][kb][r]);
-      const float mt = half_max(mx) * p.c;
+      const float mt = half_max(mx) * csc;
       const bool need = __builtin_amdgcn_ballot_w64(mt > m_run[qb] + CP_FWD_LAZY) != 0;
       const float m_new = need ? fmaxf(m_run[qb], mt) : m_run[qb];
       alpha[qb] = fast_exp2(m_run[qb] - m_new);  // 1 when the maximum is kept
@@ -373,7 +384,6 @@ attn_fwd_bf16_kernel(Params p) {
         for (int db = 0; db < D / 32; ++db) o[qb][db] *= alpha[qb];
       }
     }
-    loads();
 
     if constexpr (FUSE) scores(k_read, s_next);
 #pragma unroll
@@ -384,10 +394,11 @@ attn_fwd_bf16_kernel(Params p) {
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int kk2 = 0; kk2 < 2; ++kk2) {
+          post((qb * C::KB + kb) * 2 + kk2);  // hook between groups of 8 exponentials
           bf16x8 t;
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
-            const float e = fast_exp2(fmaf(s_cur[qb][kb][kk2 * 8 + jj], p.c, mneg));
+            const float e = fast_exp2(fmaf(s_cur[qb][kb][kk2 * 8 + jj], csc, mneg));
             ls += e;  // float32 sum of the unrounded probabilities: LSE needs it
             t[jj] = (__bf16)e;
           }
@@ -454,34 +465,59 @@ attn_fwd_bf16_kernel(Params p) {
 #endif
   };
 
-  // Matrix-core half of a ping-pong step: O^T += V_j^T P_j^T from v_read and,
+  // Ping-pong only: V^T of one tile in MFMA fragment order. Fragment
+  // f = (db * KB + kb) * 2 + kk2 is the A operand of O^T += V^T P^T for dims
+  // db*32.. and keys kb*32 + kk2*16..; lane l's 16 bytes sit at f*1024 + l*16,
+  // so it is read back with one conflict-free ds_read_b128.
+  constexpr int N_VFRAG = (D / 32) * C::KB * 2;
+  // Transpose this wave's share of the fragments of a raw V tile (row-major,
+  // swizzled, as loaded) into vt: two transposing reads (read_vt) and one
+  // write (write_vt) each.
+  static_assert(N_VFRAG % NW == 0, "fragment split");
+  constexpr int VT_PER_WAVE = N_VFRAG / NW > 0 ? N_VFRAG / NW : 1;
+  auto read_vt = [&](const char* v_raw, i16x8 (&frag)[VT_PER_WAVE]) {
+#pragma unroll
+    for (int i = 0; i < N_VFRAG / NW; ++i) {
+      const int f = wave * (N_VFRAG / NW) + i;
+      const int db = f / (2 * C::KB), kb = (f / 2) % C::KB, kk2 = f % 2;
+      const char* a0 = v_raw + (vlane ^ (db << 6)) + (kb * 32 + kk2 * 16) * C::VROW;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * C::VROW));
+      frag[i] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto write_vt = [&](char* vt, const i16x8 (&frag)[VT_PER_WAVE]) {
+#pragma unroll
+    for (int i = 0; i < N_VFRAG / NW; ++i) {
+      const int f = wave * (N_VFRAG / NW) + i;
+      *reinterpret_cast<i16x8*>(vt + f * 1024 + lane * 16) = frag[i];
+    }
+  };
+
+  // Matrix-core half of a ping-pong step: O^T += V_j^T P_j^T from vt_read and,
   // unless tile j is the last, the scores of tile j+1 from k_read into s_next.
   // Only LDS reads and MFMAs: the vector ALU work of the step is in half_a.
-  auto half_m = [&](auto last_tag, f32x16 (&s_next)[QB][C::KB], const char* k_read, const char* v_read) {
+  auto half_m = [&](auto last_tag, f32x16 (&s_next)[QB][C::KB], const char* k_read, const char* vt_read) {
     constexpr bool LAST = decltype(last_tag)::value;
+    const char* vfrag = vt_read + lane * 16;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const char* vb = v_read + (vlane ^ (db << 6));
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int kk2 = 0; kk2 < 2; ++kk2) {
-          const char* a0 = vb + (kb * 32 + kk2 * 16) * C::VROW;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
-          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * C::VROW));
-          const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
-                                                   __builtin_bit_cast(bf16x4, hi4), 0, 1, 2, 3, 4, 5, 6, 7);
+          const int f = (db * C::KB + kb) * 2 + kk2;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vfrag + f * 1024);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][kk2], o[qb][db], 0, 0, 0);
         }
-    }
     if constexpr (!LAST) scores(k_read, s_next);
 #if CP_FWD_SCHED_PV
     // Keep the LDS reads ahead of the MFMAs: eight reads up front, then two
     // per MFMA, then one, until the reads run out.
     constexpr int n_mfma = QB * ((D / 32) * C::KB * 2 + (LAST ? 0 : C::KB * C::KK));
-    constexpr int n_rd = (D / 32) * C::KB * 4 + (LAST ? 0 : C::KB * C::KK);
+    constexpr int n_rd = (D / 32) * C::KB * 2 + (LAST ? 0 : C::KB * C::KK);
     constexpr int pre = n_rd < 8 ? n_rd : 8;
     constexpr int two = (n_rd - pre) / 2 < n_mfma ? (n_rd - pre) / 2 : n_mfma;
     constexpr int one = n_rd - pre - 2 * two;
@@ -516,17 +552,16 @@ attn_fwd_bf16_kernel(Params p) {
   using Fused = std::integral_constant<bool, true>;
   using Split = std::integral_constant<bool, false>;
 
-  // prologue: K_0, V_0, K_1 in flight; scores of tile 0. K_j always lives in
-  // kbuf(j % 2) and V_j in vbuf(j % 2).
-  issue_k(0, kbuf0);
-  issue_v(0, vbuf0);
-  issue_k(1, kbuf1);
-  sync(Pend0{});
   f32x16 sa[QB][C::KB];
-  scores(kbuf0, sa);
-
   int j = 0;
   if constexpr (!C::PINGPONG) {
+    // prologue: K_0, V_0, K_1 loaded; scores of tile 0. K_j lives in
+    // kbuf(j % 2) and V_j in vbuf(j % 2).
+    issue_k(0, kbuf0);
+    issue_v(0, vbuf0);
+    issue_k(1, kbuf1);
+    sync(Pend0{});
+    scores(kbuf0, sa);
     sync(Pend0{});  // every wave is done with K_0 before K_2 overwrites it
     f32x16 sb[QB][C::KB];
     // One step over tile j: loads of K_{j+2} and V_{j+1} are issued, then
@@ -540,7 +575,7 @@ attn_fwd_bf16_kernel(Params p) {
         issue_k(jj + 2, k_write);
         issue_v(jj + 1, v_write);
       }
-      half_a(last_tag, Fused{}, jj, s_cur, s_next, k_read, NoLoads{});
+      half_a(last_tag, Fused{}, jj, s_cur, s_next, k_read, Nothing{}, Nothing{});
       half_b(v_read);
       if constexpr (!LAST) sync(Pend0{});
     };
@@ -561,43 +596,65 @@ attn_fwd_bf16_kernel(Params p) {
     // (vector ALUs) runs while the other wave's matrix-core half (LDS reads
     // and MFMAs only) runs. Intervals end with a workgroup barrier. Group A
     // runs the softmax of tile j in interval 2j and its MFMA half (PV of tile
-    // j, scores of tile j+1) in 2j+1; group B one interval later. Three LDS
-    // stages per operand: tile t lives in buffer t % 3.
+    // j, scores of tile j+1) in 2j+1; group B one interval later.
+    // Three LDS stages of K, raw V and V^T: tile t lives in stage t % 3.
     // During its softmax of tile j every wave issues its share of K_{j+2} and
-    // V_{j+1}, whose buffers were last read in interval 2j-2, and which are
-    // first read in interval 2j+3. Group A waits for its loads one softmax
-    // later (all but the newest at the end of interval 2j+2); group B, which
-    // issues in 2j+1, waits for all its loads at the end of its MFMA half in
-    // 2j+2.
+    // raw V_{j+3} and transposes its share of raw V_{j+1} into V_{j+1}^T.
+    // The buffers it writes were last read in interval 2j-1 or earlier; the
+    // tiles it loads are first read in interval 2j+3 (K) and 2j+4 (V). Group
+    // A waits for its loads one softmax later (all but the newest, at the end
+    // of interval 2j+2); group B, which issues in 2j+1, waits for all of its
+    // loads at the end of its MFMA half in 2j+2. Every barrier waits for the
+    // wave's LDS accesses, so a transposed tile is complete one interval
+    // after the second group wrote its share.
     using PendL = std::integral_constant<int, C::K_PER_WAVE + C::V_PER_WAVE>;
     const bool grp_b = wave >= NW / 2;
-    if (grp_b) sync(Pend0{});  // group B idles in interval 0
     char* const kb3[3] = {kbuf0, kbuf1, kbuf2};
     char* const vb3[3] = {vbuf0, vbuf1, vbuf2};
+    char* const vt3[3] = {vtb0, vtb1, vtb2};
+    // prologue: K_0, K_1 and raw V_0..V_2 loaded, V_0^T built, scores of tile 0
+    issue_k(0, kbuf0);
+    issue_k(1, kbuf1);
+    issue_v(0, vbuf0);
+    issue_v(1, vbuf1);
+    issue_v(2, vbuf2);
+    sync(Pend0{});
+    scores(kbuf0, sa);
+    {
+      i16x8 fr[VT_PER_WAVE];
+      read_vt(vbuf0, fr);
+      write_vt(vtb0, fr);
+    }
+    if (grp_b) sync(Pend0{});  // group B idles in interval 0
     // one tile; c = j % 3, known at compile time in the unrolled loop
     auto step = [&](auto last_tag, auto c_tag, int jj) {
       constexpr bool LAST = decltype(last_tag)::value;
       constexpr int c = decltype(c_tag)::value;
       const char* k_read = kb3[(c + 1) % 3];
-      const char* v_read = vb3[c];
+      const char* vt_read = vt3[c];
       if constexpr (!LAST) {
-        char* k_write = kb3[(c + 2) % 3];
-        char* v_write = vb3[(c + 1) % 3];
-        half_a(last_tag, Split{}, jj, sa, sa, k_read, make_loads<C::K_PER_WAVE + C::V_PER_WAVE>([&] {
-                 issue_k(jj + 2, k_write);
-                 issue_v(jj + 1, v_write);
-               }));
+        i16x8 fr[VT_PER_WAVE];
+        half_a(
+            last_tag, Split{}, jj, sa, sa, k_read,
+            [&] {
+              issue_k(jj + 2, kb3[(c + 2) % 3]);
+              issue_v(jj + 3, vb3[c]);
+              read_vt(vb3[(c + 1) % 3], fr);
+            },
+            [&](int g) {
+              if (g == 0) write_vt(vt3[(c + 1) % 3], fr);
+            });
         if (grp_b) sync(PendAll{});
         else sync(PendL{});
-        half_m(last_tag, sa, k_read, v_read);
+        half_m(last_tag, sa, k_read, vt_read);
         if (grp_b) sync(Pend0{});
         else sync(PendAll{});
       } else {
         // The last barrier ends interval 2n-2: group A passes it after its
         // last softmax, group B after its last MFMA half but one.
-        half_a(last_tag, Split{}, jj, sa, sa, k_read, NoLoads{});
+        half_a(last_tag, Split{}, jj, sa, sa, k_read, Nothing{}, Nothing{});
         if (!grp_b) sync(Pend0{});
-        half_m(last_tag, sa, k_read, v_read);
+        half_m(last_tag, sa, k_read, vt_read);
       }
     };
     using C0 = std::integral_constant<int, 0>;
