@@ -105,26 +105,81 @@ class Problem:
     def time_block_kernels(self, reps: int):
         """Average duration of one block-attention launch, as the ring issues them.
 
-        Block 0 is written, later blocks are merged in by the kernel epilogue;
-        each launch is bracketed by HIP events on the stream it runs on.
+        Block 0 is written, later blocks are merged in by the kernel epilogue.
+        The launches of `reps` ring passes run back to back between two HIP
+        events on the stream they are launched on; the mean is the region's
+        time over the number of launches.
         """
         torch, cp, w = self.torch, self.cp, self.w
         stream = torch.cuda.current_stream()
-        durs, flops = [], []
-        for _ in range(reps):
-            for i, (kb, vb) in enumerate(zip(self.kb, self.vb)):
-                if kb.shape[1] == 0:
-                    continue
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
+        blocks = [(i, kb, vb) for i, (kb, vb) in enumerate(zip(self.kb, self.vb)) if kb.shape[1] > 0]
+
+        def one_pass():
+            for i, kb, vb in blocks:
                 cp.cp_attn_block_fwd(self.q_att, kb, vb, self.out, self.lse, scale=w.scale,
                                      flags=cp.CP_BLOCK_ACCUMULATE if i > 0 else 0)
-                e1.record(stream)
-                durs.append((e0, e1))
-                flops.append(4 * w.B * w.attn_H * w.Sq * kb.shape[1] * w.D)
+
+        one_pass()
         torch.cuda.synchronize()
-        ms = [a.elapsed_time(b) for a, b in durs]
-        return sum(ms) / len(ms), sum(flops) / len(flops)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            one_pass()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        flops = sum(4 * w.B * w.attn_H * w.Sq * kb.shape[1] * w.D for _, kb, _ in blocks) / len(blocks)
+        return e0.elapsed_time(e1) / (reps * len(blocks)), flops
+
+
+def time_hbm_kernels(reps: int = 5):
+    """HBM rate of the two bandwidth-bound kernels, cold caches.
+
+    cp_lse_merge on the 32k-token ring-4 share (out [1, 8192, 24, 128] float32,
+    in place) and cp_ulysses_regroup SEQ_TO_HEAD of a [1, 16384, 24, 128] bf16
+    tensor at degree 2. Before each timed launch a 512 MiB buffer is read so
+    that neither L2 nor the 256 MB Infinity Cache holds the operands; bytes are
+    the algorithmic ones (every element read once, written once).
+    """
+    import torch
+    import context_attention_dits_amd as cp
+    stream = torch.cuda.current_stream()
+    # Read, not written: dirty lines left by a writing flush would be written
+    # back to HBM during the timed launch and slow it.
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        ms = []
+        for _ in range(reps + 1):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return sum(ms[1:]) / reps
+
+    B, Sq, H, D = 1, 8192, 24, 128
+    g = torch.Generator(device="cuda").manual_seed(5)
+    oa = torch.randn(B, Sq, H, D, device="cuda", generator=g)
+    ob = torch.randn(B, Sq, H, D, device="cuda", generator=g)
+    la = torch.randn(B, H, Sq, device="cuda", generator=g)
+    lb = torch.randn(B, H, Sq, device="cuda", generator=g)
+    merge_ms = timed(lambda: cp.cp_lse_merge(oa, la, ob, lb))
+    merge_bytes = 3 * 4 * B * Sq * H * D + 3 * 4 * B * H * Sq
+    S_l, P = 16384, 2
+    x = torch.randn(B, S_l, H, D, device="cuda", generator=g).to(torch.bfloat16)
+    y = torch.empty(B, P * S_l, H // P, D, dtype=torch.bfloat16, device="cuda")
+    regroup_ms = timed(lambda: cp.cp_ulysses_regroup(x, y, P, cp.CP_REGROUP_SEQ_TO_HEAD))
+    regroup_bytes = 2 * 2 * B * S_l * H * D
+    out = {}
+    for name, ms, nb, shape in (("lse_merge", merge_ms, merge_bytes, "out [1,8192,24,128] f32 + lse, in place"),
+                                ("ulysses_regroup", regroup_ms, regroup_bytes,
+                                 "[1,16384,24,128] bf16 -> [1,32768,12,128], degree 2")):
+        gbs = nb / (ms * 1e-3) / 1e9
+        out[name] = {"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "us": round(ms * 1e3, 2),
+                     "bytes": nb, "shape": shape}
+    return out
 
 
 def cpu_baseline(w: workloads.Workload, inp, target_s: float):
@@ -228,6 +283,10 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     log(f"[bench] block kernel: {k_ms * 1e3:.1f} us/launch, {achieved:.1f} TFLOP/s ({achieved / peak:.1%} of {peak})")
 
+    hbm = time_hbm_kernels()
+    for name, r in hbm.items():
+        log(f"[bench] {name}: {r['us']:.1f} us, {r['GB/s']:.0f} GB/s ({r['frac']:.1%} of {PEAK_HBM_GBS:.0f}), {r['shape']}")
+
     cpu = None
     if args.cpu_seconds > 0:
         log("[bench] timing the CPU oracle ...")
@@ -257,6 +316,7 @@ def main():
                      "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel",
                      "us_per_launch": round(k_ms * 1e3, 2)},
         "cpu_baseline": cpu,
+        "hbm_kernels": hbm,
     }
     print(json.dumps(rec), flush=True)
     return 0

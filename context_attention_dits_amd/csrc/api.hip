@@ -167,6 +167,8 @@ cp_status_t cp_lse_merge(float* out_acc, float* lse_acc, const float* out_blk, c
     return fail(CP_ERR_UNSUPPORTED, "cp_lse_merge: outputs must be 16-byte aligned, LSE 4-byte");
   if (out_acc == out_blk || lse_acc == lse_blk)
     return fail(CP_ERR_INVALID_ARG, "cp_lse_merge: accumulator and block must be distinct buffers");
+  if ((int64_t)B * Sq * H * (D / 4) > 0x7fffffff)
+    return fail(CP_ERR_UNSUPPORTED, "cp_lse_merge: B*Sq*H*D/4 must be below 2^31");
   const Strides as = resolve(acc_strides, Sq, H, D);
   const Strides bs = resolve(blk_strides, Sq, H, D);
   cp_status_t st;

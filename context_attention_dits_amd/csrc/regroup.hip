@@ -7,10 +7,9 @@
 //   HEAD_TO_SEQ: out[b, s, g*(H/P) + h, d] = in[b, g*S_local + s, h, d]
 //
 // For every (b, s, g) both sides hold the same (H/P)*D elements contiguously,
-// so the permutation is a copy of B*S_local*P contiguous chunks. Each thread
-// moves W-byte words (16 when the chunk size and pointers allow) with
-// consecutive threads on consecutive words, several words per thread to keep
-// enough bytes in flight. Bit-exact for any element type.
+// so the permutation is a copy of B*S_local*P contiguous chunks, moved in
+// W-byte words (16 when the chunk size and pointers allow). Bit-exact for any
+// element type.
 #include <stdint.h>
 
 #include "kernels.h"
@@ -19,7 +18,6 @@ namespace cpattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = 4;
 
 template <int W>
 struct Word;
@@ -40,32 +38,30 @@ struct Word<2> {
   typedef uint16_t type;
 };
 
-template <int W>
+// One W-byte word per thread, consecutive threads on consecutive words of the
+// sequence-sharded side; I is the index type (32-bit unless the tensor has
+// 2^31 words or more). On MI355X this plain shape streams faster than moving
+// several words per thread or non-temporal accesses.
+template <int W, typename I>
 __global__ void __launch_bounds__(kThreads)
-regroup_kernel(const char* __restrict__ in, char* __restrict__ out, int S_local, int P,
-               int64_t chunk_words, int64_t src_row_words, int64_t n_words, int direction) {
+regroup_kernel(const char* __restrict__ in, char* __restrict__ out, I S_local, I P, I chunk_words,
+               I n_words, int direction) {
   using T = typename Word<W>::type;
   const T* src = reinterpret_cast<const T*>(in);
   T* dst = reinterpret_cast<T*>(out);
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * kPerThread) + threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int64_t id = base + (int64_t)i * kThreads;
-    if (id >= n_words) return;
-    const int64_t cid = id / chunk_words;
-    const int64_t w = id - cid * chunk_words;
-    // cid enumerates (b, s, g) with g fastest: the sequence-sharded side's order.
-    const int g = (int)(cid % P);
-    const int64_t bs = cid / P;
-    const int s = (int)(bs % S_local);
-    const int64_t b = bs / S_local;
-    const int64_t seq_off = bs * src_row_words + (int64_t)g * chunk_words + w;  // [b, s, g*Hl..]
-    const int64_t head_off = ((b * P + g) * S_local + s) * chunk_words + w;      // [b, g*S_l + s, ..]
-    if (direction == 0) {
-      dst[head_off] = src[seq_off];
-    } else {
-      dst[seq_off] = src[head_off];
-    }
+  const I id = (I)blockIdx.x * kThreads + (I)threadIdx.x;
+  if (id >= n_words) return;
+  const I cid = id / chunk_words;      // (b, s, g), g fastest: the sequence-sharded order
+  const I w = id - cid * chunk_words;
+  const I bs = cid / P;
+  const I g = cid - bs * P;
+  const I b = bs / S_local;
+  const I s = bs - b * S_local;
+  const int64_t head_off = (((int64_t)b * P + g) * S_local + s) * chunk_words + w;  // [b, g*S_l + s, ..]
+  if (direction == 0) {
+    dst[head_off] = src[id];
+  } else {
+    dst[id] = src[head_off];
   }
 }
 
@@ -74,12 +70,18 @@ hipError_t launch_w(const void* in, void* out, int64_t chunk_bytes, int B, int S
                     int direction, hipStream_t stream) {
   const int64_t chunk_words = chunk_bytes / W;
   const int64_t n_words = chunk_words * P * S_local * B;
-  const int64_t per_block = (int64_t)kThreads * kPerThread;
-  const int64_t g = (n_words + per_block - 1) / per_block;
+  if (n_words == 0) return hipSuccess;
+  const int64_t g = (n_words + kThreads - 1) / kThreads;
   if (g > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(regroup_kernel<W>, dim3((unsigned)g), dim3(kThreads), 0, stream,
-                     static_cast<const char*>(in), static_cast<char*>(out), S_local, P, chunk_words,
-                     chunk_words * P, n_words, direction);
+  const char* src = static_cast<const char*>(in);
+  char* dst = static_cast<char*>(out);
+  if (n_words <= 0x7fffffff) {
+    hipLaunchKernelGGL((regroup_kernel<W, int>), dim3((unsigned)g), dim3(kThreads), 0, stream, src, dst,
+                       S_local, P, (int)chunk_words, (int)n_words, direction);
+  } else {
+    hipLaunchKernelGGL((regroup_kernel<W, int64_t>), dim3((unsigned)g), dim3(kThreads), 0, stream, src, dst,
+                       (int64_t)S_local, (int64_t)P, chunk_words, n_words, direction);
+  }
   return hipGetLastError();
 }
 

@@ -121,6 +121,7 @@ cp_status_t cp_attn_block_fwd(const void* q, const int64_t* q_strides,
  *   out_acc, out_blk [B, Sq, H, D] float32 with strides acc_strides / blk_strides
  *   lse_acc, lse_blk [B, H, Sq]    float32, contiguous
  * out_blk/lse_blk are read only and must not overlap the accumulators.
+ * B*Sq*H*D/4 must be below 2^31 (else CP_ERR_UNSUPPORTED).
  */
 cp_status_t cp_lse_merge(float* out_acc, float* lse_acc, const float* out_blk, const float* lse_blk,
                          const int64_t* acc_strides, const int64_t* blk_strides,

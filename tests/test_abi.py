@@ -116,6 +116,10 @@ def test_merge_rejects(lib):
     assert f(FAKE, FAKE, FAKE, FAKE + 8192, None, None, 1, 2, 8, 128, None) == _lib.CP_ERR_INVALID_ARG
     assert f(0, FAKE, FAKE, FAKE, None, None, 1, 2, 8, 128, None) == _lib.CP_ERR_INVALID_ARG
     assert f(0, 0, 0, 0, None, None, 1, 0, 8, 128, None) == _lib.CP_OK
+    # B*Sq*H*D/4 at 2^31 is beyond the kernel's 32-bit indices
+    assert f(FAKE, FAKE, FAKE + (1 << 30), FAKE + (1 << 31), None, None, 2, 1 << 10, 1 << 15, 128,
+             None) == _lib.CP_ERR_UNSUPPORTED
+    assert "2^31" in _err(lib)
 
 
 def test_regroup_rejects(lib):

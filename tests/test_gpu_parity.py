@@ -114,10 +114,11 @@ def test_block_fwd_and_accumulate(cp, dtype):
         assert_close("merged lse", lse.cpu().numpy(), l, TOL[dtype]["lse"])
 
 
-def test_lse_merge_kernel(cp):
-    say("lse_merge kernel")
-    rng = np.random.default_rng(5)
-    B, Sq, H, D = 2, 37, 5, 128
+@pytest.mark.parametrize("D,strided", [(128, False), (64, False), (128, True)])
+def test_lse_merge_kernel(cp, D, strided):
+    say("lse_merge kernel", D, "strided" if strided else "contiguous")
+    rng = np.random.default_rng(5 + D)
+    B, Sq, H = 2, 37, 5
     oa, ob = rng.standard_normal((B, Sq, H, D)).astype(np.float32), rng.standard_normal((B, Sq, H, D)).astype(np.float32)
     la, lb = (rng.standard_normal((B, H, Sq)) * 4).astype(np.float32), (rng.standard_normal((B, H, Sq)) * 4).astype(np.float32)
     la[0, 1, :5] = -np.inf   # accumulator empty
@@ -125,9 +126,17 @@ def test_lse_merge_kernel(cp):
     la[1, 4, 10:12] = -np.inf
     lb[1, 4, 10:12] = -np.inf  # both empty
     oa[1, 10:12, 4] = np.nan  # an empty side's output must not leak
-    ga, gla = torch.from_numpy(oa).cuda(), torch.from_numpy(la).cuda()
+    gla = torch.from_numpy(la).cuda()
+    if strided:  # accumulator is every other head of a wider buffer
+        wide = torch.full((B, Sq, 2 * H, D), 7.0, device="cuda")
+        wide[:, :, ::2] = torch.from_numpy(oa).cuda()
+        ga = wide[:, :, ::2]
+    else:
+        ga = torch.from_numpy(oa).cuda()
     cp.cp_lse_merge(ga, gla, torch.from_numpy(ob).cuda(), torch.from_numpy(lb).cuda())
     torch.cuda.synchronize()
+    if strided:
+        assert torch.all(wide[:, :, 1::2] == 7.0).item(), "write outside the accumulator view"
     o_ref, l_ref = oracle.lse_merge(np.nan_to_num(oa, nan=0.0), la, ob, lb)
     got_l = gla.cpu().numpy()
     assert np.array_equal(np.isneginf(got_l), np.isneginf(l_ref))
