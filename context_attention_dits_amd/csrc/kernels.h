@@ -12,6 +12,28 @@ struct Strides {
   int64_t b, s, h;
 };
 
+// Unsigned 32-bit division by a divisor fixed at launch, as a multiply-high,
+// an add and two shifts (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994, the round-up multiplier with an extra
+// add for the 33-bit case): for l = ceil(log2 d),
+//   m = floor(2^32 (2^l - d) / d) + 1,  t = mulhi(n, m),
+//   n / d = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0)   for all n < 2^32.
+struct FastDiv {
+  uint32_t d, m, s1, s2;
+  FastDiv() = default;
+  explicit FastDiv(uint32_t div) : d(div) {
+    uint32_t l = 0;
+    while (l < 32 && (uint64_t(1) << l) < div) ++l;
+    m = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << l) - div)) / div + 1);
+    s1 = l < 1 ? l : 1;
+    s2 = l > 1 ? l - 1 : 0;
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    const uint32_t t = __umulhi(n, m);
+    return (t + ((n - t) >> s1)) >> s2;
+  }
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;

@@ -28,21 +28,24 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kThreads = 256;
 
 // One float4 of out_acc per thread, consecutive threads on consecutive
-// float4 of a row; 32-bit index math (the host checks B*Sq*H*D/4 < 2^31).
+// float4 of a row; 32-bit index math with multiply-shift divisions (the host
+// checks B*Sq*H*D/4 < 2^31).
 // On MI355X this plain shape streams faster than batching several float4 per
 // thread or non-temporal accesses.
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 lse_merge_kernel(float* __restrict__ oa, float* __restrict__ la, const float* __restrict__ ob,
-                 const float* __restrict__ lb, Strides as, Strides bs, int H, int Sq, int n_vec) {
+                 const float* __restrict__ lb, Strides as, Strides bs, FastDiv div_h, FastDiv div_sq,
+                 int n_vec) {
   constexpr int V = D / 4;  // float4 per row
   const int id = blockIdx.x * kThreads + threadIdx.x;
   if (id >= n_vec) return;
+  const int H = (int)div_h.d, Sq = (int)div_sq.d;
   const int row = id / V;  // (b * Sq + s) * H + h
   const int c4 = id % V;
-  const int bs_row = row / H;
+  const int bs_row = (int)div_h.div((uint32_t)row);
   const int h = row - bs_row * H;
-  const int b = bs_row / Sq;
+  const int b = (int)div_sq.div((uint32_t)bs_row);
   const int s = bs_row - b * Sq;
   const int64_t li = ((int64_t)b * H + h) * Sq + s;
   f32x4* pa = reinterpret_cast<f32x4*>(oa + b * as.b + (int64_t)s * as.s + h * as.h + c4 * 4);
@@ -98,10 +101,12 @@ hipError_t launch_lse_merge(float* out_acc, float* lse_acc, const float* out_blk
   const int64_t g = grid_for(n_vec);
   if (D == 128) {
     hipLaunchKernelGGL(lse_merge_kernel<128>, dim3((unsigned)g), dim3(kThreads), 0, stream, out_acc,
-                       lse_acc, out_blk, lse_blk, as, bs, H, Sq, (int)n_vec);
+                       lse_acc, out_blk, lse_blk, as, bs, FastDiv((uint32_t)H), FastDiv((uint32_t)Sq),
+                       (int)n_vec);
   } else if (D == 64) {
     hipLaunchKernelGGL(lse_merge_kernel<64>, dim3((unsigned)g), dim3(kThreads), 0, stream, out_acc,
-                       lse_acc, out_blk, lse_blk, as, bs, H, Sq, (int)n_vec);
+                       lse_acc, out_blk, lse_blk, as, bs, FastDiv((uint32_t)H), FastDiv((uint32_t)Sq),
+                       (int)n_vec);
   } else {
     return hipErrorInvalidValue;
   }

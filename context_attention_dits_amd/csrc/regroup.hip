@@ -39,23 +39,40 @@ struct Word<2> {
 };
 
 // One W-byte word per thread, consecutive threads on consecutive words of the
-// sequence-sharded side; I is the index type (32-bit unless the tensor has
-// 2^31 words or more). On MI355X this plain shape streams faster than moving
+// sequence-sharded side; I is the index type (32-bit, with multiply-shift
+// divisions, unless the tensor has 2^31 words or more). On MI355X this plain shape streams faster than moving
 // several words per thread or non-temporal accesses.
 template <int W, typename I>
+struct RegroupDiv;
+template <int W>
+struct RegroupDiv<W, uint32_t> {  // divisors as multiply-shift
+  FastDiv chunk, p, s_local;
+  __device__ __forceinline__ uint32_t by_chunk(uint32_t n) const { return chunk.div(n); }
+  __device__ __forceinline__ uint32_t by_p(uint32_t n) const { return p.div(n); }
+  __device__ __forceinline__ uint32_t by_s(uint32_t n) const { return s_local.div(n); }
+};
+template <int W>
+struct RegroupDiv<W, int64_t> {  // plain 64-bit division for tensors of 2^31 words or more
+  int64_t chunk, p, s_local;
+  __device__ __forceinline__ int64_t by_chunk(int64_t n) const { return n / chunk; }
+  __device__ __forceinline__ int64_t by_p(int64_t n) const { return n / p; }
+  __device__ __forceinline__ int64_t by_s(int64_t n) const { return n / s_local; }
+};
+
+template <int W, typename I>
 __global__ void __launch_bounds__(kThreads)
-regroup_kernel(const char* __restrict__ in, char* __restrict__ out, I S_local, I P, I chunk_words,
-               I n_words, int direction) {
+regroup_kernel(const char* __restrict__ in, char* __restrict__ out, RegroupDiv<W, I> dv, I S_local,
+               I P, I chunk_words, I n_words, int direction) {
   using T = typename Word<W>::type;
   const T* src = reinterpret_cast<const T*>(in);
   T* dst = reinterpret_cast<T*>(out);
   const I id = (I)blockIdx.x * kThreads + (I)threadIdx.x;
   if (id >= n_words) return;
-  const I cid = id / chunk_words;      // (b, s, g), g fastest: the sequence-sharded order
+  const I cid = dv.by_chunk(id);  // (b, s, g), g fastest: the sequence-sharded order
   const I w = id - cid * chunk_words;
-  const I bs = cid / P;
+  const I bs = dv.by_p(cid);
   const I g = cid - bs * P;
-  const I b = bs / S_local;
+  const I b = dv.by_s(bs);
   const I s = bs - b * S_local;
   const int64_t head_off = (((int64_t)b * P + g) * S_local + s) * chunk_words + w;  // [b, g*S_l + s, ..]
   if (direction == 0) {
@@ -76,11 +93,13 @@ hipError_t launch_w(const void* in, void* out, int64_t chunk_bytes, int B, int S
   const char* src = static_cast<const char*>(in);
   char* dst = static_cast<char*>(out);
   if (n_words <= 0x7fffffff) {
-    hipLaunchKernelGGL((regroup_kernel<W, int>), dim3((unsigned)g), dim3(kThreads), 0, stream, src, dst,
-                       S_local, P, (int)chunk_words, (int)n_words, direction);
+    RegroupDiv<W, uint32_t> dv{FastDiv((uint32_t)chunk_words), FastDiv((uint32_t)P), FastDiv((uint32_t)S_local)};
+    hipLaunchKernelGGL((regroup_kernel<W, uint32_t>), dim3((unsigned)g), dim3(kThreads), 0, stream, src, dst,
+                       dv, (uint32_t)S_local, (uint32_t)P, (uint32_t)chunk_words, (uint32_t)n_words, direction);
   } else {
+    RegroupDiv<W, int64_t> dv{chunk_words, (int64_t)P, (int64_t)S_local};
     hipLaunchKernelGGL((regroup_kernel<W, int64_t>), dim3((unsigned)g), dim3(kThreads), 0, stream, src, dst,
-                       (int64_t)S_local, (int64_t)P, chunk_words, n_words, direction);
+                       dv, (int64_t)S_local, (int64_t)P, chunk_words, n_words, direction);
   }
   return hipGetLastError();
 }
