@@ -71,19 +71,28 @@ class Problem:
         if len(set(w.block_lens)) > 1:
             self.flags |= cp.CP_RING_ANYTHING
         if w.ulysses_degree > 1:
-            P = w.ulysses_degree
-            shp = (B, P * w.S_local, w.H // P, D)
+            # This rank regroups its own Q/K/V shard every step; the other ring
+            # ranks' blocks arrive already regrouped (they are regrouped once,
+            # here, as the peers would have done).
+            P, S_l = w.ulysses_degree, w.S_local
+            shp = (B, P * S_l, w.H // P, D)
             self.qr = torch.empty(shp, dtype=tdt, device="cuda")
-            self.kr = torch.empty(shp, dtype=tdt, device="cuda")
-            self.vr = torch.empty(shp, dtype=tdt, device="cuda")
-            self.back = torch.empty((B, w.S_local, w.H, D), dtype=torch.float32, device="cuda")
-            q_att, k_att, v_att = self.qr, self.kr, self.vr
+            self.k_own = self.k[:, :S_l].contiguous()
+            self.v_own = self.v[:, :S_l].contiguous()
+            self.kb = [torch.empty(shp, dtype=tdt, device="cuda") for _ in range(w.ring_degree)]
+            self.vb = [torch.empty(shp, dtype=tdt, device="cuda") for _ in range(w.ring_degree)]
+            for r in range(1, w.ring_degree):
+                cp.cp_ulysses_regroup(self.k[:, r * S_l:(r + 1) * S_l].contiguous(), self.kb[r], P,
+                                      cp.CP_REGROUP_SEQ_TO_HEAD)
+                cp.cp_ulysses_regroup(self.v[:, r * S_l:(r + 1) * S_l].contiguous(), self.vb[r], P,
+                                      cp.CP_REGROUP_SEQ_TO_HEAD)
+            self.back = torch.empty((B, S_l, w.H, D), dtype=torch.float32, device="cuda")
+            self.q_att = self.qr
         else:
-            q_att, k_att, v_att = self.q, self.k, self.v
-        self.q_att = q_att
-        offs = workloads.block_offsets(w.block_lens)
-        self.kb = [k_att[:, o:o + L] for o, L in zip(offs, w.block_lens)]
-        self.vb = [v_att[:, o:o + L] for o, L in zip(offs, w.block_lens)]
+            self.q_att = self.q
+            offs = workloads.block_offsets(w.block_lens)
+            self.kb = [self.k[:, o:o + L] for o, L in zip(offs, w.block_lens)]
+            self.vb = [self.v[:, o:o + L] for o, L in zip(offs, w.block_lens)]
         H = w.attn_H
         self.out = torch.empty((B, w.Sq, H, D), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((B, H, w.Sq), dtype=torch.float32, device="cuda")
@@ -95,8 +104,8 @@ class Problem:
         if w.ulysses_degree > 1:
             P = w.ulysses_degree
             cp.cp_ulysses_regroup(self.q, self.qr, P, cp.CP_REGROUP_SEQ_TO_HEAD)
-            cp.cp_ulysses_regroup(self.k, self.kr, P, cp.CP_REGROUP_SEQ_TO_HEAD)
-            cp.cp_ulysses_regroup(self.v, self.vr, P, cp.CP_REGROUP_SEQ_TO_HEAD)
+            cp.cp_ulysses_regroup(self.k_own, self.kb[0], P, cp.CP_REGROUP_SEQ_TO_HEAD)
+            cp.cp_ulysses_regroup(self.v_own, self.vb[0], P, cp.CP_REGROUP_SEQ_TO_HEAD)
         cp.cp_ring_attention(self.q_att, self.kb, self.vb, self.out, self.lse, scale=w.scale,
                              flags=self.flags, workspace=self.ws)
         if w.ulysses_degree > 1:
@@ -197,15 +206,19 @@ def cpu_baseline(w: workloads.Workload, inp, target_s: float):
         cores = 1
     if w.ulysses_degree > 1:
         P = w.ulysses_degree
-        q, k, v = (oracle.ulysses_regroup(x, P) for x in (inp.q, inp.k, inp.v))
+        q = oracle.ulysses_regroup(inp.q, P)
+        k_blocks = [oracle.ulysses_regroup(inp.k_shard(r), P) for r in range(w.ring_degree)]
+        v_blocks = [oracle.ulysses_regroup(inp.v_shard(r), P) for r in range(w.ring_degree)]
     else:
-        q, k, v = inp.q, inp.k, inp.v
-    offs = workloads.block_offsets(w.block_lens)
+        q = inp.q
+        offs = workloads.block_offsets(w.block_lens)
+        k_blocks = [inp.k[:, o:o + L] for o, L in zip(offs, w.block_lens)]
+        v_blocks = [inp.v[:, o:o + L] for o, L in zip(offs, w.block_lens)]
     H = w.attn_H
 
     def run(h0, h1):
-        kb = [k[:, o:o + L, h0:h1] for o, L in zip(offs, w.block_lens)]
-        vb = [v[:, o:o + L, h0:h1] for o, L in zip(offs, w.block_lens)]
+        kb = [x[:, :, h0:h1] for x in k_blocks]
+        vb = [x[:, :, h0:h1] for x in v_blocks]
         t = time.perf_counter()
         oracle.ring_attention(q[:, :, h0:h1], kb, vb, w.scale)
         return time.perf_counter() - t

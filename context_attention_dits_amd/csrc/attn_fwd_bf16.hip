@@ -78,6 +78,9 @@
 #ifndef CP_FWD_SCHED_PV
 #define CP_FWD_SCHED_PV 1  // pipeline the transposing V reads ahead of the PV MFMAs
 #endif
+#ifndef CP_FWD_SFIRST
+#define CP_FWD_SFIRST 1  // ping-pong MFMA half: next scores before the PV products
+#endif
 #ifndef CP_FWD_LAZY
 #define CP_FWD_LAZY 8.0f  // rescale threshold on the row maximum, log2 units
 #endif
@@ -499,6 +502,11 @@ attn_fwd_bf16_kernel(Params p) {
   // Only LDS reads and MFMAs: the vector ALU work of the step is in half_a.
   auto half_m = [&](auto last_tag, f32x16 (&s_next)[QB][C::KB], const char* k_read, const char* vt_read) {
     constexpr bool LAST = decltype(last_tag)::value;
+#if CP_FWD_SFIRST
+    // Scores first: the next softmax half waits on them, not on the PV
+    // products, which finish on the matrix cores behind it.
+    if constexpr (!LAST) scores(k_read, s_next);
+#endif
     const char* vfrag = vt_read + lane * 16;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -512,7 +520,9 @@ attn_fwd_bf16_kernel(Params p) {
           for (int qb = 0; qb < QB; ++qb)
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][kk2], o[qb][db], 0, 0, 0);
         }
+#if !CP_FWD_SFIRST
     if constexpr (!LAST) scores(k_read, s_next);
+#endif
 #if CP_FWD_SCHED_PV
     // Keep the LDS reads ahead of the MFMAs: eight reads up front, then two
     // per MFMA, then one, until the reads run out.
@@ -747,17 +757,18 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
 
 // Workgroup shape for one launch. The ping-pong kernel (8 waves, 256 query
 // rows, one workgroup per CU) is the faster one per workgroup; the 4-wave
-// kernel (128 rows, two workgroups per CU) drains a nearly empty last round
-// of workgroups faster, since a workgroup alone on a CU runs at full speed.
-// So: ping-pong unless its grid is under four rounds of 256 workgroups and
-// its last round is less than half full.
+// kernel (128 rows, two workgroups per CU) spreads a small grid, or a nearly
+// empty last round of workgroups, over twice as many CUs, and a workgroup
+// alone on a CU runs at full speed. So: ping-pong unless its grid is under
+// four rounds of 256 workgroups and its last (or only) round is less than
+// half full.
 int pick_waves(const FwdArgs& a) {
   if (a.D != 128) return 4;
   if (a.waves != 0) return a.waves;
   if (CP_FWD_NW != 0) return CP_FWD_NW;
   const int64_t n_wg8 = (int64_t)((a.Sq + 255) / 256) * a.H * a.B;
   const int64_t rounds = (n_wg8 + 255) / 256, last = n_wg8 - (rounds - 1) * 256;
-  return (rounds < 4 && rounds > 1 && last < 128) ? 4 : 8;
+  return (rounds < 4 && last < 128) ? 4 : 8;
 }
 
 template <int D>

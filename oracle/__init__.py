@@ -195,6 +195,25 @@ def ulysses_regroup_inv(y: np.ndarray, degree: int) -> np.ndarray:
         y.reshape(B, degree, S_l, Hl, D).transpose(0, 2, 1, 3, 4).reshape(B, S_l, degree * Hl, D))
 
 
+def usp_attention(q: np.ndarray, k_shards: Sequence[np.ndarray], v_shards: Sequence[np.ndarray],
+                  degree: int, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One rank's share of Unified (Ulysses x Ring) attention, exchanges as loopbacks.
+
+    "Paralelismo de contexto", "Atenção Unificada": an all-to-all regroups
+    heads and tokens, Ring Attention runs on the result, and the all-to-all is
+    reversed. q is this rank's [B, S_local, H, D] shard; k_shards[r] and
+    v_shards[r] are ring rank r's [B, S_local, H, D] shards, each regrouped the
+    same way and forming ring block r. Returns the output in the original
+    layout [B, S_local, H, D] and the LSE in the head-sharded layout
+    [B, H/P, P*S_local].
+    """
+    q_h = ulysses_regroup(q, degree)
+    kb = [ulysses_regroup(k, degree) for k in k_shards]
+    vb = [ulysses_regroup(v, degree) for v in v_shards]
+    o_h, lse = ring_attention(q_h, kb, vb, scale)
+    return ulysses_regroup_inv(o_h, degree), lse
+
+
 def brute_attention(q, k, v, scale: float):
     """Pure-Python attention with math.exp / math.log, for tiny shapes only.
 

@@ -304,3 +304,58 @@ def test_workload_ulysses2(cp):
     rows = workloads.sample_rows(w.Sq, 48, seed=2, must=_edges(w.Sq) + [w.S_local - 1, w.S_local])
     _check_rows(w.name, out_np, lse_np, ref["q"], ref["k"], ref["v"], w.scale, rows, w.dtype)
     assert np.array_equal(back.cpu().numpy(), oracle.ulysses_regroup_inv(out_np, P))
+
+
+def _usp_gpu(cp, q_local, k_shards, v_shards, P, scale):
+    """Unified attention share on the GPU: regroup Q and each K/V shard, ring, inverse regroup."""
+    def regroup(x):
+        t = dev(x, "bf16")
+        B, S_l, H, D = t.shape
+        y = torch.empty(B, P * S_l, H // P, D, dtype=torch.bfloat16, device="cuda")
+        cp.cp_ulysses_regroup(t, y, P, cp.CP_REGROUP_SEQ_TO_HEAD)
+        return y
+    q = regroup(q_local)
+    kb = [regroup(k) for k in k_shards]
+    vb = [regroup(v) for v in v_shards]
+    out, lse = cp.ring_attention(q, kb, vb, scale=scale)
+    B, S_l, H, D = q_local.shape
+    back = torch.empty(B, S_l, H, D, dtype=torch.float32, device="cuda")
+    cp.cp_ulysses_regroup(out, back, P, cp.CP_REGROUP_HEAD_TO_SEQ)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), back.cpu().numpy(), q.float().cpu().numpy(), \
+        [x.float().cpu().numpy() for x in kb], [x.float().cpu().numpy() for x in vb]
+
+
+@pytest.mark.parametrize("B,S_l,H,D,P,R", [(1, 40, 6, 128, 3, 2), (2, 33, 4, 64, 2, 3), (1, 100, 8, 128, 2, 2)])
+def test_usp_small_full_compare(cp, B, S_l, H, D, P, R):
+    """Unified attention share (regroup, ring over R blocks, inverse regroup) vs the oracle."""
+    say("usp small", B, S_l, H, D, P, R)
+    rng = np.random.default_rng(900 + S_l + P + R)
+    mk = lambda: workloads.round_to_bf16(rng.standard_normal((B, S_l, H, D), dtype=np.float32))  # noqa: E731
+    q, ks, vs = mk(), [mk() for _ in range(R)], [mk() for _ in range(R)]
+    scale = 1.0 / math.sqrt(D)
+    for wv in SHAPES:
+        with fwd_waves(cp, wv):
+            out, lse, back, *_ = _usp_gpu(cp, q, ks, vs, P, scale)
+        o_ref, l_ref = oracle.usp_attention(q, ks, vs, P, scale)
+        assert_close(f"usp out (waves={wv})", back, o_ref, TOL["bf16"]["o"])
+        assert_close(f"usp lse (waves={wv})", lse, l_ref, TOL["bf16"]["lse"])
+        assert np.array_equal(back, oracle.ulysses_regroup_inv(out, P)), "inverse regroup not bit-exact"
+
+
+def test_workload_usp_u2r2(cp):
+    w = workloads.by_name("flux1024_usp_u2r2_bf16")
+    say(w.name, "regroups + ring over 2 blocks + inverse regroup, sampled rows")
+    inp = workloads.make_inputs(w)
+    P, R = w.ulysses_degree, w.ring_degree
+    ks = [inp.k_shard(r) for r in range(R)]
+    vs = [inp.v_shard(r) for r in range(R)]
+    out, lse, back, q_h, kb, vb = _usp_gpu(cp, inp.q, ks, vs, P, w.scale)
+    # the GPU's regroups are bit-exact
+    assert np.array_equal(q_h, oracle.ulysses_regroup(inp.q, P))
+    for r in range(R):
+        assert np.array_equal(kb[r], oracle.ulysses_regroup(ks[r], P))
+    k_all, v_all = np.concatenate(kb, axis=1), np.concatenate(vb, axis=1)
+    rows = workloads.sample_rows(w.Sq, 48, seed=5, must=_edges(w.Sq) + [w.S_local - 1, w.S_local])
+    _check_rows(w.name, out, lse, q_h, k_all, v_all, w.scale, rows, w.dtype)
+    assert np.array_equal(back, oracle.ulysses_regroup_inv(out, P))

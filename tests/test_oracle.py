@@ -353,6 +353,63 @@ def test_ulysses_multi_rank_simulation_equals_full_attention(P):
         np.testing.assert_allclose(oracle.ulysses_regroup_inv(back, P), shard(full_o, r), atol=1e-12)
 
 
+@pytest.mark.parametrize("U,R", [(2, 2), (2, 3), (3, 2)])
+def test_usp_multi_rank_simulation_equals_full_attention(U, R):
+    """Unified attention on a U x R grid, exchanges simulated.
+
+    The sequence is cut into R ring chunks, each into U Ulysses shards; rank
+    (r, u) holds shard u of chunk r. The Ulysses all-to-all inside ring group r
+    leaves rank (r, u) with chunk r's tokens for head group u; Ring Attention
+    over the R chunks then sees every token; the reverse all-to-all returns each
+    rank's tokens with all heads. Every rank must end with full attention rows.
+    """
+    B, S_l, H, D = 1, 3, 2 * U, 8
+    S = U * R * S_l
+    Q, K, V = _rand((B, S, H, D), 71), _rand((B, S, H, D), 72), _rand((B, S, H, D), 73)
+    s = 1.0 / math.sqrt(D)
+    full_o, _ = oracle.attention(Q, K, V, s)
+    Hl = H // U
+    shard = lambda X, r, u: X[:, (r * U + u) * S_l:(r * U + u + 1) * S_l]  # noqa: E731
+    head_sharded = {}  # (name, r, u) -> chunk r's tokens, head group u
+    for name, X in (("q", Q), ("k", K), ("v", V)):
+        for r in range(R):
+            sent = [oracle.ulysses_regroup(shard(X, r, u), U) for u in range(U)]
+            for u in range(U):
+                head_sharded[(name, r, u)] = np.concatenate(
+                    [sent[src][:, u * S_l:(u + 1) * S_l] for src in range(U)], axis=1)
+    for u in range(U):
+        kb = [head_sharded[("k", r, u)] for r in range(R)]
+        vb = [head_sharded[("v", r, u)] for r in range(R)]
+        outs = {r: oracle.ring_attention(head_sharded[("q", r, u)], kb, vb, s)[0] for r in range(R)}
+        for r in range(R):
+            np.testing.assert_allclose(outs[r], full_o[:, r * U * S_l:(r + 1) * U * S_l, u * Hl:(u + 1) * Hl],
+                                       atol=1e-12)
+
+
+def test_usp_share_equals_full_attention_on_exchange_symmetric_data():
+    """Pin of ``usp_attention`` (exchanges as loopbacks).
+
+    When, inside every ring chunk, all U shards are the same tokens and all U
+    head groups carry the same values, each exchange hands a rank exactly what
+    its loopback produces, so one rank's share must equal full attention of the
+    whole sequence for that rank's tokens.
+    """
+    U, R, B, S_l, Hl, D = 2, 3, 1, 3, 2, 8
+    H = U * Hl
+    s = 1.0 / math.sqrt(D)
+    shards = {}
+    for name, seed in (("q", 81), ("k", 82), ("v", 83)):
+        base = _rand((R, B, S_l, Hl, D), seed)
+        shards[name] = [np.concatenate([base[r]] * U, axis=2) for r in range(R)]  # head groups equal
+    glob = {n: np.concatenate([x for r in range(R) for x in [shards[n][r]] * U], axis=1) for n in shards}
+    full_o, full_l = oracle.attention(glob["q"], glob["k"], glob["v"], s)
+    o, lse = oracle.usp_attention(shards["q"][0], shards["k"], shards["v"], U, s)
+    np.testing.assert_allclose(o, full_o[:, :S_l], atol=1e-12)
+    # LSE is head-sharded: [B, H/U, U*S_l], token chunk g holds this rank's tokens again
+    for g in range(U):
+        np.testing.assert_allclose(lse[:, :, g * S_l:(g + 1) * S_l], full_l[:, :Hl, :S_l], atol=1e-12)
+
+
 # ------------------------------------------------------- the input recipe ---
 
 def test_bf16_rounding_matches_torch():
@@ -373,3 +430,6 @@ def test_workload_inputs_are_seeded_and_bf16_exact():
     assert w.flops == 4 * 1 * 24 * 2304 * 4608 * 128
     u = workloads.by_name("flux1024_ulysses2_bf16")
     assert (u.attn_H, u.Sq, u.Skv) == (12, 4608, 4608)
+    usp = workloads.by_name("flux1024_usp_u2r2_bf16")
+    assert (usp.attn_H, usp.Sq, usp.Skv, usp.ring_degree) == (12, 2304, 4608, 2)
+    assert usp.ulysses_degree * usp.ring_degree * usp.S_local == 4608  # one rank of the 2x2 grid

@@ -32,11 +32,14 @@ import numpy as np
 class Workload:
     """One synthetic workload.
 
-    ``block_lens`` are the ring K/V block lengths (ring_degree entries).
-    For a Ulysses workload (``ulysses_degree > 1``) the drawn tensors are one
-    rank's sequence shard ``[B, S_local, H, D]``; after the local head/token
-    regroup the attention runs with ``H / ulysses_degree`` heads over
-    ``ulysses_degree * S_local`` tokens, as a single block.
+    ``block_lens`` are the ring K/V block lengths (ring_degree entries) as the
+    attention sees them. For a Ulysses workload (``ulysses_degree = P > 1``)
+    the drawn Q is one rank's sequence shard ``[B, S_local, H, D]`` and K/V
+    hold the ring ranks' shards back to back, ``[B, ring_degree * S_local, H,
+    D]``; after the local head/token regroup of each shard the attention runs
+    with ``H / P`` heads, ``P * S_local`` queries and one block of
+    ``P * S_local`` keys per ring rank (ring_degree 1: plain Ulysses; more:
+    Unified attention).
     """
 
     index: int
@@ -86,6 +89,11 @@ WORKLOADS: List[Workload] = [
              block_lens=(8192, 8192, 8192, 8192)),
     Workload(4, "ring_anything3_uneven_bf16", "bf16", B=2, H=24, D=128, Sq=1536,
              block_lens=(1536, 1536, 1535)),
+    # Unified attention, one rank of a 2 (Ulysses) x 2 (ring) grid on the FLUX
+    # 1024px sequence: 1152 tokens per rank, 12 heads over 2304 queries after
+    # the regroup, two ring blocks of 2304 keys.
+    Workload(5, "flux1024_usp_u2r2_bf16", "bf16", B=1, H=24, D=128, Sq=2304, block_lens=(2304, 2304),
+             ulysses_degree=2, S_local=1152),
 ]
 
 
@@ -144,9 +152,18 @@ class Inputs:
     """float32 arrays holding exactly the values the kernels consume."""
 
     q: np.ndarray  # [B, Sq, H, D]   (Ulysses: [B, S_local, H, D] before regroup)
-    k: np.ndarray  # [B, Skv, H, D]  (Ulysses: [B, S_local, H, D])
+    k: np.ndarray  # [B, Skv, H, D]  (Ulysses: [B, ring_degree * S_local, H, D])
     v: np.ndarray
     workload: Workload
+
+    def k_shard(self, r: int) -> np.ndarray:
+        """Ulysses: ring rank r's K shard [B, S_local, H, D], before its regroup."""
+        S_l = self.workload.S_local
+        return self.k[:, r * S_l:(r + 1) * S_l]
+
+    def v_shard(self, r: int) -> np.ndarray:
+        S_l = self.workload.S_local
+        return self.v[:, r * S_l:(r + 1) * S_l]
 
     def k_block(self, i: int) -> np.ndarray:
         offs = block_offsets(self.workload.block_lens)
@@ -172,8 +189,8 @@ def make_inputs(w: Workload, q_scale: float = 1.0) -> Inputs:
     """
     rng = np.random.default_rng(w.seed)
     if w.ulysses_degree > 1:
-        shp = (w.B, w.S_local, w.H, w.D)
-        q = rng.standard_normal(shp, dtype=np.float32)
+        q = rng.standard_normal((w.B, w.S_local, w.H, w.D), dtype=np.float32)
+        shp = (w.B, w.ring_degree * w.S_local, w.H, w.D)
         k = rng.standard_normal(shp, dtype=np.float32)
         v = rng.standard_normal(shp, dtype=np.float32)
     else:
