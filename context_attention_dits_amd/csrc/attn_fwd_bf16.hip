@@ -78,9 +78,6 @@
 #ifndef CP_FWD_SCHED_PV
 #define CP_FWD_SCHED_PV 1  // pipeline the transposing V reads ahead of the PV MFMAs
 #endif
-#ifndef CP_FWD_SFIRST
-#define CP_FWD_SFIRST 1  // ping-pong MFMA half: next scores before the PV products
-#endif
 #ifndef CP_FWD_LAZY
 #define CP_FWD_LAZY 8.0f  // rescale threshold on the row maximum, log2 units
 #endif
@@ -502,11 +499,9 @@ attn_fwd_bf16_kernel(Params p) {
   // Only LDS reads and MFMAs: the vector ALU work of the step is in half_a.
   auto half_m = [&](auto last_tag, f32x16 (&s_next)[QB][C::KB], const char* k_read, const char* vt_read) {
     constexpr bool LAST = decltype(last_tag)::value;
-#if CP_FWD_SFIRST
     // Scores first: the next softmax half waits on them, not on the PV
     // products, which finish on the matrix cores behind it.
     if constexpr (!LAST) scores(k_read, s_next);
-#endif
     const char* vfrag = vt_read + lane * 16;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -520,9 +515,6 @@ attn_fwd_bf16_kernel(Params p) {
           for (int qb = 0; qb < QB; ++qb)
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][kk2], o[qb][db], 0, 0, 0);
         }
-#if !CP_FWD_SFIRST
-    if constexpr (!LAST) scores(k_read, s_next);
-#endif
 #if CP_FWD_SCHED_PV
     // Keep the LDS reads ahead of the MFMAs: eight reads up front, then two
     // per MFMA, then one, until the reads run out.

@@ -32,7 +32,9 @@ Pins: every function here is checked by the CPU tests against something other
 than itself -- a pure-Python brute force, closed forms, a library attention
 routine, hand-computed golden values under ``tests/golden/`` and invariants
 (ring over any split == single pass, shift/permutation invariance, regroup
-round trip, a multi-rank Ulysses simulation). No function is "parity unpinned".
+round trip, multi-rank Ulysses and Unified simulations); the backward against
+central differences of the forward, a library autograd and its invariants.
+No function is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -48,6 +50,9 @@ __all__ = [
     "ring_attention",
     "ulysses_regroup",
     "ulysses_regroup_inv",
+    "usp_attention",
+    "attention_bwd",
+    "ring_attention_bwd",
     "brute_attention",
 ]
 
@@ -212,6 +217,70 @@ def usp_attention(q: np.ndarray, k_shards: Sequence[np.ndarray], v_shards: Seque
     vb = [ulysses_regroup(v, degree) for v in v_shards]
     o_h, lse = ring_attention(q_h, kb, vb, scale)
     return ulysses_regroup_inv(o_h, degree), lse
+
+
+def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, o: np.ndarray, lse: np.ndarray,
+                  do: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of ``attention`` with respect to q, k and v, given dL/dO.
+
+    The pages run Ring Attention for training as well as inference (only the
+    Ring Anything variant is inference-only: "Paralelismo de contexto",
+    "Ring Anything Attention"), so the ring's blocks need a backward pass.
+    The pages print no formula; this is the derivative of the definition in
+    ``attention`` (o and lse are that function's outputs for q, k, v), for one
+    (b, h) pair:
+        P_ij  = exp(scale * <q_i, k_j> - LSE_i)      (the softmax weights)
+        D_i   = sum_d dO_id * O_id
+        dV_j  = sum_i P_ij dO_i
+        dP_ij = <dO_i, v_j>
+        dS_ij = P_ij * (dP_ij - D_i)
+        dQ_i  = scale * sum_j dS_ij k_j
+        dK_j  = scale * sum_i dS_ij q_i
+    All float64; returns dq [B, Sq, H, D], dk and dv [B, Skv, H, D].
+    """
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    dq = np.zeros((B, Sq, H, D), dtype=_F64)
+    dk = np.zeros((B, Skv, H, D), dtype=_F64)
+    dv = np.zeros((B, Skv, H, D), dtype=_F64)
+    if Skv == 0 or Sq == 0:
+        return dq, dk, dv
+    for b in range(B):
+        for h in range(H):
+            qh = np.asarray(q[b, :, h, :], dtype=_F64)
+            kh = np.asarray(k[b, :, h, :], dtype=_F64)
+            vh = np.asarray(v[b, :, h, :], dtype=_F64)
+            oh = np.asarray(o[b, :, h, :], dtype=_F64)
+            doh = np.asarray(do[b, :, h, :], dtype=_F64)
+            lh = np.asarray(lse[b, h, :], dtype=_F64)[:, None]
+            p = np.exp(scale * (qh @ kh.T) - lh)      # [Sq, Skv]
+            d = (doh * oh).sum(axis=1, keepdims=True)  # [Sq, 1]
+            dv[b, :, h, :] = p.T @ doh
+            ds = p * (doh @ vh.T - d)
+            dq[b, :, h, :] = scale * (ds @ kh)
+            dk[b, :, h, :] = scale * (ds.T @ qh)
+    return dq, dk, dv
+
+
+def ring_attention_bwd(q: np.ndarray, k_blocks: Sequence[np.ndarray], v_blocks: Sequence[np.ndarray],
+                       o: np.ndarray, lse: np.ndarray, do: np.ndarray,
+                       scale: float) -> Tuple[np.ndarray, List[np.ndarray], List[np.ndarray]]:
+    """Backward of one rank's ring share, block by block.
+
+    o and lse are the merged (full-ring) output and LSE. Block i contributes
+    ``attention_bwd`` evaluated with those global o and lse on its own keys:
+    the softmax weights of its keys are exp(scale <q, k> - LSE) with the
+    global LSE, so the per-block terms add up to the single-pass gradient.
+    Returns dq (summed over blocks) and each block's dk, dv.
+    """
+    dq = np.zeros(q.shape, dtype=_F64)
+    dks, dvs = [], []
+    for kb, vb in zip(k_blocks, v_blocks):
+        dq_i, dk_i, dv_i = attention_bwd(q, kb, vb, o, lse, do, scale)
+        dq += dq_i
+        dks.append(dk_i)
+        dvs.append(dv_i)
+    return dq, dks, dvs
 
 
 def brute_attention(q, k, v, scale: float):

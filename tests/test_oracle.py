@@ -410,6 +410,87 @@ def test_usp_share_equals_full_attention_on_exchange_symmetric_data():
         np.testing.assert_allclose(lse[:, :, g * S_l:(g + 1) * S_l], full_l[:, :Hl, :S_l], atol=1e-12)
 
 
+# ---------------------------------------------------------------- backward ---
+
+def _loss(q, k, v, do, s):
+    o, _ = oracle.attention(q, k, v, s)
+    return float((o * do).sum())
+
+
+def test_bwd_matches_central_differences():
+    """dL/dq, dL/dk, dL/dv for L = sum(dO * O) against central differences of the forward."""
+    B, Sq, Skv, H, D = 1, 3, 4, 2, 3
+    q, k, v, do = (_rand(shp, sd) for shp, sd in (((B, Sq, H, D), 91), ((B, Skv, H, D), 92),
+                                                  ((B, Skv, H, D), 93), ((B, Sq, H, D), 94)))
+    s = 0.7
+    o, lse = oracle.attention(q, k, v, s)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, o, lse, do, s)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            lp = _loss(**{**args, name: xp}, do=do, s=s)
+            lm = _loss(**{**args, name: xm}, do=do, s=s)
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=1e-7, rtol=1e-6, err_msg=name)
+
+
+def test_bwd_matches_torch_autograd_float64():
+    torch = pytest.importorskip("torch")
+    B, Sq, Skv, H, D = 2, 5, 7, 3, 8
+    q, k, v, do = (_rand(shp, sd) for shp, sd in (((B, Sq, H, D), 95), ((B, Skv, H, D), 96),
+                                                  ((B, Skv, H, D), 97), ((B, Sq, H, D), 98)))
+    s = 1.0 / math.sqrt(D)
+    o, lse = oracle.attention(q, k, v, s)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, o, lse, do, s)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    x = torch.einsum("bqhd,bkhd->bhqk", tq, tk) * s
+    to = torch.einsum("bhqk,bkhd->bqhd", torch.softmax(x, dim=-1), tv)
+    to.backward(torch.tensor(do, dtype=torch.float64))
+    for g, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(g, t.grad.numpy(), atol=1e-12)
+
+
+def test_bwd_invariants():
+    """Key-shift invariance gives sum_j dK_j = 0; rows of P sum to 1 give
+    sum_j dV_j = sum_i dO_i; identical keys make the output independent of q."""
+    B, Sq, Skv, H, D = 1, 6, 9, 2, 4
+    q, k, v, do = (_rand(shp, sd) for shp, sd in (((B, Sq, H, D), 101), ((B, Skv, H, D), 102),
+                                                  ((B, Skv, H, D), 103), ((B, Sq, H, D), 104)))
+    s = 0.5
+    o, lse = oracle.attention(q, k, v, s)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, o, lse, do, s)
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(axis=1), do.sum(axis=1), atol=1e-12)
+    k_same = np.broadcast_to(k[:, :1], k.shape).copy()
+    o2, lse2 = oracle.attention(q, k_same, v, s)
+    dq2, _, _ = oracle.attention_bwd(q, k_same, v, o2, lse2, do, s)
+    np.testing.assert_allclose(dq2, 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("lens", [(4, 5), (3, 0, 6), (1, 1, 1, 6)])
+def test_ring_bwd_equals_single_pass(lens):
+    B, Sq, H, D = 2, 5, 2, 4
+    Skv = sum(lens)
+    q, k, v, do = (_rand(shp, sd) for shp, sd in (((B, Sq, H, D), 111), ((B, Skv, H, D), 112),
+                                                  ((B, Skv, H, D), 113), ((B, Sq, H, D), 114)))
+    s = 0.6
+    o, lse = oracle.attention(q, k, v, s)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, o, lse, do, s)
+    offs = workloads.block_offsets(lens)
+    kb = [k[:, a:a + L] for a, L in zip(offs, lens)]
+    vb = [v[:, a:a + L] for a, L in zip(offs, lens)]
+    o_r, lse_r = oracle.ring_attention(q, kb, vb, s)
+    dq_r, dks, dvs = oracle.ring_attention_bwd(q, kb, vb, o_r, lse_r, do, s)
+    np.testing.assert_allclose(dq_r, dq, atol=1e-12)
+    np.testing.assert_allclose(np.concatenate(dks, axis=1), dk, atol=1e-12)
+    np.testing.assert_allclose(np.concatenate(dvs, axis=1), dv, atol=1e-12)
+
+
 # ------------------------------------------------------- the input recipe ---
 
 def test_bf16_rounding_matches_torch():
