@@ -17,7 +17,7 @@ import math
 from typing import Optional, Sequence, Tuple
 
 from . import _lib
-from ._lib import (CP_BF16, CP_BLOCK_ACCUMULATE, CP_ERR_HIP, CP_ERR_INVALID_ARG,  # noqa: F401
+from ._lib import (CP_BF16, CP_BLOCK_ACCUMULATE, CP_BWD_ACCUMULATE_DQ, CP_ERR_HIP, CP_ERR_INVALID_ARG,  # noqa: F401
                    CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_F32, CP_OK, CP_REGROUP_HEAD_TO_SEQ,
                    CP_REGROUP_SEQ_TO_HEAD, CP_RING_ANYTHING, CP_RING_SEPARATE_MERGE, STATUS_NAMES)
 
@@ -25,6 +25,8 @@ __all__ = [
     "CpAttnError", "load", "cp_abi_version", "cp_last_error", "cp_attn_set_fwd_waves", "cp_attn_block_fwd",
     "cp_lse_merge",
     "cp_ring_attention", "cp_ring_attention_workspace_size", "cp_ulysses_regroup",
+    "cp_attn_bwd_workspace_size", "cp_attn_bwd_prep", "cp_attn_block_bwd", "cp_ring_attention_bwd",
+    "ring_attention", "ring_attention_bwd",
 ]
 
 
@@ -152,6 +154,37 @@ def cp_lse_merge(out_acc, lse_acc, out_blk, lse_blk, stream=None):
     _check(st, "cp_lse_merge")
 
 
+def _block_list(q, k_blocks, v_blocks, dev, dtype=None, what="K/V"):
+    """Check a list of [B, L_i, H, D] block pairs against q; returns (P, lens, shared stride triple)."""
+    B, _, H, D = q.shape
+    P = len(k_blocks)
+    if P < 1 or len(v_blocks) != P:
+        raise ValueError(f"need as many {what} blocks of each kind (>= 1)")
+    stride0 = None
+    for i, (kb, vb) in enumerate(zip(k_blocks, v_blocks)):
+        _gpu(f"{what} block {i}", _bshd(f"{what} block", kb), dev); _gpu(f"{what} block {i}", _bshd(f"{what} block", vb), dev)
+        L = kb.shape[1]
+        if tuple(kb.shape) != (B, L, H, D) or tuple(vb.shape) != (B, L, H, D):
+            raise ValueError(f"{what} block {i}: shapes {tuple(kb.shape)}/{tuple(vb.shape)} do not match q")
+        want = q.dtype if dtype is None else dtype
+        if kb.dtype != want or vb.dtype != want:
+            raise TypeError(f"every {what} block must have dtype {want}")
+        s = (kb.stride(0), kb.stride(1), kb.stride(2))
+        if stride0 is None:
+            stride0 = s
+        if s != stride0 or (vb.stride(0), vb.stride(1), vb.stride(2)) != stride0:
+            raise ValueError(f"every {what} block must share one stride triple")
+    lens = (ctypes.c_int * P)(*[int(kb.shape[1]) for kb in k_blocks])
+    return P, lens, stride0
+
+
+def _workspace(workspace, dev):
+    if workspace is None:
+        return None, 0
+    _gpu("workspace", workspace, dev)
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def cp_ring_attention_workspace_size(B: int, H: int, Sq: int, D: int, flags: int = 0) -> int:
     return int(_lib.load().cp_ring_attention_workspace_size(B, H, Sq, D, flags))
 
@@ -167,34 +200,15 @@ def cp_ring_attention(q, k_blocks: Sequence, v_blocks: Sequence, out, lse, scale
     dev = _gpu("q", _bshd("q", q)).device
     _gpu("out", _bshd("out", out), dev); _gpu("lse", lse, dev)
     B, Sq, H, D = q.shape
-    P = len(k_blocks)
-    if P < 1 or len(v_blocks) != P:
-        raise ValueError("need as many v_blocks as k_blocks (>= 1)")
-    stride0 = None
-    for i, (kb, vb) in enumerate(zip(k_blocks, v_blocks)):
-        _gpu(f"k_blocks[{i}]", _bshd("k block", kb), dev); _gpu(f"v_blocks[{i}]", _bshd("v block", vb), dev)
-        L = kb.shape[1]
-        if tuple(kb.shape) != (B, L, H, D) or tuple(vb.shape) != (B, L, H, D):
-            raise ValueError(f"block {i}: shapes {tuple(kb.shape)}/{tuple(vb.shape)} do not match q")
-        if kb.dtype != q.dtype or vb.dtype != q.dtype:
-            raise TypeError("q and every K/V block must share a dtype")
-        s = (kb.stride(0), kb.stride(1), kb.stride(2))
-        if stride0 is None:
-            stride0 = s
-        if s != stride0 or (vb.stride(0), vb.stride(1), vb.stride(2)) != stride0:
-            raise ValueError("every K/V block must share one stride triple")
+    P, lens, stride0 = _block_list(q, k_blocks, v_blocks, dev)
     if tuple(out.shape) != (B, Sq, H, D):
         raise ValueError("out must be [B, Sq, H, D]")
     _f32("out", out)
     _lse_shape("lse", lse, B, H, Sq)
     kptr = (ctypes.c_void_p * P)(*[kb.data_ptr() for kb in k_blocks])
     vptr = (ctypes.c_void_p * P)(*[vb.data_ptr() for vb in v_blocks])
-    lens = (ctypes.c_int * P)(*[int(kb.shape[1]) for kb in k_blocks])
     kvs = (ctypes.c_int64 * 3)(*stride0)
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        _gpu("workspace", workspace, dev)
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace(workspace, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     st = lib.cp_ring_attention(q.data_ptr(), _strides(q), kptr, vptr, kvs, lens, P, _dtype_code(q), B, H,
                                D, Sq, scale, flags, out.data_ptr(), _strides(out), lse.data_ptr(), ws_ptr,
@@ -227,6 +241,80 @@ def cp_ulysses_regroup(inp, out, degree: int, direction: int = CP_REGROUP_SEQ_TO
     _check(st, "cp_ulysses_regroup")
 
 
+def cp_attn_bwd_workspace_size(B: int, H: int, Sq: int, D: int) -> int:
+    return int(_lib.load().cp_attn_bwd_workspace_size(B, H, Sq, D))
+
+
+def cp_attn_bwd_prep(out, dout, workspace, dtype: int = CP_BF16, stream=None):
+    """Fill the backward workspace (dO in bfloat16 and D = rowsum(dO * O)); see cp_attn_bwd_prep."""
+    lib = _lib.load()
+    dev = _gpu("out", _bshd("out", out)).device
+    _gpu("dout", _bshd("dout", dout), dev)
+    B, Sq, H, D = out.shape
+    if tuple(dout.shape) != (B, Sq, H, D):
+        raise ValueError("dout must match out")
+    _f32("out", out); _f32("dout", dout)
+    ws_ptr, ws_bytes = _workspace(workspace, dev)
+    st = lib.cp_attn_bwd_prep(out.data_ptr(), _strides(out), dout.data_ptr(), _strides(dout), dtype, B, H, Sq, D,
+                              ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "cp_attn_bwd_prep")
+
+
+def cp_attn_block_bwd(q, k, v, lse, workspace, dq, dk, dv, scale: Optional[float] = None, flags: int = 0,
+                      stream=None):
+    """Gradients of one K/V block (dq overwritten or, with CP_BWD_ACCUMULATE_DQ, added to); see the header."""
+    lib = _lib.load()
+    dev = _gpu("q", _bshd("q", q)).device
+    B, Sq, H, D = q.shape
+    _, lens, kvs = _block_list(q, [k], [v], dev)
+    _, _, dkvs = _block_list(q, [dk], [dv], dev, dtype=_torch().float32, what="dK/dV")
+    if dk.shape[1] != k.shape[1]:
+        raise ValueError("dk/dv must match k/v")
+    _gpu("dq", _bshd("dq", dq), dev); _gpu("lse", lse, dev)
+    if tuple(dq.shape) != (B, Sq, H, D):
+        raise ValueError("dq must be [B, Sq, H, D]")
+    _f32("dq", dq)
+    _lse_shape("lse", lse, B, H, Sq)
+    ws_ptr, ws_bytes = _workspace(workspace, dev)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.cp_attn_block_bwd(q.data_ptr(), _strides(q), k.data_ptr(), v.data_ptr(), (ctypes.c_int64 * 3)(*kvs),
+                               _dtype_code(q), B, H, D, Sq, lens[0], scale, flags, lse.data_ptr(), ws_ptr, ws_bytes,
+                               dq.data_ptr(), _strides(dq), dk.data_ptr(), dv.data_ptr(),
+                               (ctypes.c_int64 * 3)(*dkvs), _stream(stream))
+    _check(st, "cp_attn_block_bwd")
+
+
+def cp_ring_attention_bwd(q, k_blocks: Sequence, v_blocks: Sequence, out, lse, dout, dq, dk_blocks: Sequence,
+                          dv_blocks: Sequence, scale: Optional[float] = None, flags: int = 0, workspace=None,
+                          stream=None):
+    """Backward of cp_ring_attention for one rank: dq and per-block dk, dv; see cp_ring_attention_bwd."""
+    lib = _lib.load()
+    dev = _gpu("q", _bshd("q", q)).device
+    B, Sq, H, D = q.shape
+    P, lens, kvs = _block_list(q, k_blocks, v_blocks, dev)
+    P2, lens2, dkvs = _block_list(q, dk_blocks, dv_blocks, dev, dtype=_torch().float32, what="dK/dV")
+    if P2 != P or list(lens2) != list(lens):
+        raise ValueError("dk/dv blocks must match the K/V blocks")
+    for name, t in (("out", out), ("dout", dout), ("dq", dq)):
+        _gpu(name, _bshd(name, t), dev)
+        _f32(name, t)
+        if tuple(t.shape) != (B, Sq, H, D):
+            raise ValueError(f"{name} must be [B, Sq, H, D]")
+    _gpu("lse", lse, dev)
+    _lse_shape("lse", lse, B, H, Sq)
+    kptr = (ctypes.c_void_p * P)(*[t.data_ptr() for t in k_blocks])
+    vptr = (ctypes.c_void_p * P)(*[t.data_ptr() for t in v_blocks])
+    dkptr = (ctypes.c_void_p * P)(*[t.data_ptr() for t in dk_blocks])
+    dvptr = (ctypes.c_void_p * P)(*[t.data_ptr() for t in dv_blocks])
+    ws_ptr, ws_bytes = _workspace(workspace, dev)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.cp_ring_attention_bwd(q.data_ptr(), _strides(q), kptr, vptr, (ctypes.c_int64 * 3)(*kvs), lens, P,
+                                   _dtype_code(q), B, H, D, Sq, scale, flags, out.data_ptr(), _strides(out),
+                                   dout.data_ptr(), _strides(dout), lse.data_ptr(), dq.data_ptr(), _strides(dq),
+                                   dkptr, dvptr, (ctypes.c_int64 * 3)(*dkvs), ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "cp_ring_attention_bwd")
+
+
 # ------------------------------------------------------- allocating helpers ---
 
 def ring_attention(q, k_blocks, v_blocks, scale: Optional[float] = None, ring_anything: Optional[bool] = None,
@@ -246,3 +334,28 @@ def ring_attention(q, k_blocks, v_blocks, scale: Optional[float] = None, ring_an
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     cp_ring_attention(q, k_blocks, v_blocks, out, lse, scale=scale, flags=flags, workspace=ws, stream=stream)
     return out, lse
+
+
+def ring_attention_bwd(q, k_blocks, v_blocks, out, lse, dout, scale: Optional[float] = None,
+                       ring_anything: Optional[bool] = None, stream=None) -> Tuple:
+    """Allocate the gradients and workspace and run cp_ring_attention_bwd; returns (dq, [dk_i], [dv_i]).
+
+    dk_i, dv_i are views of one [B, sum(L_i), H, D] float32 buffer each.
+    """
+    torch = _torch()
+    B, Sq, H, D = q.shape
+    dq = torch.empty((B, Sq, H, D), dtype=torch.float32, device=q.device)
+    lens = [kb.shape[1] for kb in k_blocks]
+    # one [B, sum(lens), H, D] buffer each, so the blocks share a stride triple
+    dk_all = torch.empty((B, sum(lens), H, D), dtype=torch.float32, device=q.device)
+    dv_all = torch.empty((B, sum(lens), H, D), dtype=torch.float32, device=q.device)
+    offs = [sum(lens[:i]) for i in range(len(lens))]
+    dk = [dk_all[:, a:a + L] for a, L in zip(offs, lens)]
+    dv = [dv_all[:, a:a + L] for a, L in zip(offs, lens)]
+    if ring_anything is None:
+        ring_anything = len(set(lens)) > 1 or 0 in lens
+    nbytes = cp_attn_bwd_workspace_size(B, H, Sq, D)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    cp_ring_attention_bwd(q, k_blocks, v_blocks, out, lse, dout, dq, dk, dv, scale=scale,
+                          flags=CP_RING_ANYTHING if ring_anything else 0, workspace=ws, stream=stream)
+    return dq, dk, dv

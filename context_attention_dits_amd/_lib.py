@@ -30,6 +30,8 @@ CP_BLOCK_ACCUMULATE = 0x1
 CP_RING_ANYTHING = 0x2
 CP_RING_SEPARATE_MERGE = 0x4
 
+CP_BWD_ACCUMULATE_DQ = 0x1
+
 CP_REGROUP_SEQ_TO_HEAD = 0
 CP_REGROUP_HEAD_TO_SEQ = 1
 
@@ -49,6 +51,14 @@ _SIGNATURES = {
                                ctypes.POINTER(_i), _i, _i, _i, _i, _i, _i, ctypes.c_float, ctypes.c_uint,
                                _vp, _i64p, _vp, _vp, ctypes.c_size_t, _vp]),
     "cp_ulysses_regroup": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "cp_attn_bwd_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "cp_attn_bwd_prep": (_i, [_vp, _i64p, _vp, _i64p, _i, _i, _i, _i, _i, _vp, ctypes.c_size_t, _vp]),
+    "cp_attn_block_bwd": (_i, [_vp, _i64p, _vp, _vp, _i64p, _i, _i, _i, _i, _i, _i, ctypes.c_float,
+                               ctypes.c_uint, _vp, _vp, ctypes.c_size_t, _vp, _i64p, _vp, _vp, _i64p, _vp]),
+    "cp_ring_attention_bwd": (_i, [_vp, _i64p, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64p,
+                                   ctypes.POINTER(_i), _i, _i, _i, _i, _i, _i, ctypes.c_float, ctypes.c_uint,
+                                   _vp, _i64p, _vp, _i64p, _vp, _vp, _i64p, ctypes.POINTER(_vp),
+                                   ctypes.POINTER(_vp), _i64p, _vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None

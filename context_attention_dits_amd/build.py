@@ -22,7 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libcpattn.so"
-SOURCES = ["api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "lse_merge.hip", "regroup.hip"]
+SOURCES = ["api.hip", "attn_bwd_bf16.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "lse_merge.hip", "regroup.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are left out of the generated code on purpose.

@@ -260,6 +260,204 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
   return CP_OK;
 }
 
+size_t cp_attn_bwd_workspace_size(int B, int H, int Sq, int D) {
+  if (B <= 0 || H <= 0 || Sq <= 0 || D <= 0) return 0;
+  return align_up((size_t)B * Sq * H * D * 2, 256) + align_up((size_t)B * H * Sq * sizeof(float), 256);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The two parts of the backward workspace: dO in bf16 and delta.
+struct BwdWorkspace {
+  void* dout_b;
+  float* delta;
+};
+
+cp_status_t bwd_workspace(const char* fn, void* workspace, size_t bytes, int B, int H, int Sq, int D,
+                          BwdWorkspace* w) {
+  const size_t need = cp_attn_bwd_workspace_size(B, H, Sq, D);
+  if (workspace == nullptr || bytes < need)
+    return fail(CP_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace == nullptr ? (size_t)0 : bytes);
+  if (!aligned(workspace, 256)) return fail(CP_ERR_UNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
+  w->dout_b = workspace;
+  w->delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)B * Sq * H * D * 2, 256));
+  return CP_OK;
+}
+
+cp_status_t check_bwd_common(const char* fn, int dtype, int B, int H, int D, int Sq, float scale) {
+  if (dtype != CP_BF16)
+    return fail(CP_ERR_UNSUPPORTED, "%s: the backward supports dtype CP_BF16 (1) only (got %d)", fn, dtype);
+  if (D != 64 && D != 128)
+    return fail(CP_ERR_UNSUPPORTED, "%s: head dim D=%d is not supported (D = 64 or 128)", fn, D);
+  if (B < 0 || H < 0 || Sq < 0) return fail(CP_ERR_INVALID_ARG, "%s: sizes must be non-negative", fn);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(CP_ERR_INVALID_ARG, "%s: scale must be finite and > 0 (got %g)", fn, (double)scale);
+  return CP_OK;
+}
+
+// Arguments of one block's backward once the common checks passed.
+cp_status_t run_block_bwd(const void* q, Strides qs, const void* k, const void* v, Strides kvs, int B, int H,
+                          int D, int Sq, int Skv, float scale, bool accumulate_dq, const float* lse,
+                          const BwdWorkspace& w, float* dq, Strides dqs, float* dk, float* dv, Strides dkvs,
+                          hipStream_t stream) {
+  if (Skv == 0 && accumulate_dq) return CP_OK;  // no keys: nothing to add
+  cpattn::BwdArgs a;
+  a.q = q; a.k = k; a.v = v;
+  a.dout_b = w.dout_b; a.lse = lse; a.delta = w.delta;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.qs = qs; a.kvs = kvs; a.dqs = dqs; a.dkvs = dkvs;
+  a.B = B; a.H = H; a.D = D; a.Sq = Sq; a.Skv = Skv;
+  a.scale = scale;
+  a.accumulate_dq = accumulate_dq;
+  return hip_status(cpattn::launch_attn_bwd_bf16(a, stream), "attn_bwd_bf16");
+}
+
+// Q side (when Sq > 0) and the stride limits of the tile loads: row offsets
+// within a 32-row tile are 32-bit, so sequence strides (and H*D, the row
+// stride of the bf16 dO copy) stay at most 2^24 elements.
+cp_status_t check_bwd_tensors(const char* fn, int Sq, int H, int D, const void* q, Strides qs, Strides kvs,
+                              const float* lse, const float* dq, Strides dqs, Strides dkvs) {
+  cp_status_t st;
+  if ((st = check_strides("k/v", kvs, 2, 2, H, D)) != CP_OK) return st;
+  if ((st = check_strides("dk/dv", dkvs, 4, 2, H, D)) != CP_OK) return st;
+  if (qs.s > (int64_t(1) << 24) || kvs.s > (int64_t(1) << 24) || (int64_t)H * D > (int64_t(1) << 24))
+    return fail(CP_ERR_UNSUPPORTED, "%s: q and k/v sequence strides and H*D must not exceed 2^24 elements", fn);
+  if (Sq == 0) return CP_OK;
+  if (!q || !dq || !lse) return fail(CP_ERR_INVALID_ARG, "%s: q, dq and lse must be non-null", fn);
+  if (!aligned(q, 16) || !aligned(dq, 16) || !aligned(lse, 4))
+    return fail(CP_ERR_UNSUPPORTED, "%s: q and dq must be 16-byte aligned, lse 4-byte aligned", fn);
+  // q rows are fetched in tiles through a byte range that ends at row Sq, so
+  // a row must not extend past the next one's start even when Sq == 1.
+  if ((st = check_strides("q", qs, 2, 2, H, D)) != CP_OK) return st;
+  if ((st = check_strides("dq", dqs, 4, Sq, H, D)) != CP_OK) return st;
+  return CP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status_t cp_attn_bwd_prep(const float* out, const int64_t* out_strides, const float* dout,
+                             const int64_t* dout_strides, int dtype, int B, int H, int Sq, int D,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  cp_status_t st = check_bwd_common("cp_attn_bwd_prep", dtype, B, H, D, Sq, 1.f);
+  if (st != CP_OK) return st;
+  if (B == 0 || H == 0 || Sq == 0) return CP_OK;
+  if (!out || !dout) return fail(CP_ERR_INVALID_ARG, "cp_attn_bwd_prep: out and dout must be non-null");
+  if (!aligned(out, 16) || !aligned(dout, 16))
+    return fail(CP_ERR_UNSUPPORTED, "cp_attn_bwd_prep: out and dout must be 16-byte aligned");
+  if ((int64_t)B * Sq * H * (D / 8) > 0x7fffffff)
+    return fail(CP_ERR_UNSUPPORTED, "cp_attn_bwd_prep: B*Sq*H*D/8 must be below 2^31");
+  const Strides os = resolve(out_strides, Sq, H, D);
+  const Strides ds = resolve(dout_strides, Sq, H, D);
+  if ((st = check_strides("out", os, 4, Sq, H, D)) != CP_OK) return st;
+  if ((st = check_strides("dout", ds, 4, Sq, H, D)) != CP_OK) return st;
+  BwdWorkspace w;
+  if ((st = bwd_workspace("cp_attn_bwd_prep", workspace, workspace_bytes, B, H, Sq, D, &w)) != CP_OK) return st;
+  return hip_status(cpattn::launch_attn_bwd_prep(out, os, dout, ds, w.dout_b, w.delta, B, H, Sq, D,
+                                                 static_cast<hipStream_t>(stream)),
+                    "attn_bwd_prep");
+}
+
+cp_status_t cp_attn_block_bwd(const void* q, const int64_t* q_strides, const void* k, const void* v,
+                              const int64_t* kv_strides, int dtype, int B, int H, int D, int Sq, int Skv,
+                              float scale, unsigned flags, const float* lse, const void* workspace,
+                              size_t workspace_bytes, float* dq, const int64_t* dq_strides, float* dk, float* dv,
+                              const int64_t* dkv_strides, void* stream) {
+  const char* fn = "cp_attn_block_bwd";
+  if (flags & ~CP_BWD_ACCUMULATE_DQ) return fail(CP_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
+  cp_status_t st = check_bwd_common(fn, dtype, B, H, D, Sq, scale);
+  if (st != CP_OK) return st;
+  if (Skv < 0) return fail(CP_ERR_INVALID_ARG, "%s: K/V length must be non-negative (got %d)", fn, Skv);
+  if (B == 0 || H == 0 || (Sq == 0 && Skv == 0)) return CP_OK;
+  const Strides qs = resolve(q_strides, Sq, H, D);
+  const Strides kvs = resolve(kv_strides, Skv, H, D);
+  const Strides dqs = resolve(dq_strides, Sq, H, D);
+  const Strides dkvs = resolve(dkv_strides, Skv, H, D);
+  if ((st = check_bwd_tensors(fn, Sq, H, D, q, qs, kvs, lse, dq, dqs, dkvs)) != CP_OK) return st;
+  if ((st = check_kv(k, v, Skv)) != CP_OK) return st;
+  if (Skv > 0 && (!dk || !dv || !aligned(dk, 16) || !aligned(dv, 16)))
+    return fail(CP_ERR_INVALID_ARG, "%s: dk and dv must be non-null and 16-byte aligned", fn);
+  BwdWorkspace w{nullptr, nullptr};  // with no queries the kernels read no dO and no delta
+  if (Sq > 0 && (st = bwd_workspace(fn, const_cast<void*>(workspace), workspace_bytes, B, H, Sq, D, &w)) != CP_OK)
+    return st;
+  return run_block_bwd(q, qs, k, v, kvs, B, H, D, Sq, Skv, scale, (flags & CP_BWD_ACCUMULATE_DQ) != 0, lse, w,
+                       dq, dqs, dk, dv, dkvs, static_cast<hipStream_t>(stream));
+}
+
+cp_status_t cp_ring_attention_bwd(const void* q, const int64_t* q_strides, const void* const* k_blocks,
+                                  const void* const* v_blocks, const int64_t* kv_strides, const int* block_len,
+                                  int ring_degree, int dtype, int B, int H, int D, int Sq, float scale,
+                                  unsigned flags, const float* out, const int64_t* out_strides, const float* dout,
+                                  const int64_t* dout_strides, const float* lse, float* dq,
+                                  const int64_t* dq_strides, float* const* dk_blocks, float* const* dv_blocks,
+                                  const int64_t* dkv_strides, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  const char* fn = "cp_ring_attention_bwd";
+  if (flags & ~CP_RING_ANYTHING) return fail(CP_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
+  if (ring_degree < 1) return fail(CP_ERR_INVALID_ARG, "%s: ring_degree must be >= 1 (got %d)", fn, ring_degree);
+  if (!k_blocks || !v_blocks || !block_len || !dk_blocks || !dv_blocks)
+    return fail(CP_ERR_INVALID_ARG, "%s: block arrays must be non-null", fn);
+  const bool anything = (flags & CP_RING_ANYTHING) != 0;
+  int64_t total = 0;
+  for (int i = 0; i < ring_degree; ++i) {
+    if (block_len[i] < 0)
+      return fail(CP_ERR_INVALID_ARG, "%s: block %d has negative length %d", fn, i, block_len[i]);
+    if (!anything && block_len[i] != block_len[0])
+      return fail(CP_ERR_INVALID_ARG, "%s: block lengths differ (block 0: %d, block %d: %d); pass "
+                  "CP_RING_ANYTHING for uneven blocks", fn, block_len[0], i, block_len[i]);
+    total += block_len[i];
+  }
+  if (!anything && block_len[0] == 0) return fail(CP_ERR_INVALID_ARG, "%s: empty blocks need CP_RING_ANYTHING", fn);
+  cp_status_t st = check_bwd_common(fn, dtype, B, H, D, Sq, scale);
+  if (st != CP_OK) return st;
+  if (B == 0 || H == 0) return CP_OK;
+  const int tot = total > 0x7fffffff ? 0 : (int)total;
+  const Strides qs = resolve(q_strides, Sq, H, D);
+  const Strides kvs = resolve(kv_strides, tot, H, D);
+  const Strides dqs = resolve(dq_strides, Sq, H, D);
+  const Strides dkvs = resolve(dkv_strides, tot, H, D);
+  if ((st = check_bwd_tensors(fn, Sq, H, D, q, qs, kvs, lse, dq, dqs, dkvs)) != CP_OK) return st;
+  for (int i = 0; i < ring_degree; ++i) {
+    if ((st = check_kv(k_blocks[i], v_blocks[i], block_len[i])) != CP_OK)
+      return fail(st, "%s: block %d: %s", fn, i, g_err.c_str());
+    if (block_len[i] > 0 && (!dk_blocks[i] || !dv_blocks[i] || !aligned(dk_blocks[i], 16) ||
+                             !aligned(dv_blocks[i], 16)))
+      return fail(CP_ERR_INVALID_ARG, "%s: block %d: dk and dv must be non-null and 16-byte aligned", fn, i);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  BwdWorkspace w{nullptr, nullptr};
+  if (Sq > 0) {
+    if ((st = bwd_workspace(fn, workspace, workspace_bytes, B, H, Sq, D, &w)) != CP_OK) return st;
+    if (!out || !dout || !aligned(out, 16) || !aligned(dout, 16))
+      return fail(CP_ERR_INVALID_ARG, "%s: out and dout must be non-null and 16-byte aligned", fn);
+    const Strides os = resolve(out_strides, Sq, H, D);
+    const Strides ds = resolve(dout_strides, Sq, H, D);
+    if ((st = check_strides("out", os, 4, Sq, H, D)) != CP_OK) return st;
+    if ((st = check_strides("dout", ds, 4, Sq, H, D)) != CP_OK) return st;
+    if ((int64_t)B * Sq * H * (D / 8) > 0x7fffffff)
+      return fail(CP_ERR_UNSUPPORTED, "%s: B*Sq*H*D/8 must be below 2^31", fn);
+    if ((st = hip_status(cpattn::launch_attn_bwd_prep(out, os, dout, ds, w.dout_b, w.delta, B, H, Sq, D, s),
+                         "attn_bwd_prep")) != CP_OK)
+      return st;
+  }  // with no queries every dK, dV is zero (the dkv kernel still writes them) and no workspace is read
+  bool have_dq = false;
+  for (int i = 0; i < ring_degree; ++i) {
+    if (block_len[i] == 0) continue;
+    st = run_block_bwd(q, qs, k_blocks[i], v_blocks[i], kvs, B, H, D, Sq, block_len[i], scale, have_dq, lse, w, dq,
+                       dqs, dk_blocks[i], dv_blocks[i], dkvs, s);
+    if (st != CP_OK) return st;
+    have_dq = true;
+  }
+  if (!have_dq && Sq > 0)  // every block empty: dQ = 0 (the dq kernel over no keys writes zeros)
+    return run_block_bwd(q, qs, nullptr, nullptr, kvs, B, H, D, Sq, 0, scale, false, lse, w, dq, dqs, nullptr,
+                         nullptr, dkvs, s);
+  return CP_OK;
+}
+
 cp_status_t cp_ulysses_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
                                int D, int degree, int direction, void* stream) {
   if (elem_bytes != 2 && elem_bytes != 4)

@@ -47,6 +47,28 @@ struct FwdArgs {
   int waves;        // bf16 workgroup shape: 4, 8, or 0 to choose per launch
 };
 
+// Backward of one ring block (bf16 inputs): dQ (+)= scale dS K, dK = scale dS^T Q,
+// dV = P^T dO with P from the global LSE and dS = P (dO V^T - delta).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout_b;  // dO rounded to bf16, contiguous [B, Sq, H, D]
+  const float* lse;    // [B, H, Sq], natural log, full-ring
+  const float* delta;  // [B, H, Sq], rowsum(dO * O)
+  float* dq;
+  float* dk;
+  float* dv;
+  Strides qs, kvs, dqs, dkvs;
+  int B, H, D, Sq, Skv;
+  float scale;
+  bool accumulate_dq;
+};
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+// delta = rowsum(dO * O) and dO rounded to bf16 (contiguous [B, Sq, H, D]).
+hipError_t launch_attn_bwd_prep(const float* out, Strides os, const float* dout, Strides ds, void* dout_b,
+                                float* delta, int B, int H, int Sq, int D, hipStream_t stream);
+
 // Partial attention of Q against one K/V block (Skv >= 1), float32 out + LSE.
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);

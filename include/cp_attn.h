@@ -67,6 +67,9 @@ typedef enum cp_dtype { CP_F32 = 0, CP_BF16 = 1 } cp_dtype_t;
  * a separate cp_lse_merge pass, instead of merging inside the attention kernel. */
 #define CP_RING_SEPARATE_MERGE 0x4u
 
+/* cp_attn_block_bwd flag: add this block's dQ to dq instead of overwriting it. */
+#define CP_BWD_ACCUMULATE_DQ 0x1u
+
 /* cp_ulysses_regroup directions. */
 #define CP_REGROUP_SEQ_TO_HEAD 0 /* first all-to-all: [B, S_local, H, D] -> [B, P*S_local, H/P, D] */
 #define CP_REGROUP_HEAD_TO_SEQ 1 /* second all-to-all: [B, P*S_local, H/P, D] -> [B, S_local, H, D] */
@@ -183,6 +186,88 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides,
  */
 cp_status_t cp_ulysses_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
                                int D, int degree, int direction, void* stream);
+
+/*
+ * Backward of the ring share (bfloat16 Q/K/V, float32 gradients).
+ *
+ * [CP] the variants table that opens the page and the note under "Ring
+ * Anything Attention" restrict only Ring Anything to inference; [API] the
+ * introduction of "Paralelismo" names training as well as inference. So ring
+ * attention's blocks also run backward. With O and LSE the merged forward
+ * results over all blocks (cp_ring_attention's out and lse) and dO the loss
+ * gradient with respect to O, for every (b, h):
+ *   P_ij  = exp(scale <q_i, k_j> - lse_i)        (global softmax weights)
+ *   D_i   = sum_d dO_id O_id
+ *   dS_ij = P_ij (<dO_i, v_j> - D_i)
+ *   dV_j  = sum_i P_ij dO_i
+ *   dK_j  = scale sum_i dS_ij q_i
+ *   dQ_i  = scale sum_j dS_ij k_j                (sum over every block's keys)
+ * the derivative of softmax attention; per block, j runs over that block's
+ * keys. The MFMA operands dO and P, dS are rounded to bfloat16, D_i, the
+ * exponent and every accumulation are float32.
+ *
+ * Workspace (caller-owned, 256-byte aligned): dO rounded to bfloat16
+ * ([B, Sq, H, D], contiguous) and D ([B, H, Sq] float32), written by
+ * cp_attn_bwd_prep and read by cp_attn_block_bwd.
+ */
+
+/* Bytes of backward workspace for these sizes (0 if any size is <= 0). */
+size_t cp_attn_bwd_workspace_size(int B, int H, int Sq, int D);
+
+/*
+ * cp_attn_bwd_prep -- fill the workspace from O and dO (once per backward,
+ * before the blocks).
+ *   out, dout  [B, Sq, H, D] float32, strides out_strides / dout_strides
+ *   dtype      CP_BF16 (the dtype of the Q/K/V the blocks will use)
+ * B*Sq*H*D/8 must be below 2^31. B, H or Sq == 0 enqueues nothing.
+ */
+cp_status_t cp_attn_bwd_prep(const float* out, const int64_t* out_strides, const float* dout,
+                             const int64_t* dout_strides, int dtype, int B, int H, int Sq, int D,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * cp_attn_block_bwd -- gradients of one K/V block.
+ *   q      [B, Sq, H, D] bfloat16, strides q_strides
+ *   k, v   [B, Skv, H, D] bfloat16, shared strides kv_strides
+ *   lse    [B, H, Sq] float32: the merged LSE over all blocks (not this
+ *          block's own)
+ *   workspace  as filled by cp_attn_bwd_prep for the same B, H, Sq, D
+ *   dq     [B, Sq, H, D] float32, strides dq_strides: overwritten with this
+ *          block's dQ, or, with CP_BWD_ACCUMULATE_DQ, added to in place
+ *   dk, dv [B, Skv, H, D] float32, shared strides dkv_strides: overwritten
+ * The sequence strides of q and k/v, and H*D, must not exceed 2^24 elements.
+ * Skv == 0 writes dq = 0 (or leaves it with CP_BWD_ACCUMULATE_DQ); Sq == 0
+ * writes dk = dv = 0 and needs no workspace (it may be NULL); B or H == 0
+ * enqueues nothing. dtype CP_F32 is CP_ERR_UNSUPPORTED.
+ */
+cp_status_t cp_attn_block_bwd(const void* q, const int64_t* q_strides, const void* k, const void* v,
+                              const int64_t* kv_strides, int dtype, int B, int H, int D, int Sq, int Skv,
+                              float scale, unsigned flags, const float* lse, const void* workspace,
+                              size_t workspace_bytes, float* dq, const int64_t* dq_strides, float* dk, float* dv,
+                              const int64_t* dkv_strides, void* stream);
+
+/*
+ * cp_ring_attention_bwd -- backward of cp_ring_attention for one rank: the
+ * prep, then every block in ring order; dQ is summed over the blocks.
+ *   q, k_blocks, v_blocks, kv_strides, block_len, ring_degree, dtype, B, H,
+ *   D, Sq, scale, flags (0 or CP_RING_ANYTHING)  as cp_ring_attention
+ *   out, lse   the forward's merged output and LSE
+ *   dout       [B, Sq, H, D] float32, strides dout_strides
+ *   dq         [B, Sq, H, D] float32, overwritten
+ *   dk_blocks, dv_blocks  ring_degree pointers to [B, block_len[i], H, D]
+ *              float32 outputs (shared strides dkv_strides), overwritten;
+ *              entries of empty blocks are not used
+ *   workspace  cp_attn_bwd_workspace_size(B, H, Sq, D) bytes
+ * If every block is empty, dq = 0.
+ */
+cp_status_t cp_ring_attention_bwd(const void* q, const int64_t* q_strides, const void* const* k_blocks,
+                                  const void* const* v_blocks, const int64_t* kv_strides, const int* block_len,
+                                  int ring_degree, int dtype, int B, int H, int D, int Sq, float scale,
+                                  unsigned flags, const float* out, const int64_t* out_strides, const float* dout,
+                                  const int64_t* dout_strides, const float* lse, float* dq,
+                                  const int64_t* dq_strides, float* const* dk_blocks, float* const* dv_blocks,
+                                  const int64_t* dkv_strides, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* Workgroup shape of the bfloat16 block kernel, a process-wide tuning knob
  * (no source passage; a property of this implementation). 0 = chosen per

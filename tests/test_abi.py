@@ -26,7 +26,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
     assert {"cp_attn_block_fwd", "cp_lse_merge", "cp_ring_attention", "cp_ring_attention_workspace_size",
-            "cp_ulysses_regroup", "cp_last_error", "cp_abi_version"} <= set(names)
+            "cp_ulysses_regroup", "cp_last_error", "cp_abi_version", "cp_attn_bwd_workspace_size",
+            "cp_attn_bwd_prep", "cp_attn_block_bwd", "cp_ring_attention_bwd"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert lib.cp_abi_version() == 1
@@ -132,6 +133,79 @@ def test_regroup_rejects(lib):
     assert f(FAKE, FAKE + 64, 2, 1, 16, 24, 128, 2, 0, None) == _lib.CP_ERR_INVALID_ARG  # overlap
     assert "overlap" in _err(lib)
     assert f(0, 0, 2, 0, 16, 24, 128, 2, 0, None) == _lib.CP_OK
+
+
+BWD_NEED = 4096 + 256  # bf16 dO [1, 8, 2, 128] and D [1, 2, 8] float32, each padded to 256 bytes
+
+
+def _block_bwd(lib, dtype=1, B=1, H=2, D=128, Sq=8, Skv=8, scale=0.1, flags=0, q=FAKE, k=FAKE, v=FAKE,
+               lse=FAKE, ws=FAKE, ws_bytes=BWD_NEED, dq=FAKE, dk=FAKE, dv=FAKE, qs=None, kvs=None):
+    return lib.cp_attn_block_bwd(q, qs, k, v, kvs, dtype, B, H, D, Sq, Skv, scale, flags, lse, ws, ws_bytes,
+                                 dq, None, dk, dv, None, None)
+
+
+def test_bwd_workspace_size(lib):
+    assert lib.cp_attn_bwd_workspace_size(1, 2, 8, 128) == BWD_NEED
+    assert lib.cp_attn_bwd_workspace_size(1, 24, 4608, 128) == 1 * 4608 * 24 * 128 * 2 + 24 * 4608 * 4
+    assert lib.cp_attn_bwd_workspace_size(1, 2, 0, 128) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=0), _lib.CP_ERR_UNSUPPORTED, "CP_BF16"),
+    (dict(D=96), _lib.CP_ERR_UNSUPPORTED, "D=96"),
+    (dict(flags=0x2), _lib.CP_ERR_INVALID_ARG, "flags"),
+    (dict(scale=-1.0), _lib.CP_ERR_INVALID_ARG, "scale"),
+    (dict(Skv=-1), _lib.CP_ERR_INVALID_ARG, "non-negative"),
+    (dict(q=0), _lib.CP_ERR_INVALID_ARG, "non-null"),
+    (dict(dq=0), _lib.CP_ERR_INVALID_ARG, "non-null"),
+    (dict(lse=0), _lib.CP_ERR_INVALID_ARG, "non-null"),
+    (dict(k=0), _lib.CP_ERR_INVALID_ARG, "non-null"),
+    (dict(dv=0), _lib.CP_ERR_INVALID_ARG, "dk and dv"),
+    (dict(dk=FAKE + 8), _lib.CP_ERR_INVALID_ARG, "aligned"),
+    (dict(ws=0), _lib.CP_ERR_WORKSPACE, "workspace"),
+    (dict(ws_bytes=BWD_NEED - 1), _lib.CP_ERR_WORKSPACE, "workspace"),
+    (dict(ws=FAKE + 16), _lib.CP_ERR_UNSUPPORTED, "256-byte"),
+    (dict(qs=(ctypes.c_int64 * 3)(1 << 30, (1 << 24) + 8, 128)), _lib.CP_ERR_UNSUPPORTED, "2^24"),
+])
+def test_block_bwd_rejects(lib, kw, status, needle):
+    assert _block_bwd(lib, **kw) == status
+    assert needle in _err(lib)
+
+
+def test_block_bwd_empty_is_a_no_op(lib):
+    assert _block_bwd(lib, B=0, q=0, k=0, v=0, lse=0, ws=0, dq=0, dk=0, dv=0) == _lib.CP_OK
+    assert _block_bwd(lib, Sq=0, Skv=0, q=0, k=0, v=0, lse=0, ws=0, dq=0, dk=0, dv=0) == _lib.CP_OK
+
+
+def test_bwd_prep_rejects(lib):
+    f = lib.cp_attn_bwd_prep
+    assert f(FAKE, None, FAKE, None, 0, 1, 2, 8, 128, FAKE, BWD_NEED, None) == _lib.CP_ERR_UNSUPPORTED
+    assert f(0, None, FAKE, None, 1, 1, 2, 8, 128, FAKE, BWD_NEED, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(FAKE, None, FAKE + 4, None, 1, 1, 2, 8, 128, FAKE, BWD_NEED, None) == _lib.CP_ERR_UNSUPPORTED
+    assert f(FAKE, None, FAKE, None, 1, 1, 2, 8, 128, FAKE, BWD_NEED - 256, None) == _lib.CP_ERR_WORKSPACE
+    assert f(0, None, 0, None, 1, 1, 2, 0, 128, 0, 0, None) == _lib.CP_OK
+
+
+def _ring_bwd(lib, lens, flags=0, dtype=1, ws=FAKE, ws_bytes=BWD_NEED, dkptrs=None, out=FAKE):
+    P = len(lens)
+    arr = lambda xs: (ctypes.c_void_p * P)(*xs)  # noqa: E731
+    L = (ctypes.c_int * P)(*lens)
+    return lib.cp_ring_attention_bwd(FAKE, None, arr([FAKE] * P), arr([FAKE] * P), None, L, P, dtype, 1, 2, 128, 8,
+                                     0.1, flags, out, None, FAKE, None, FAKE, FAKE, None,
+                                     arr(dkptrs or [FAKE] * P), arr([FAKE] * P), None, ws, ws_bytes, None)
+
+
+def test_ring_bwd_rejects(lib):
+    assert _ring_bwd(lib, [8, 7]) == _lib.CP_ERR_INVALID_ARG
+    assert "CP_RING_ANYTHING" in _err(lib)
+    assert _ring_bwd(lib, []) == _lib.CP_ERR_INVALID_ARG
+    assert _ring_bwd(lib, [8, 8], flags=_lib.CP_RING_SEPARATE_MERGE) == _lib.CP_ERR_INVALID_ARG
+    assert _ring_bwd(lib, [8, 8], dtype=0) == _lib.CP_ERR_UNSUPPORTED
+    assert _ring_bwd(lib, [8, 8], dkptrs=[FAKE, 0]) == _lib.CP_ERR_INVALID_ARG
+    assert "block 1" in _err(lib)
+    assert _ring_bwd(lib, [8, 8], ws_bytes=16) == _lib.CP_ERR_WORKSPACE
+    assert _ring_bwd(lib, [8, 8], out=0) == _lib.CP_ERR_INVALID_ARG
+    assert "out and dout" in _err(lib)
 
 
 def test_set_fwd_waves(lib):

@@ -14,7 +14,9 @@ side sees them, so the oracle and the GPU consume bit-identical values.
 
 Seeds: ``numpy.random.default_rng(42 + index)``; 42 is the seed the pages'
 example script gives its generator. Draw order: Q_local, then K, then V, each
-``standard_normal(shape, dtype=float32)``. Q_local is drawn directly at its
+``standard_normal(shape, dtype=float32)``. The backward's output gradient dO
+is drawn by ``grad_out`` from its own generator (seed + 1000), float32 N(0, 1)
+and not rounded (the loss gradient arrives in float32). Q_local is drawn directly at its
 local shape ``[B, Sq, H, D]`` (one rank's slice); K and V are drawn at
 ``[B, sum(block_lens), H, D]`` and ring block i is the contiguous token range
 ``[off_i, off_i + L_i)``.
@@ -218,6 +220,11 @@ def make_custom(B: int, H: int, D: int, Sq: int, block_lens: Sequence[int], dtyp
     if dtype == "bf16":
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     return Inputs(q=q, k=k, v=v, workload=w)
+
+
+def grad_out(shape, seed: int) -> np.ndarray:
+    """dL/dO for the backward: float32 N(0, 1) of ``shape`` from ``default_rng(seed + 1000)``."""
+    return np.random.default_rng(seed + 1000).standard_normal(tuple(shape), dtype=np.float32)
 
 
 def sample_rows(n_rows: int, n_samples: int, seed: int, must: Optional[Sequence[int]] = None) -> np.ndarray:
