@@ -12,7 +12,8 @@ Prints ONE JSON line on stdout. ``value`` is attention TFLOP/s over the whole
 step, counting 4*B*H*Sq*Skv*D flops; ``roofline`` prices the dominant kernel
 (block attention) from its per-launch duration measured with HIP events on
 the launch stream; ``cpu_baseline`` times the float64 CPU oracle on a bounded
-sample of the same workload on this host.
+sample of the same workload on this host. ``backward`` times the ring
+share's backward (bf16 workloads) on the same inputs, outside the step.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -138,6 +139,41 @@ class Problem:
         torch.cuda.synchronize()
         flops = sum(4 * w.B * w.attn_H * w.Sq * kb.shape[1] * w.D for _, kb, _ in blocks) / len(blocks)
         return e0.elapsed_time(e1) / (reps * len(blocks)), flops
+
+
+    def time_backward(self, reps: int):
+        """The ring share's backward (cp_ring_attention_bwd: prep, then the dq and dkv kernels per
+        block) on this step's Q/K/V, its merged out/LSE and a seeded dO: mean time of `reps` passes
+        run back to back between two HIP events, and the algorithmic flops of one pass,
+        10*B*H*Sq*Skv*D (the products S = QK^T, dP = dO V^T, dV, dK and dQ)."""
+        torch, cp, w = self.torch, self.cp, self.w
+        B, H, D, Sq = w.B, w.attn_H, w.D, w.Sq
+        self.step()  # out, lse of the forward
+        do = torch.from_numpy(workloads.grad_out((B, Sq, H, D), w.seed)).cuda()
+        lens = [kb.shape[1] for kb in self.kb]
+        dq = torch.empty((B, Sq, H, D), dtype=torch.float32, device="cuda")
+        dk_all = torch.empty((B, sum(lens), H, D), dtype=torch.float32, device="cuda")
+        dv_all = torch.empty_like(dk_all)
+        offs = workloads.block_offsets(lens)
+        dk = [dk_all[:, a:a + L] for a, L in zip(offs, lens)]
+        dv = [dv_all[:, a:a + L] for a, L in zip(offs, lens)]
+        ws = torch.empty(cp.cp_attn_bwd_workspace_size(B, H, Sq, D), dtype=torch.uint8, device="cuda")
+        flags = cp.CP_RING_ANYTHING if (len(set(lens)) > 1 or 0 in lens) else 0
+
+        def one_pass():
+            cp.cp_ring_attention_bwd(self.q_att, self.kb, self.vb, self.out, self.lse, do, dq, dk, dv,
+                                     scale=w.scale, flags=flags, workspace=ws)
+
+        stream = torch.cuda.current_stream()
+        one_pass()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            one_pass()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps, 10 * B * H * Sq * sum(lens) * D
 
 
 def time_hbm_kernels(reps: int = 5):
@@ -288,13 +324,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
-    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step)")
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us/step)")
     tflops = w.flops / (ms_step * 1e-3) / 1e12
 
     k_ms, k_flops = prob.time_block_kernels(max(5, min(args.steps, 50)))
     achieved = k_flops / (k_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     log(f"[bench] block kernel: {k_ms * 1e3:.1f} us/launch, {achieved:.1f} TFLOP/s ({achieved / peak:.1%} of {peak})")
+
+    bwd = None
+    if w.dtype == "bf16":
+        b_ms, b_flops = prob.time_backward(max(5, min(args.steps, 20)))
+        b_tf = b_flops / (b_ms * 1e-3) / 1e12
+        bwd = {"TFLOP/s": round(b_tf, 2), "frac": round(b_tf / PEAK_TFLOPS["bf16"], 4),
+               "ms_per_pass": round(b_ms, 5), "flops_per_pass": b_flops,
+               "counting": "10*B*H*Sq*Skv*D (S, dP, dV, dK, dQ products)",
+               "kernels": "attn_bwd_prep_kernel, attn_bwd_dq_kernel, attn_bwd_dkv_kernel"}
+        log(f"[bench] backward: {b_ms * 1e3:.1f} us/pass, {b_tf:.1f} TFLOP/s ({b_tf / PEAK_TFLOPS['bf16']:.1%} of bf16 peak)")
 
     hbm = time_hbm_kernels()
     for name, r in hbm.items():
@@ -330,6 +376,7 @@ def main():
                      "us_per_launch": round(k_ms * 1e3, 2)},
         "cpu_baseline": cpu,
         "hbm_kernels": hbm,
+        "backward": bwd,
     }
     print(json.dumps(rec), flush=True)
     return 0

@@ -41,6 +41,10 @@
 
 #include "kernels.h"
 
+#ifndef CP_BWD_DKV_WPE
+#define CP_BWD_DKV_WPE 2  // waves per SIMD the dkv kernel's register budget must allow (1 or 2)
+#endif
+
 namespace cpattn {
 namespace {
 
@@ -308,7 +312,7 @@ attn_bwd_dq_kernel(BwdParams p) {
 // --------------------------------------------------------------- dKV kernel
 
 template <int D>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(CP_BWD_DKV_WPE)))
 attn_bwd_dkv_kernel(BwdParams p) {
   using T = TileCfg<D>;
   __shared__ __attribute__((aligned(1024))) char qf0[T::BYTES];
@@ -379,16 +383,15 @@ attn_bwd_dkv_kernel(BwdParams p) {
   }
 
   auto step = [&](const char* qf, const char* df, const char* qr, const char* dr, const char* st) {
+    // S and dP interleaved: each fragment read is consumed at once, which
+    // keeps the register count within two waves per SIMD.
     f32x16 s = f32x16{}, dpm = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < T::KK; ++kk) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(qf + kk * 1024 + lane * 16);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kt_[kk], s, 0, 0, 0);
-    }
-#pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(df + kk * 1024 + lane * 16);
-      dpm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vt_[kk], dpm, 0, 0, 0);
+      const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(df + kk * 1024 + lane * 16);
+      dpm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, vt_[kk], dpm, 0, 0, 0);
     }
     // Register r holds query 8*(r/4) + 4*hi + r%4 of the tile; its LSE and D
     // are 4 consecutive floats per group of 4 registers.
