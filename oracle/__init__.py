@@ -32,7 +32,8 @@ Pins: every function here is checked by the CPU tests against something other
 than itself -- a pure-Python brute force, closed forms, a library attention
 routine, hand-computed golden values under ``tests/golden/`` and invariants
 (ring over any split == single pass, shift/permutation invariance, regroup
-round trip, multi-rank Ulysses and Unified simulations); the backward against
+round trip, multi-rank Ulysses, Ulysses Anything and Unified simulations); the
+uneven packs against a hand-written golden map and pure-Python loops; the backward against
 central differences of the forward, a library autograd and its invariants.
 No function is "parity unpinned".
 """
@@ -51,6 +52,11 @@ __all__ = [
     "ulysses_regroup",
     "ulysses_regroup_inv",
     "usp_attention",
+    "ulysses_pack_heads",
+    "ulysses_unpack_heads",
+    "ulysses_concat_seq",
+    "ulysses_split_seq",
+    "ulysses_anything_attention",
     "attention_bwd",
     "ring_attention_bwd",
     "brute_attention",
@@ -217,6 +223,107 @@ def usp_attention(q: np.ndarray, k_shards: Sequence[np.ndarray], v_shards: Seque
     vb = [ulysses_regroup(v, degree) for v in v_shards]
     o_h, lse = ring_attention(q_h, kb, vb, scale)
     return ulysses_regroup_inv(o_h, degree), lse
+
+
+def ulysses_pack_heads(x: np.ndarray, head_counts: Sequence[int]) -> np.ndarray:
+    """Ulysses Anything: one rank's all-to-all buffer ordered by head group.
+
+    "Paralelismo de contexto", "Ulysses Anything Attention" (and the API's
+    ``ulysses_anything``): the sequence length and the head count need not
+    divide by the degree. x is the rank's [B, S_r, H, D]; head group g is the
+    next head_counts[g] heads (sum = H, contiguous, in order) and goes to rank
+    g. The first all-to-all sends piece g = x[:, :, heads of g, :] (shape
+    [B, S_r, H_g, D], row-major) to rank g; the pieces lie back to back in the
+    returned 1-D buffer. A pure permutation.
+    """
+    B, S_r, H, D = x.shape
+    assert sum(head_counts) == H and all(c >= 0 for c in head_counts)
+    pieces = []
+    h0 = 0
+    for c in head_counts:
+        pieces.append(np.ascontiguousarray(x[:, :, h0:h0 + c, :]).reshape(-1))
+        h0 += c
+    return np.concatenate(pieces) if pieces else np.zeros(0, dtype=x.dtype)
+
+
+def ulysses_unpack_heads(buf: np.ndarray, B: int, S_r: int, head_counts: Sequence[int], D: int) -> np.ndarray:
+    """Inverse of ``ulysses_pack_heads``: after the second all-to-all a rank
+    holds, from each rank g, its S_r tokens for head group g back to back;
+    they are placed at heads g's offset of a [B, S_r, H, D] tensor."""
+    H = sum(head_counts)
+    out = np.zeros((B, S_r, H, D), dtype=buf.dtype)
+    pos = h0 = 0
+    for c in head_counts:
+        n = B * S_r * c * D
+        out[:, :, h0:h0 + c, :] = buf[pos:pos + n].reshape(B, S_r, c, D)
+        pos += n
+        h0 += c
+    assert pos == buf.size
+    return out
+
+
+def ulysses_concat_seq(buf: np.ndarray, B: int, seq_counts: Sequence[int], H_g: int, D: int) -> np.ndarray:
+    """The receiving side of the first all-to-all: from each rank r a piece
+    [B, S_r, H_g, D] (back to back, rank order) becomes the token range of rank
+    r in [B, sum S_r, H_g, D] (every token of this rank's heads)."""
+    parts = []
+    pos = 0
+    for c in seq_counts:
+        n = B * c * H_g * D
+        parts.append(buf[pos:pos + n].reshape(B, c, H_g, D))
+        pos += n
+    assert pos == buf.size
+    return np.concatenate(parts, axis=1)
+
+
+def ulysses_split_seq(y: np.ndarray, seq_counts: Sequence[int]) -> np.ndarray:
+    """Inverse of ``ulysses_concat_seq``: the sending side of the second
+    all-to-all, token range of rank r as piece r ([B, S_r, H_g, D]), back to back."""
+    assert sum(seq_counts) == y.shape[1]
+    pieces = []
+    s0 = 0
+    for c in seq_counts:
+        pieces.append(np.ascontiguousarray(y[:, s0:s0 + c]).reshape(-1))
+        s0 += c
+    return np.concatenate(pieces) if pieces else np.zeros(0, dtype=y.dtype)
+
+
+def ulysses_anything_attention(q_shards: Sequence[np.ndarray], k_shards: Sequence[np.ndarray],
+                               v_shards: Sequence[np.ndarray], head_counts: Sequence[int],
+                               scale: float) -> List[np.ndarray]:
+    """Every rank of an uneven Ulysses group, with both all-to-alls simulated.
+
+    Rank r holds the [B, S_r, H, D] shards of Q, K and V (S_r arbitrary); rank
+    g ends up with every token of head group g (head_counts[g] heads), attends
+    over the whole sequence, and the second all-to-all returns each rank its
+    own tokens with every head. Returns each rank's output [B, S_r, H, D]; the
+    concatenation over ranks is full attention on the whole sequence.
+    """
+    P = len(q_shards)
+    assert len(head_counts) == P
+    B, _, H, D = q_shards[0].shape
+    seq_counts = [x.shape[1] for x in q_shards]
+
+    def exchange(send_bufs, piece_sizes):
+        # piece_sizes[r][g]: elements rank r sends to rank g; rank g receives in rank order
+        recv = []
+        for g in range(P):
+            parts = []
+            for r in range(P):
+                off = sum(piece_sizes[r][:g])
+                parts.append(send_bufs[r][off:off + piece_sizes[r][g]])
+            recv.append(np.concatenate(parts))
+        return recv
+
+    sizes1 = [[B * seq_counts[r] * head_counts[g] * D for g in range(P)] for r in range(P)]
+    heads_view = []
+    for shards in (q_shards, k_shards, v_shards):
+        recv = exchange([ulysses_pack_heads(x, head_counts) for x in shards], sizes1)
+        heads_view.append([ulysses_concat_seq(recv[g], B, seq_counts, head_counts[g], D) for g in range(P)])
+    outs = [attention(heads_view[0][g], heads_view[1][g], heads_view[2][g], scale)[0] for g in range(P)]
+    sizes2 = [[B * seq_counts[r] * head_counts[g] * D for r in range(P)] for g in range(P)]
+    recv = exchange([ulysses_split_seq(outs[g], seq_counts) for g in range(P)], sizes2)
+    return [ulysses_unpack_heads(recv[r], B, seq_counts[r], head_counts, D) for r in range(P)]
 
 
 def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, o: np.ndarray, lse: np.ndarray,

@@ -302,6 +302,82 @@ def test_merge_weights_follow_lse_not_position():
     np.testing.assert_allclose(ml, np.log(1 + np.exp(lse_b)), atol=1e-15)
 
 
+# ------------------------------------------------------- Ulysses Anything ---
+
+@pytest.mark.parametrize("case", _golden()["ulysses_anything"], ids=lambda c: c["name"])
+def test_golden_ulysses_anything(case):
+    if case["op"] == "pack_heads":
+        x = np.array(case["in"], dtype=np.float64)
+        buf = oracle.ulysses_pack_heads(x, case["counts"])
+        assert buf.tolist() == case["expected_buf"]
+        B, S_r, _, D = x.shape
+        assert np.array_equal(oracle.ulysses_unpack_heads(buf, B, S_r, case["counts"], D), x)
+    else:
+        buf = np.array(case["buf"], dtype=np.float64)
+        y = oracle.ulysses_concat_seq(buf, case["B"], case["counts"], case["H_g"], case["D"])
+        assert y.tolist() == case["expected_out"]
+        assert np.array_equal(oracle.ulysses_split_seq(y, case["counts"]), buf)
+
+
+@pytest.mark.parametrize("B,S_r,counts,D", [(1, 3, (2, 1, 2), 2), (2, 2, (0, 3, 1), 3), (3, 1, (1,), 2)])
+def test_pack_heads_matches_index_loops(B, S_r, counts, D):
+    """Pure-Python loops over every element: piece g holds (b, s, head h0_g + j, d) at
+    offset B*S_r*D*h0_g + ((b*S_r + s)*H_g + j)*D + d."""
+    H = sum(counts)
+    x = np.arange(B * S_r * H * D, dtype=np.float64).reshape(B, S_r, H, D)
+    buf = oracle.ulysses_pack_heads(x, counts)
+    want = [None] * x.size
+    h0 = 0
+    for Hg in counts:
+        for b in range(B):
+            for s in range(S_r):
+                for j in range(Hg):
+                    for d in range(D):
+                        want[B * S_r * D * h0 + ((b * S_r + s) * Hg + j) * D + d] = float(x[b, s, h0 + j, d])
+        h0 += Hg
+    assert buf.tolist() == want
+
+
+@pytest.mark.parametrize("B,counts,Hg,D", [(1, (3, 2, 2), 2, 2), (2, (1, 0, 3), 1, 3)])
+def test_concat_seq_matches_index_loops(B, counts, Hg, D):
+    n = B * sum(counts) * Hg * D
+    buf = np.arange(n, dtype=np.float64)
+    y = oracle.ulysses_concat_seq(buf, B, counts, Hg, D)
+    pos = s0 = 0
+    for c in counts:
+        for b in range(B):
+            for s in range(c):
+                for h in range(Hg):
+                    for d in range(D):
+                        assert y[b, s0 + s, h, d] == buf[pos]
+                        pos += 1
+        s0 += c
+    assert pos == n
+
+
+def test_pack_even_split_is_the_regroup():
+    """Equal head groups, one batch: the pieces back to back are the even regroup's tokens chunks."""
+    x = _rand((1, 5, 6, 4), 120)
+    buf = oracle.ulysses_pack_heads(x, (2, 2, 2))
+    np.testing.assert_array_equal(buf.reshape(15, 2, 4), oracle.ulysses_regroup(x, 3)[0])
+    np.testing.assert_array_equal(oracle.ulysses_pack_heads(x, (6,)), x.reshape(-1))
+
+
+@pytest.mark.parametrize("seq,heads,B", [((5, 4, 4), (2, 2, 1), 2), ((3, 3, 3, 2), (2, 1, 1, 2), 1),
+                                          ((7, 0), (1, 3), 1)])
+def test_ulysses_anything_simulation_is_full_attention(seq, heads, B):
+    """All ranks of an uneven Ulysses group, both exchanges simulated: rank outputs concatenated
+    over the sequence equal full attention."""
+    H, D = sum(heads), 4
+    S = sum(seq)
+    q, k, v = (_rand((B, S, H, D), sd) for sd in (121, 122, 123))
+    offs = np.cumsum((0,) + seq)
+    shard = lambda x: [x[:, offs[r]:offs[r + 1]] for r in range(len(seq))]  # noqa: E731
+    outs = oracle.ulysses_anything_attention(shard(q), shard(k), shard(v), heads, 0.4)
+    want, _ = oracle.attention(q, k, v, 0.4)
+    np.testing.assert_allclose(np.concatenate(outs, axis=1), want, atol=1e-12)
+
+
 # ------------------------------------------------------------- the regroup ---
 
 @pytest.mark.parametrize("B,S_l,H,D,P", [(1, 5, 4, 3, 2), (2, 3, 6, 2, 3), (1, 4, 8, 1, 4), (2, 2, 3, 2, 1)])
