@@ -4,9 +4,10 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: for a ring workload, attention of the local Q
 against every K/V block with each float32 partial merged by LSE rescaling
-(cp_ring_attention); for the Ulysses workload, the head/token regroup of Q, K
-and V, attention over all tokens for the local heads, and the inverse regroup
-of the output.
+(cp_ring_attention); for the Ulysses workloads, the head/token regroup of Q,
+K and V, attention over all tokens for the local heads, and the inverse
+regroup of the output (Ulysses Anything: the uneven head-group packs around
+the two exchanges, which are outside the step).
 
 Prints ONE JSON line on stdout. ``value`` is attention TFLOP/s over the whole
 step, counting 4*B*H*Sq*Skv*D flops; ``roofline`` prices the dominant kernel
@@ -71,7 +72,9 @@ class Problem:
         self.flags = cp.CP_RING_SEPARATE_MERGE if separate_merge else 0
         if len(set(w.block_lens)) > 1:
             self.flags |= cp.CP_RING_ANYTHING
-        if w.ulysses_degree > 1:
+        if w.anything:
+            self._setup_anything(tdt)
+        elif w.ulysses_degree > 1:
             # This rank regroups its own Q/K/V shard every step; the other ring
             # ranks' blocks arrive already regrouped (they are regrouped once,
             # here, as the peers would have done).
@@ -100,8 +103,55 @@ class Problem:
         nbytes = cp.cp_ring_attention_workspace_size(B, H, w.Sq, D, self.flags)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
 
+    def _setup_anything(self, tdt):
+        """Ulysses Anything, rank 0 of the group. The step packs this rank's Q/K/V shards by head
+        group (the first exchange's send buffers), attends over every token of its head group and
+        unpacks the output pieces of the second exchange into [B, S_0, H, D]. The exchanges are
+        outside the step: their receive buffers are filled here, once, with what every rank (this
+        one included) sends; with B = 1 a receive buffer is already the [B, S, H_0, D] tensor and
+        the send buffer of the second exchange is the output itself, so concat_seq is not needed."""
+        torch, cp, w = self.torch, self.cp, self.w
+        B, H, D, P = w.B, w.H, w.D, w.ulysses_degree
+        assert B == 1
+        seq, heads = w.seq_counts, w.head_counts
+        offs = workloads.block_offsets(seq)
+        self.seq, self.heads = seq, heads
+        S0, H0 = seq[0], heads[0]
+        own = [x[:, :S0].contiguous() for x in (self.q, self.k, self.v)]
+        self.own = own
+        self.send = [torch.empty(x.numel(), dtype=tdt, device="cuda") for x in own]
+        recv = []
+        for x in (self.q, self.k, self.v):  # piece 0 of every rank r, back to back
+            pieces = []
+            for r in range(P):
+                buf = torch.empty(B * seq[r] * H * D, dtype=tdt, device="cuda")
+                cp.cp_ulysses_pack_heads(x[:, offs[r]:offs[r] + seq[r]].contiguous(), buf, heads)
+                pieces.append(buf[:B * seq[r] * H0 * D])
+            recv.append(torch.cat(pieces).view(B, w.Sq, H0, D))
+        self.q_att, kfull, vfull = recv
+        self.kb, self.vb = [kfull], [vfull]
+        # second exchange: from each rank g, rank 0's tokens of head group g (the peers' outputs,
+        # computed once here with the library itself)
+        hoffs = workloads.block_offsets(heads)
+        pieces2 = []
+        for g in range(P):
+            cols = slice(hoffs[g], hoffs[g] + heads[g])
+            q_g = self.q[:, :, cols].contiguous()
+            o_g, _ = cp.ring_attention(q_g, [self.k[:, :, cols].contiguous()], [self.v[:, :, cols].contiguous()],
+                                       scale=w.scale)
+            pieces2.append(o_g[:, :S0].contiguous().view(-1))
+        self.recv2 = torch.cat(pieces2)
+        self.back = torch.empty((B, S0, H, D), dtype=torch.float32, device="cuda")
+
     def step(self):
         cp, w = self.cp, self.w
+        if w.anything:
+            for x, buf in zip(self.own, self.send):
+                cp.cp_ulysses_pack_heads(x, buf, self.heads, cp.CP_REGROUP_SEQ_TO_HEAD)
+            cp.cp_ring_attention(self.q_att, self.kb, self.vb, self.out, self.lse, scale=w.scale,
+                                 flags=self.flags, workspace=self.ws)
+            cp.cp_ulysses_pack_heads(self.recv2, self.back, self.heads, cp.CP_REGROUP_HEAD_TO_SEQ)
+            return
         if w.ulysses_degree > 1:
             P = w.ulysses_degree
             cp.cp_ulysses_regroup(self.q, self.qr, P, cp.CP_REGROUP_SEQ_TO_HEAD)
@@ -240,7 +290,11 @@ def cpu_baseline(w: workloads.Workload, inp, target_s: float):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001 - threadpoolctl is optional
         cores = 1
-    if w.ulysses_degree > 1:
+    if w.anything:  # rank 0's head group over every token
+        H0 = w.head_counts[0]
+        q = inp.q[:, :, :H0]
+        k_blocks, v_blocks = [inp.k[:, :, :H0]], [inp.v[:, :, :H0]]
+    elif w.ulysses_degree > 1:
         P = w.ulysses_degree
         q = oracle.ulysses_regroup(inp.q, P)
         k_blocks = [oracle.ulysses_regroup(inp.k_shard(r), P) for r in range(w.ring_degree)]
@@ -368,6 +422,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.attn_H, "D": w.D, "Sq": w.Sq,
                    "block_lens": list(w.block_lens), "ring_degree": w.ring_degree,
                    "ulysses_degree": w.ulysses_degree,
+                   **({"seq_counts": w.seq_counts, "head_counts": w.head_counts} if w.anything else {}),
                    "merge": "separate" if args.separate_merge else "fused",
                    "pct_of_bf16_peak": round(100 * tflops / PEAK_TFLOPS["bf16"], 2)},
         "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),

@@ -25,6 +25,7 @@ __all__ = [
     "CpAttnError", "load", "cp_abi_version", "cp_last_error", "cp_attn_set_fwd_waves", "cp_attn_block_fwd",
     "cp_lse_merge",
     "cp_ring_attention", "cp_ring_attention_workspace_size", "cp_ulysses_regroup",
+    "cp_ulysses_pack_heads", "cp_ulysses_concat_seq", "split_counts",
     "cp_attn_bwd_workspace_size", "cp_attn_bwd_prep", "cp_attn_block_bwd", "cp_ring_attention_bwd",
     "ring_attention", "ring_attention_bwd",
 ]
@@ -239,6 +240,66 @@ def cp_ulysses_regroup(inp, out, degree: int, direction: int = CP_REGROUP_SEQ_TO
     st = lib.cp_ulysses_regroup(inp.data_ptr(), out.data_ptr(), inp.element_size(), B, S_l, H, D, degree,
                                 direction, _stream(stream))
     _check(st, "cp_ulysses_regroup")
+
+
+def split_counts(n: int, parts: int):
+    """Uneven split sizes: the first n % parts parts get one more (e.g. 4481 over 4: 1121, 1120, 1120, 1120)."""
+    if parts < 1 or n < 0:
+        raise ValueError("need n >= 0 and parts >= 1")
+    return [n // parts + (1 if i < n % parts else 0) for i in range(parts)]
+
+
+def _counts(name, counts):
+    counts = [int(c) for c in counts]
+    if not counts or any(c < 0 for c in counts):
+        raise ValueError(f"{name} must be a non-empty list of non-negative counts")
+    return (ctypes.c_int * len(counts))(*counts), counts
+
+
+def cp_ulysses_pack_heads(inp, out, head_counts: Sequence[int], direction: int = CP_REGROUP_SEQ_TO_HEAD,
+                          stream=None):
+    """Ulysses Anything: [B, S_r, H, D] <-> pieces [B, S_r, H_g, D] back to back (1-D ``out`` or ``inp``).
+
+    SEQ_TO_HEAD: ``inp`` is the contiguous tensor, ``out`` a flat buffer of the same size;
+    HEAD_TO_SEQ: the reverse. See cp_ulysses_pack_heads in the header.
+    """
+    lib = _lib.load()
+    dev = _gpu("inp", inp).device
+    _gpu("out", out, dev)
+    arr, counts = _counts("head_counts", head_counts)
+    tensor = inp if direction == CP_REGROUP_SEQ_TO_HEAD else out
+    pieces = out if direction == CP_REGROUP_SEQ_TO_HEAD else inp
+    if inp.dtype != out.dtype or not (inp.is_contiguous() and out.is_contiguous()) or tensor.dim() != 4:
+        raise ValueError("tensors must share a dtype, be contiguous, and the tensor side must be [B, S_r, H, D]")
+    B, S_r, H, D = tensor.shape
+    if sum(counts) != H or pieces.numel() != tensor.numel():
+        raise ValueError(f"head_counts must sum to H={H} and the pieces buffer must hold {tensor.numel()} elements")
+    st = lib.cp_ulysses_pack_heads(inp.data_ptr(), out.data_ptr(), inp.element_size(), B, S_r, D, len(counts), arr,
+                                   direction, _stream(stream))
+    _check(st, "cp_ulysses_pack_heads")
+
+
+def cp_ulysses_concat_seq(inp, out, seq_counts: Sequence[int], direction: int = CP_REGROUP_SEQ_TO_HEAD,
+                          stream=None):
+    """Ulysses Anything: pieces [B, S_r, H_g, D] back to back (flat) <-> [B, sum S_r, H_g, D].
+
+    SEQ_TO_HEAD: ``inp`` is the flat pieces buffer, ``out`` the tensor; HEAD_TO_SEQ: the reverse.
+    See cp_ulysses_concat_seq in the header.
+    """
+    lib = _lib.load()
+    dev = _gpu("inp", inp).device
+    _gpu("out", out, dev)
+    arr, counts = _counts("seq_counts", seq_counts)
+    tensor = out if direction == CP_REGROUP_SEQ_TO_HEAD else inp
+    pieces = inp if direction == CP_REGROUP_SEQ_TO_HEAD else out
+    if inp.dtype != out.dtype or not (inp.is_contiguous() and out.is_contiguous()) or tensor.dim() != 4:
+        raise ValueError("tensors must share a dtype, be contiguous, and the tensor side must be [B, S, H_g, D]")
+    B, S, Hg, D = tensor.shape
+    if sum(counts) != S or pieces.numel() != tensor.numel():
+        raise ValueError(f"seq_counts must sum to S={S} and the pieces buffer must hold {tensor.numel()} elements")
+    st = lib.cp_ulysses_concat_seq(inp.data_ptr(), out.data_ptr(), inp.element_size(), B, Hg, D, len(counts), arr,
+                                   direction, _stream(stream))
+    _check(st, "cp_ulysses_concat_seq")
 
 
 def cp_attn_bwd_workspace_size(B: int, H: int, Sq: int, D: int) -> int:

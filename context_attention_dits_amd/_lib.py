@@ -51,6 +51,8 @@ _SIGNATURES = {
                                ctypes.POINTER(_i), _i, _i, _i, _i, _i, _i, ctypes.c_float, ctypes.c_uint,
                                _vp, _i64p, _vp, _vp, ctypes.c_size_t, _vp]),
     "cp_ulysses_regroup": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "cp_ulysses_pack_heads": (_i, [_vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(_i), _i, _vp]),
+    "cp_ulysses_concat_seq": (_i, [_vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(_i), _i, _vp]),
     "cp_attn_bwd_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "cp_attn_bwd_prep": (_i, [_vp, _i64p, _vp, _i64p, _i, _i, _i, _i, _i, _vp, ctypes.c_size_t, _vp]),
     "cp_attn_block_bwd": (_i, [_vp, _i64p, _vp, _vp, _i64p, _i, _i, _i, _i, _i, _i, ctypes.c_float,

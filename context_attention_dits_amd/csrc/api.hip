@@ -485,3 +485,66 @@ cp_status_t cp_ulysses_regroup(const void* in, void* out, int elem_bytes, int B,
 }
 
 }  // extern "C"
+namespace {
+
+// Shared checks of the uneven packs; *total receives the sum of counts.
+cp_status_t check_pieces(const char* fn, const void* in, void* out, int elem_bytes, int B, int other, int D,
+                         int degree, const int* counts, int direction, int64_t* total) {
+  if (elem_bytes != 2 && elem_bytes != 4)
+    return fail(CP_ERR_UNSUPPORTED, "%s: elem_bytes must be 2 or 4 (got %d)", fn, elem_bytes);
+  if (B < 0 || other < 0 || D < 0) return fail(CP_ERR_INVALID_ARG, "%s: sizes must be non-negative", fn);
+  if (degree < 1 || degree > cpattn::kMaxUlyssesDegree)
+    return fail(CP_ERR_INVALID_ARG, "%s: degree must be in 1..%d (got %d)", fn, cpattn::kMaxUlyssesDegree,
+                degree);
+  if (!counts) return fail(CP_ERR_INVALID_ARG, "%s: counts must be non-null", fn);
+  if (direction != CP_REGROUP_SEQ_TO_HEAD && direction != CP_REGROUP_HEAD_TO_SEQ)
+    return fail(CP_ERR_INVALID_ARG, "%s: unknown direction %d", fn, direction);
+  int64_t t = 0;
+  for (int g = 0; g < degree; ++g) {
+    if (counts[g] < 0) return fail(CP_ERR_INVALID_ARG, "%s: counts[%d] = %d is negative", fn, g, counts[g]);
+    t += counts[g];
+  }
+  *total = t;
+  const int64_t bytes = (int64_t)B * other * t * D * elem_bytes;
+  if (bytes == 0) return CP_OK;
+  if (bytes >= (int64_t(1) << 32))
+    return fail(CP_ERR_UNSUPPORTED, "%s: tensors of 2^32 bytes or more are not supported", fn);
+  if (!in || !out) return fail(CP_ERR_INVALID_ARG, "%s: pointers must be non-null", fn);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(in), b = reinterpret_cast<uintptr_t>(out);
+  if (a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes)
+    return fail(CP_ERR_INVALID_ARG, "%s: in and out overlap", fn);
+  if (!aligned(in, elem_bytes) || !aligned(out, elem_bytes))
+    return fail(CP_ERR_UNSUPPORTED, "%s: pointers must be aligned to elem_bytes", fn);
+  return CP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status_t cp_ulysses_pack_heads(const void* in, void* out, int elem_bytes, int B, int S_r, int D, int degree,
+                                  const int* head_counts, int direction, void* stream) {
+  int64_t H = 0;
+  cp_status_t st = check_pieces("cp_ulysses_pack_heads", in, out, elem_bytes, B, S_r, D, degree, head_counts,
+                                direction, &H);
+  if (st != CP_OK || (int64_t)B * S_r * H * D == 0) return st;
+  // [B*S_r, H heads] rows split by head: axis 2 with one unit per head
+  return hip_status(cpattn::launch_pieces(in, out, 2, 1, (int64_t)B * S_r, (int64_t)D * elem_bytes, H,
+                                          head_counts, degree, direction == CP_REGROUP_SEQ_TO_HEAD,
+                                          static_cast<hipStream_t>(stream)),
+                    "ulysses_pack_heads");
+}
+
+cp_status_t cp_ulysses_concat_seq(const void* in, void* out, int elem_bytes, int B, int H_g, int D, int degree,
+                                  const int* seq_counts, int direction, void* stream) {
+  int64_t S = 0;
+  cp_status_t st = check_pieces("cp_ulysses_concat_seq", in, out, elem_bytes, B, H_g, D, degree, seq_counts,
+                                direction, &S);
+  if (st != CP_OK || (int64_t)B * S * H_g * D == 0) return st;
+  // [B, S tokens, one token's H_g*D elements] split by token: axis 1
+  return hip_status(cpattn::launch_pieces(in, out, 1, B, S, (int64_t)H_g * D * elem_bytes, 1, seq_counts, degree,
+                                          direction == CP_REGROUP_HEAD_TO_SEQ, static_cast<hipStream_t>(stream)),
+                    "ulysses_concat_seq");
+}
+
+}  // extern "C"

@@ -82,6 +82,16 @@ hipError_t launch_lse_merge(float* out_acc, float* lse_acc, const float* out_blk
                             const float* lse_blk, Strides as, Strides bs, int B, int H, int Sq,
                             int D, hipStream_t stream);
 
+// Largest degree of the uneven Ulysses packs (per-piece tables travel in the kernel arguments).
+constexpr int kMaxUlyssesDegree = 64;
+
+// Uneven split of a [B, M, units_per_row] tensor (units of unit_bytes) along
+// M (axis 1, seg_units in rows) or along a row (axis 2, seg_units in units)
+// into P pieces back to back; to_pieces selects the direction. The caller
+// guarantees fewer than 2^31 words and unit_bytes a multiple of 2.
+hipError_t launch_pieces(const void* in, void* out, int axis, int64_t B, int64_t M, int64_t unit_bytes,
+                         int64_t units_per_row, const int* seg_units, int P, int to_pieces, hipStream_t stream);
+
 // Ulysses regroup bit copy; see cp_ulysses_regroup.
 hipError_t launch_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
                           int D, int degree, int direction, hipStream_t stream);

@@ -188,6 +188,46 @@ cp_status_t cp_ulysses_regroup(const void* in, void* out, int elem_bytes, int B,
                                int D, int degree, int direction, void* stream);
 
 /*
+ * Ulysses Anything: the packs around an all-to-all whose splits are uneven.
+ *
+ * [CP] "Ulysses Anything Attention" and [API] ulysses_anything: the sequence
+ * length and the head count need not divide by ulysses_degree (FLUX at
+ * 1008x1008, 4481 tokens over 4 GPUs). Rank r holds S_r tokens of every head;
+ * head group g (head_counts[g] consecutive heads) goes to rank g. Around the
+ * exchange (which is not part of this library) a rank runs:
+ *   first all-to-all:  cp_ulysses_pack_heads  SEQ_TO_HEAD, exchange,
+ *                      cp_ulysses_concat_seq  SEQ_TO_HEAD
+ *   second all-to-all: cp_ulysses_concat_seq  HEAD_TO_SEQ, exchange,
+ *                      cp_ulysses_pack_heads  HEAD_TO_SEQ
+ * Both are bit-exact permutations of elem_bytes-sized elements (2 or 4).
+ * Pieces lie back to back, each row-major, in rank order. degree is 1..64;
+ * counts may hold zeros. Tensors must stay below 2^32 bytes; in and out
+ * must not overlap. Zero-sized problems enqueue nothing.
+ */
+
+/*
+ * cp_ulysses_pack_heads -- [B, S_r, H, D] <-> pieces [B, S_r, head_counts[g], D],
+ * H = sum of head_counts.
+ *   SEQ_TO_HEAD: in = the tensor, out = the pieces (the first exchange's send buffer)
+ *   HEAD_TO_SEQ: in = the pieces (the second exchange's receive buffer, from
+ *                rank g the tokens of this rank for head group g), out = the tensor
+ */
+cp_status_t cp_ulysses_pack_heads(const void* in, void* out, int elem_bytes, int B, int S_r, int D, int degree,
+                                  const int* head_counts, int direction, void* stream);
+
+/*
+ * cp_ulysses_concat_seq -- pieces [B, seq_counts[r], H_g, D] <-> [B, S, H_g, D],
+ * S = sum of seq_counts (every token of this rank's head group).
+ *   SEQ_TO_HEAD: in = the pieces (the first exchange's receive buffer, rank r's
+ *                tokens from rank r), out = the tensor
+ *   HEAD_TO_SEQ: in = the tensor (this rank's output), out = the pieces (the
+ *                second exchange's send buffer)
+ * With B = 1 the two layouts coincide and the call is a plain copy.
+ */
+cp_status_t cp_ulysses_concat_seq(const void* in, void* out, int elem_bytes, int B, int H_g, int D, int degree,
+                                  const int* seq_counts, int direction, void* stream);
+
+/*
  * Backward of the ring share (bfloat16 Q/K/V, float32 gradients).
  *
  * [CP] the variants table that opens the page and the note under "Ring

@@ -27,7 +27,8 @@ def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
     assert {"cp_attn_block_fwd", "cp_lse_merge", "cp_ring_attention", "cp_ring_attention_workspace_size",
             "cp_ulysses_regroup", "cp_last_error", "cp_abi_version", "cp_attn_bwd_workspace_size",
-            "cp_attn_bwd_prep", "cp_attn_block_bwd", "cp_ring_attention_bwd"} <= set(names)
+            "cp_attn_bwd_prep", "cp_attn_block_bwd", "cp_ring_attention_bwd", "cp_ulysses_pack_heads",
+            "cp_ulysses_concat_seq"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert lib.cp_abi_version() == 1
@@ -206,6 +207,34 @@ def test_ring_bwd_rejects(lib):
     assert _ring_bwd(lib, [8, 8], ws_bytes=16) == _lib.CP_ERR_WORKSPACE
     assert _ring_bwd(lib, [8, 8], out=0) == _lib.CP_ERR_INVALID_ARG
     assert "out and dout" in _err(lib)
+
+
+def test_uneven_packs_reject(lib):
+    counts = (ctypes.c_int * 3)(2, 1, 3)
+    big = FAKE + (1 << 30)
+    for f in (lib.cp_ulysses_pack_heads, lib.cp_ulysses_concat_seq):
+        assert f(FAKE, big, 3, 1, 16, 128, 3, counts, 0, None) == _lib.CP_ERR_UNSUPPORTED  # elem_bytes
+        assert f(FAKE, big, 2, 1, 16, 128, 0, counts, 0, None) == _lib.CP_ERR_INVALID_ARG  # degree
+        assert f(FAKE, big, 2, 1, 16, 128, 65, counts, 0, None) == _lib.CP_ERR_INVALID_ARG
+        assert "1..64" in _err(lib)
+        assert f(FAKE, big, 2, 1, 16, 128, 3, None, 0, None) == _lib.CP_ERR_INVALID_ARG  # counts
+        assert f(FAKE, big, 2, 1, 16, 128, 3, counts, 5, None) == _lib.CP_ERR_INVALID_ARG  # direction
+        neg = (ctypes.c_int * 2)(3, -1)
+        assert f(FAKE, big, 2, 1, 16, 128, 2, neg, 0, None) == _lib.CP_ERR_INVALID_ARG
+        assert "negative" in _err(lib)
+        assert f(FAKE, FAKE + 64, 2, 1, 16, 128, 3, counts, 0, None) == _lib.CP_ERR_INVALID_ARG  # overlap
+        assert "overlap" in _err(lib)
+        assert f(0, 0, 2, 0, 16, 128, 3, counts, 0, None) == _lib.CP_OK  # empty: nothing enqueued
+        huge = (ctypes.c_int * 1)(1 << 20)
+        assert f(FAKE, big, 2, 16, 16, 128, 1, huge, 0, None) == _lib.CP_ERR_UNSUPPORTED  # >= 2^32 bytes
+        assert "2^32" in _err(lib)
+
+
+def test_split_counts():
+    import context_attention_dits_amd as cp
+    assert cp.split_counts(4481, 4) == [1121, 1120, 1120, 1120]
+    assert cp.split_counts(24, 5) == [5, 5, 5, 5, 4]
+    assert cp.split_counts(2, 3) == [1, 1, 0]
 
 
 def test_set_fwd_waves(lib):

@@ -359,3 +359,133 @@ def test_workload_usp_u2r2(cp):
     rows = workloads.sample_rows(w.Sq, 48, seed=5, must=_edges(w.Sq) + [w.S_local - 1, w.S_local])
     _check_rows(w.name, out, lse, q_h, k_all, v_all, w.scale, rows, w.dtype)
     assert np.array_equal(back, oracle.ulysses_regroup_inv(out, P))
+
+
+# -------------------------------------------------------- Ulysses Anything ---
+
+def _bits(x):
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    return a.view(np.uint32)
+
+
+@pytest.mark.parametrize("B,S_r,counts,D,dt", [(1, 1121, (6, 6, 6, 6), 128, "bf16"), (2, 37, (3, 0, 2, 5), 128, "bf16"),
+                                               (3, 5, (1, 2), 64, "f32"), (1, 9, (7,), 64, "bf16"),
+                                               (2, 3, (1, 1, 1), 4, "bf16")])
+def test_pack_heads_bit_exact(cp, B, S_r, counts, D, dt):
+    say("pack_heads", B, S_r, counts, D, dt)
+    H = sum(counts)
+    rng = np.random.default_rng(B * 1000 + S_r + H)
+    x = rng.standard_normal((B, S_r, H, D)).astype(np.float32)
+    if dt == "bf16":
+        x = workloads.round_to_bf16(x)
+    t = dev(x, dt)
+    buf = torch.empty(t.numel(), dtype=t.dtype, device="cuda")
+    cp.cp_ulysses_pack_heads(t, buf, counts, cp.CP_REGROUP_SEQ_TO_HEAD)
+    back = torch.full_like(t, float("nan"))
+    cp.cp_ulysses_pack_heads(buf, back, counts, cp.CP_REGROUP_HEAD_TO_SEQ)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(buf.float().cpu().numpy()), _bits(oracle.ulysses_pack_heads(x, counts)))
+    assert torch.equal(back, t)
+
+
+@pytest.mark.parametrize("B,counts,Hg,D,dt", [(2, (1121, 1120, 1120, 1120), 6, 128, "bf16"),
+                                              (3, (5, 0, 7), 2, 64, "f32"), (1, (4, 3), 3, 128, "bf16"),
+                                              (2, (1, 2, 3, 4, 5), 1, 4, "bf16")])
+def test_concat_seq_bit_exact(cp, B, counts, Hg, D, dt):
+    say("concat_seq", B, counts, Hg, D, dt)
+    S = sum(counts)
+    rng = np.random.default_rng(B * 7 + S + Hg)
+    buf = rng.standard_normal(B * S * Hg * D).astype(np.float32)
+    if dt == "bf16":
+        buf = workloads.round_to_bf16(buf)
+    tb = dev(buf, dt)
+    y = torch.empty((B, S, Hg, D), dtype=tb.dtype, device="cuda")
+    cp.cp_ulysses_concat_seq(tb, y, counts, cp.CP_REGROUP_SEQ_TO_HEAD)
+    back = torch.full_like(tb, float("nan"))
+    cp.cp_ulysses_concat_seq(y, back, counts, cp.CP_REGROUP_HEAD_TO_SEQ)
+    torch.cuda.synchronize()
+    want = oracle.ulysses_concat_seq(buf, B, counts, Hg, D)
+    assert np.array_equal(_bits(y.float().cpu().numpy()), _bits(want))
+    assert torch.equal(back, tb)
+
+
+def _anything_gpu(cp, q, k, v, seq, heads, scale):
+    """Every rank of an uneven Ulysses group on one GPU: the packs and the attention in the
+    library, the two exchanges as device copies between the ranks' buffers (test scaffolding)."""
+    P = len(seq)
+    B, S, H, D = q.shape
+    offs = workloads.block_offsets(seq)
+    piece = lambda r, g: B * seq[r] * heads[g] * D  # noqa: E731 - elements rank r sends rank g
+    views = []
+    for x in (q, k, v):
+        send = []
+        for r in range(P):
+            buf = torch.empty(B * seq[r] * H * D, dtype=x.dtype, device="cuda")
+            cp.cp_ulysses_pack_heads(x[:, offs[r]:offs[r] + seq[r]].contiguous(), buf, heads)
+            send.append(buf)
+        per_rank = []
+        for g in range(P):
+            recv = torch.cat([send[r][sum(piece(r, j) for j in range(g)):][:piece(r, g)] for r in range(P)])
+            t = torch.empty((B, S, heads[g], D), dtype=x.dtype, device="cuda")
+            cp.cp_ulysses_concat_seq(recv, t, seq, cp.CP_REGROUP_SEQ_TO_HEAD)
+            per_rank.append(t)
+        views.append(per_rank)
+    send2 = []
+    for g in range(P):
+        if heads[g] == 0:
+            send2.append(torch.empty(0, device="cuda"))
+            continue
+        o, _ = cp.ring_attention(views[0][g], [views[1][g]], [views[2][g]], scale=scale)
+        buf = torch.empty(o.numel(), dtype=torch.float32, device="cuda")
+        cp.cp_ulysses_concat_seq(o, buf, seq, cp.CP_REGROUP_HEAD_TO_SEQ)
+        send2.append(buf)
+    outs = []
+    for r in range(P):
+        got = [send2[g][sum(B * seq[j] * heads[g] * D for j in range(r)):][:B * seq[r] * heads[g] * D]
+               for g in range(P)]
+        out = torch.empty((B, seq[r], H, D), dtype=torch.float32, device="cuda")
+        cp.cp_ulysses_pack_heads(torch.cat(got), out, heads, cp.CP_REGROUP_HEAD_TO_SEQ)
+        outs.append(out)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+@pytest.mark.parametrize("B,seq,heads,D", [(2, (40, 39, 39), (2, 2, 1), 128), (1, (70, 69, 69, 69), (3, 2, 2, 2), 64)])
+def test_ulysses_anything_all_ranks(cp, B, seq, heads, D):
+    """Each rank's output after both exchanges equals full attention on its tokens."""
+    say("ulysses anything all ranks", B, seq, heads, D)
+    inp = workloads.make_custom(B, sum(heads), D, sum(seq), (sum(seq),), "bf16", seed=61)
+    scale = 1.0 / math.sqrt(D)
+    outs = _anything_gpu(cp, dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16"), seq, heads, scale)
+    want = oracle.ulysses_anything_attention(
+        [inp.q[:, a:a + L] for a, L in zip(workloads.block_offsets(seq), seq)],
+        [inp.k[:, a:a + L] for a, L in zip(workloads.block_offsets(seq), seq)],
+        [inp.v[:, a:a + L] for a, L in zip(workloads.block_offsets(seq), seq)], heads, scale)
+    for r in range(len(seq)):
+        assert_close(f"rank {r} out", outs[r], want[r], TOL["bf16"]["o"])
+
+
+def test_workload_ulysses_anything4(cp):
+    """Rank 0's share as bench.py runs it: pack of its shards, attention of head group 0 over all
+    4481 tokens, unpack of the second exchange's pieces; sampled rows against the oracle."""
+    w = workloads.by_name("flux1008_ulysses_anything4_bf16")
+    say(w.name)
+    import bench
+    prob = bench.Problem(w, False)
+    prob.step()
+    torch.cuda.synchronize()
+    inp = prob.inp
+    seq, heads = w.seq_counts, w.head_counts
+    # the pack of rank 0's own shards is bit-exact
+    for x, buf in zip((inp.q, inp.k, inp.v), prob.send):
+        want = oracle.ulysses_pack_heads(x[:, :seq[0]], heads)
+        assert np.array_equal(_bits(buf.float().cpu().numpy()), _bits(want))
+    H0 = heads[0]
+    rows = workloads.sample_rows(w.Sq, 48, seed=6, must=_edges(w.Sq) + [seq[0] - 1, seq[0]])
+    _check_rows(w.name, prob.out.cpu().numpy(), prob.lse.cpu().numpy(), inp.q[:, :, :H0], inp.k[:, :, :H0],
+                inp.v[:, :, :H0], w.scale, rows, w.dtype)
+    # rank 0's final output: full attention on its own tokens, every head
+    back = prob.back.cpu().numpy()
+    rows0 = workloads.sample_rows(seq[0], 24, seed=7)
+    o_ref, _ = oracle.attention(inp.q[:, rows0], inp.k, inp.v, w.scale)
+    assert_close(f"{w.name} rank-0 output", back[:, rows0], o_ref, TOL["bf16"]["o"])

@@ -19,7 +19,9 @@ is drawn by ``grad_out`` from its own generator (seed + 1000), float32 N(0, 1)
 and not rounded (the loss gradient arrives in float32). Q_local is drawn directly at its
 local shape ``[B, Sq, H, D]`` (one rank's slice); K and V are drawn at
 ``[B, sum(block_lens), H, D]`` and ring block i is the contiguous token range
-``[off_i, off_i + L_i)``.
+``[off_i, off_i + L_i)``. The Ulysses Anything workload draws Q, K and V
+for the whole sequence ``[B, Sq, H, D]``; rank r's shard is its token range
+(``split_lengths``), head group g its share of the heads.
 """
 from __future__ import annotations
 
@@ -53,7 +55,8 @@ class Workload:
     Sq: int
     block_lens: tuple
     ulysses_degree: int = 1
-    S_local: int = 0  # Ulysses: tokens per rank before the regroup
+    S_local: int = 0  # Ulysses: tokens per rank before the regroup (Ulysses Anything: rank 0's)
+    anything: bool = False  # Ulysses Anything: uneven sequence and head splits over the ranks
 
     @property
     def seed(self) -> int:
@@ -69,8 +72,20 @@ class Workload:
 
     @property
     def attn_H(self) -> int:
-        """Heads seen by the attention kernel (after any Ulysses regroup)."""
+        """Heads seen by the attention kernel (after any Ulysses regroup; rank 0's group)."""
+        if self.anything:
+            return self.head_counts[0]
         return self.H // self.ulysses_degree
+
+    @property
+    def seq_counts(self) -> List[int]:
+        """Ulysses Anything: tokens per rank (the whole sequence is Sq)."""
+        return split_lengths(self.Sq, self.ulysses_degree)
+
+    @property
+    def head_counts(self) -> List[int]:
+        """Ulysses Anything: heads per rank's group."""
+        return split_lengths(self.H, self.ulysses_degree)
 
     @property
     def flops(self) -> int:
@@ -96,6 +111,11 @@ WORKLOADS: List[Workload] = [
     # the regroup, two ring blocks of 2304 keys.
     Workload(5, "flux1024_usp_u2r2_bf16", "bf16", B=1, H=24, D=128, Sq=2304, block_lens=(2304, 2304),
              ulysses_degree=2, S_local=1152),
+    # Ulysses Anything, rank 0 of 4 on FLUX at 1008x1008: 63*63 image + 512
+    # text = 4481 tokens (1121, 1120, 1120, 1120 per rank), 6 heads per rank
+    # after the exchange, attention over all 4481 tokens.
+    Workload(6, "flux1008_ulysses_anything4_bf16", "bf16", B=1, H=24, D=128, Sq=4481, block_lens=(4481,),
+             ulysses_degree=4, S_local=1121, anything=True),
 ]
 
 
@@ -190,7 +210,13 @@ def make_inputs(w: Workload, q_scale: float = 1.0) -> Inputs:
     softmax's dynamic range); 1.0 is the standard recipe.
     """
     rng = np.random.default_rng(w.seed)
-    if w.ulysses_degree > 1:
+    if w.anything:
+        # every rank's shards: rank r holds tokens [off_r, off_r + S_r) of each
+        shp = (w.B, w.Sq, w.H, w.D)
+        q = rng.standard_normal(shp, dtype=np.float32)
+        k = rng.standard_normal(shp, dtype=np.float32)
+        v = rng.standard_normal(shp, dtype=np.float32)
+    elif w.ulysses_degree > 1:
         q = rng.standard_normal((w.B, w.S_local, w.H, w.D), dtype=np.float32)
         shp = (w.B, w.ring_degree * w.S_local, w.H, w.D)
         k = rng.standard_normal(shp, dtype=np.float32)
