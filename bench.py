@@ -230,8 +230,9 @@ def time_hbm_kernels(reps: int = 5):
     """HBM rate of the two bandwidth-bound kernels, cold caches.
 
     cp_lse_merge on the 32k-token ring-4 share (out [1, 8192, 24, 128] float32,
-    in place) and cp_ulysses_regroup SEQ_TO_HEAD of a [1, 16384, 24, 128] bf16
-    tensor at degree 2. Before each timed launch a 512 MiB buffer is read so
+    in place), cp_ulysses_regroup SEQ_TO_HEAD of a [1, 16384, 24, 128] bf16
+    tensor at degree 2 and cp_ulysses_pack_heads of the same tensor into
+    uneven head groups (7, 6, 6, 5). Before each timed launch a 512 MiB buffer is read so
     that neither L2 nor the 256 MB Infinity Cache holds the operands; bytes are
     the algorithmic ones (every element read once, written once).
     """
@@ -267,10 +268,14 @@ def time_hbm_kernels(reps: int = 5):
     y = torch.empty(B, P * S_l, H // P, D, dtype=torch.bfloat16, device="cuda")
     regroup_ms = timed(lambda: cp.cp_ulysses_regroup(x, y, P, cp.CP_REGROUP_SEQ_TO_HEAD))
     regroup_bytes = 2 * 2 * B * S_l * H * D
+    pieces = torch.empty(x.numel(), dtype=torch.bfloat16, device="cuda")
+    pack_ms = timed(lambda: cp.cp_ulysses_pack_heads(x, pieces, [7, 6, 6, 5], cp.CP_REGROUP_SEQ_TO_HEAD))
     out = {}
     for name, ms, nb, shape in (("lse_merge", merge_ms, merge_bytes, "out [1,8192,24,128] f32 + lse, in place"),
                                 ("ulysses_regroup", regroup_ms, regroup_bytes,
-                                 "[1,16384,24,128] bf16 -> [1,32768,12,128], degree 2")):
+                                 "[1,16384,24,128] bf16 -> [1,32768,12,128], degree 2"),
+                                ("ulysses_pack_heads", pack_ms, regroup_bytes,
+                                 "[1,16384,24,128] bf16 -> pieces of 7, 6, 6, 5 heads")):
         gbs = nb / (ms * 1e-3) / 1e9
         out[name] = {"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "us": round(ms * 1e3, 2),
                      "bytes": nb, "shape": shape}
