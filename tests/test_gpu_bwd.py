@@ -265,3 +265,26 @@ def test_bwd_workload_full_size_sampled(cp, idx, heads):
         lse[:, h:h + 1] = l_h
     got = _run(cp, inp, do, o, lse, scale)
     _check_all(f"bwd {w.name}", inp, do, scale, got, heads=heads)
+
+
+def test_bwd_padded_gather_with_nan_pads(cp):
+    """K/V blocks as slices of a padded all-gather [P, B, Lmax, H, D] whose pad rows hold NaN: the
+    backward never reads past a block's length."""
+    B, H, D, Sq, lens = 2, 2, 128, 90, (64, 63, 50)
+    say("bwd padded gather NaN", lens)
+    inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=41)
+    scale = 1.0 / np.sqrt(D)
+    do = workloads.grad_out((B, Sq, H, D), 41)
+    o, lse = _fwd_oracle(inp, scale)
+    Lmax = max(lens)
+    kpad = torch.full((len(lens), B, Lmax, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vpad = torch.full_like(kpad, float("nan"))
+    for i, L in enumerate(lens):
+        kpad[i, :, :L] = _bf16(inp.k_block(i))
+        vpad[i, :, :L] = _bf16(inp.v_block(i))
+    kb = [kpad[i, :, :L] for i, L in enumerate(lens)]
+    vb = [vpad[i, :, :L] for i, L in enumerate(lens)]
+    dq, dk, dv = cp.ring_attention_bwd(_bf16(inp.q), kb, vb, _f32(o), _f32(lse), _f32(do), scale=scale)
+    torch.cuda.synchronize()
+    got = (dq.cpu().numpy(), [t.cpu().numpy() for t in dk], [t.cpu().numpy() for t in dv])
+    _check_all("bwd padded gather", inp, do, scale, got)
