@@ -25,6 +25,8 @@
 //     registers (the row statistics LSE_i and D_i are per lane), and
 //     dQ^T += K^T dS^T takes K^T from transposing LDS reads of a row-major
 //     copy of the K tile and dS^T as bf16 in the accumulator's key order.
+//     The next tile's S and dP run on the matrix cores while the vector ALUs
+//     turn the current tile into dS (three LDS stages).
 //   * dkv kernel, one lane per key: the same with the roles of queries and
 //     keys exchanged: S = Q K^T and dP = dO V^T with K^T, V^T in registers and
 //     Q, dO fragments from LDS; the accumulator rows are queries, so LSE_i and
@@ -33,11 +35,12 @@
 //     copies.
 //   * Tiles of 32 rows (keys for dq, queries for dkv) go from global memory
 //     straight into LDS with buffer loads (descriptor ranges end at the valid
-//     rows, so padding rows arrive as zeros), two LDS stages, one barrier per
-//     tile. Padding queries have Q = dO = 0 and contribute nothing; padding
+//     rows, so padding rows arrive as zeros), one barrier per tile. Padding queries have Q = dO = 0 and contribute nothing; padding
 //     keys have their scores set to -inf in the dq kernel and their dK, dV
 //     rows are not stored by the dkv kernel.
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -189,6 +192,11 @@ __device__ __forceinline__ int range_bytes(int rows_left, int64_t row_bytes) {
 }
 
 // ---------------------------------------------------------------- dQ kernel
+//
+// Software-pipelined over 32-key tiles: while the vector ALUs turn tile t's
+// scores into dS_t, the matrix cores compute tile t+1's S and dP; then
+// dQ += K_t^T dS_t. Three LDS stages: in iteration t the waves read tile t+1's
+// fragments and tile t's row-major K, while tile t+2 is being loaded.
 
 template <int D, bool ACC>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
@@ -196,10 +204,13 @@ attn_bwd_dq_kernel(BwdParams p) {
   using T = TileCfg<D>;
   __shared__ __attribute__((aligned(1024))) char kf0[T::BYTES];
   __shared__ __attribute__((aligned(1024))) char kf1[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) char kf2[T::BYTES];
   __shared__ __attribute__((aligned(1024))) char vf0[T::BYTES];
   __shared__ __attribute__((aligned(1024))) char vf1[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vf2[T::BYTES];
   __shared__ __attribute__((aligned(1024))) char kr0[T::BYTES];
   __shared__ __attribute__((aligned(1024))) char kr1[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) char kr2[T::BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -248,30 +259,36 @@ attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
-  auto step = [&](int t, const char* kf, const char* vf, const char* kr) {
-    f32x16 s = f32x16{}, dpt = f32x16{};
+  // S^T = K Q^T and dP^T = V dO^T of one tile (16 MFMAs), fragments from LDS.
+  auto scores = [&](const char* kf, const char* vf, f32x16& s, f32x16& dpt) {
+    s = f32x16{};
+    dpt = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < T::KK; ++kk) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(kf + kk * 1024 + lane * 16);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
+      const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(vf + kk * 1024 + lane * 16);
+      dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, df[kk], dpt, 0, 0, 0);
     }
-#pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vf + kk * 1024 + lane * 16);
-      dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[kk], dpt, 0, 0, 0);
-    }
-    // This lane holds keys t*32 + 8*(r/4) + 4*hi + r%4; those past Skv get P = 0.
+  };
+  // dS^T of tile t as bf16 B operands; this lane holds keys t*32 + 8*(r/4) +
+  // 4*hi + r%4, and only the last tile can hold keys past Skv (P = 0 there).
+  auto softmax = [&](auto last_tag, int t, const f32x16& s, const f32x16& dpt, bf16x8 (&dsb)[2]) {
+    constexpr bool LAST = decltype(last_tag)::value;
     const int lim = p.Skv - t * TR - 4 * hi;
-    bf16x8 dsb[2];
 #pragma unroll
     for (int kk2 = 0; kk2 < 2; ++kk2) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int r = kk2 * 8 + jj;
-        const float pr = (8 * (r >> 2) + (r & 3) < lim) ? __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -lse2)) : 0.f;
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -lse2));
+        if constexpr (LAST) pr = (8 * (r >> 2) + (r & 3) < lim) ? pr : 0.f;
         dsb[kk2][jj] = (__bf16)(pr * (dpt[r] - dlt));
       }
     }
+  };
+  // dQ^T += K^T dS^T for one tile (8 MFMAs), K^T from transposing reads.
+  auto dq_update = [&](const char* kr, const bf16x8 (&dsb)[2]) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -279,18 +296,56 @@ attn_bwd_dq_kernel(BwdParams p) {
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(kr, tr_lane, db, kk2), dsb[kk2], acc[db], 0, 0, 0);
   };
 
-  issue(0, kf0, vf0, kr0);
-  sync();
-  int t = 0;
-  for (; t + 2 <= n_tiles; t += 2) {
-    issue(t + 1, kf1, vf1, kr1);
-    step(t, kf0, vf0, kr0);
-    sync();
-    if (t + 2 < n_tiles) issue(t + 2, kf0, vf0, kr0);
-    step(t + 1, kf1, vf1, kr1);
-    sync();
+  f32x16 s_cur, d_cur, s_nxt, d_nxt;
+  // One iteration: tile t's softmax interleaved with tile t+1's scores, then
+  // tile t's dQ update. Stage c holds tile t, stage n tile t+1, stage f is
+  // free (tile t+2 goes there).
+  auto iter = [&](int t, const char* kr_c, const char* kf_n, const char* vf_n, const char* kr_n, char* kf_f,
+                  char* vf_f, char* kr_f) {
+    sync();  // tile t+1 has landed; every wave is done with the free stage
+    if (t + 2 < n_tiles) issue(t + 2, kf_f, vf_f, kr_f);
+    bf16x8 dsb[2];
+    if (t + 1 < n_tiles) {
+      scores(kf_n, vf_n, s_nxt, d_nxt);
+      softmax(std::false_type{}, t, s_cur, d_cur, dsb);
+      // 16 MFMAs with their 16 fragment reads, ~80 VALU ops between them
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+    } else {
+      softmax(std::true_type{}, t, s_cur, d_cur, dsb);
+    }
+    dq_update(kr_c, dsb);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    s_cur = s_nxt;
+    d_cur = d_nxt;
+    (void)kr_n;
+  };
+
+  if (n_tiles > 0) {  // no keys: dQ = 0
+    issue(0, kf0, vf0, kr0);
+    if (n_tiles > 1) issue(1, kf1, vf1, kr1);
+    __builtin_amdgcn_s_waitcnt(0);  // tiles 0 and 1 in LDS
+    __syncthreads();
+    scores(kf0, vf0, s_cur, d_cur);
   }
-  if (t < n_tiles) step(t, kf0, vf0, kr0);
+  int t = 0;
+  for (; t + 3 <= n_tiles; t += 3) {
+    iter(t, kr0, kf1, vf1, kr1, kf2, vf2, kr2);
+    iter(t + 1, kr1, kf2, vf2, kr2, kf0, vf0, kr0);
+    iter(t + 2, kr2, kf0, vf0, kr0, kf1, vf1, kr1);
+  }
+  if (t < n_tiles) iter(t, kr0, kf1, vf1, kr1, kf2, vf2, kr2);
+  if (t + 1 < n_tiles) iter(t + 1, kr1, kf2, vf2, kr2, kf0, vf0, kr0);
 
   if (valid) {
     float* out = p.dq + b * p.dq_sb + (int64_t)row * p.dq_ss + h * p.dq_sh;
@@ -308,6 +363,7 @@ attn_bwd_dq_kernel(BwdParams p) {
       }
   }
 }
+
 
 // --------------------------------------------------------------- dKV kernel
 
