@@ -489,3 +489,25 @@ def test_workload_ulysses_anything4(cp):
     rows0 = workloads.sample_rows(seq[0], 24, seed=7)
     o_ref, _ = oracle.attention(inp.q[:, rows0], inp.k, inp.v, w.scale)
     assert_close(f"{w.name} rank-0 output", back[:, rows0], o_ref, TOL["bf16"]["o"])
+
+
+# ------------------------------------------------------ short key blocks ---
+
+@pytest.mark.parametrize("waves", SHAPES)
+def test_short_blocks_many_seeds(cp, waves):
+    """Blocks of one to three 64-key tiles (full and partial), where the pipeline's prologue,
+    tail steps and empty-range loads all meet, over several seeds and 8 heads."""
+    B, H, D, Sq = 1, 8, 128, 300
+    with fwd_waves(cp, waves):
+        for Skv in (64, 100, 128, 129, 192):
+            for seed in range(4):
+                inp = workloads.make_custom(B, H, D, Sq, (Skv,), "bf16", seed=900 + 10 * Skv + seed)
+                q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+                out = torch.empty((B, Sq, H, D), device="cuda")
+                lse = torch.empty((B, H, Sq), device="cuda")
+                cp.cp_attn_block_fwd(q, k, v, out, lse, scale=inp.workload.scale)
+                torch.cuda.synchronize()
+                o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.workload.scale)
+                say(f"waves={waves} Skv={Skv} seed={seed}")
+                assert_close("out", out.cpu().numpy(), o_ref, TOL["bf16"]["o"])
+                assert_close("lse", lse.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
