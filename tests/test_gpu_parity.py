@@ -511,3 +511,54 @@ def test_short_blocks_many_seeds(cp, waves):
                 say(f"waves={waves} Skv={Skv} seed={seed}")
                 assert_close("out", out.cpu().numpy(), o_ref, TOL["bf16"]["o"])
                 assert_close("lse", lse.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
+
+
+# ------------------------------------------------------- graph capture ---
+
+def test_ring_and_backward_replay_in_a_graph(cp):
+    """cp_ring_attention and cp_ring_attention_bwd only enqueue kernels on the caller's stream,
+    so they can be captured into a HIP graph. Replays, with eager work between them, must give
+    exactly the eager results (the kernels are deterministic)."""
+    B, H, D, Sq, lens = 1, 4, 128, 300, (256, 200)
+    say("graph capture ring + backward")
+    inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=81)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    offs = workloads.block_offsets(lens)
+    kb = [k[:, a:a + L] for a, L in zip(offs, lens)]
+    vb = [v[:, a:a + L] for a, L in zip(offs, lens)]
+    do = torch.from_numpy(workloads.grad_out((B, Sq, H, D), 81)).cuda()
+    out = torch.empty((B, Sq, H, D), device="cuda")
+    lse = torch.empty((B, H, Sq), device="cuda")
+    dq = torch.empty_like(out)
+    dk_all = torch.empty((B, sum(lens), H, D), device="cuda")
+    dv_all = torch.empty_like(dk_all)
+    dk = [dk_all[:, a:a + L] for a, L in zip(offs, lens)]
+    dv = [dv_all[:, a:a + L] for a, L in zip(offs, lens)]
+    ws = torch.empty(cp.cp_attn_bwd_workspace_size(B, H, Sq, D), dtype=torch.uint8, device="cuda")
+    flags = cp.CP_RING_ANYTHING
+
+    def step():
+        cp.cp_ring_attention(q, kb, vb, out, lse, scale=inp.workload.scale, flags=flags)
+        cp.cp_ring_attention_bwd(q, kb, vb, out, lse, do, dq, dk, dv, scale=inp.workload.scale, flags=flags,
+                                 workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (out, lse, dq, dk_all, dv_all)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in (out, lse, dq, dk_all, dv_all):
+            t.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, w in zip(("out", "lse", "dq", "dk", "dv"), (out, lse, dq, dk_all, dv_all), want):
+            assert torch.equal(got, w), f"replay {rep}: {name} differs from the eager run"
+    say("graph replays match the eager run bit for bit")
