@@ -9,6 +9,15 @@ K and V, attention over all tokens for the local heads, and the inverse
 regroup of the output (Ulysses Anything: the uneven head-group packs around
 the two exchanges, which are outside the step).
 
+bf16 workloads whose block kernel runs its 8-wave shape (cp_attn_fwd_waves)
+pass V to the attention kernel packed (cp_attn_pack_v), and the
+step includes the packing a rank does itself: a ring rank packs its own V block
+(the other ranks' blocks arrive packed by their owners, so they are packed once
+at setup, as the peers would have done); a Ulysses rank packs the V it received
+(its regrouped V: the regroup and the packing run as one pass,
+cp_ulysses_regroup_pack_v). ``--unpacked-v`` runs the same step with V as
+[B, S, H, D].
+
 Prints ONE JSON line on stdout. ``value`` is attention TFLOP/s over the whole
 step, counting 4*B*H*Sq*Skv*D flops; ``roofline`` prices the dominant kernel
 (block attention) from its per-launch duration measured with HIP events on
@@ -51,6 +60,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=[w.name for w in workloads.WORKLOADS])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample (0 disables it)")
+    ap.add_argument("--unpacked-v", action="store_true",
+                    help="pass V as [B, S, H, D] instead of packed (bf16 workloads)")
     ap.add_argument("--separate-merge", action="store_true",
                     help="merge partials with the standalone merge kernel instead of the fused epilogue")
     return ap.parse_args()
@@ -59,7 +70,7 @@ def parse():
 class Problem:
     """Device-resident inputs and outputs of one workload, and its step."""
 
-    def __init__(self, w: workloads.Workload, separate_merge: bool):
+    def __init__(self, w: workloads.Workload, separate_merge: bool, packed_v: bool = True):
         import torch
         import context_attention_dits_amd as cp
         self.cp, self.torch, self.w = cp, torch, w
@@ -90,6 +101,8 @@ class Problem:
                                       cp.CP_REGROUP_SEQ_TO_HEAD)
                 cp.cp_ulysses_regroup(self.v[:, r * S_l:(r + 1) * S_l].contiguous(), self.vb[r], P,
                                       cp.CP_REGROUP_SEQ_TO_HEAD)
+            # this rank's own block, regrouped once here too (the backward reads it unpacked)
+            cp.cp_ulysses_regroup(self.v_own, self.vb[0], P, cp.CP_REGROUP_SEQ_TO_HEAD)
             self.back = torch.empty((B, S_l, w.H, D), dtype=torch.float32, device="cuda")
             self.q_att = self.qr
         else:
@@ -98,6 +111,14 @@ class Problem:
             self.kb = [self.k[:, o:o + L] for o, L in zip(offs, w.block_lens)]
             self.vb = [self.v[:, o:o + L] for o, L in zip(offs, w.block_lens)]
         H = w.attn_H
+        # V as the attention kernel reads it: block 0 (this rank's own block, or the V it received)
+        # is packed in every step, the others once here
+        # (only where the kernel runs its 8-wave shape: the 4-wave kernel gains nothing from it)
+        self.packed = packed_v and w.dtype == "bf16" and cp.cp_attn_fwd_waves(B, H, D, w.Sq) == 8
+        self.vb_att = list(self.vb)
+        if self.packed:
+            self.vb_att = [cp.pack_v(x) for x in self.vb]
+            torch.cuda.synchronize()
         self.out = torch.empty((B, w.Sq, H, D), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((B, H, w.Sq), dtype=torch.float32, device="cuda")
         nbytes = cp.cp_ring_attention_workspace_size(B, H, w.Sq, D, self.flags)
@@ -148,7 +169,9 @@ class Problem:
         if w.anything:
             for x, buf in zip(self.own, self.send):
                 cp.cp_ulysses_pack_heads(x, buf, self.heads, cp.CP_REGROUP_SEQ_TO_HEAD)
-            cp.cp_ring_attention(self.q_att, self.kb, self.vb, self.out, self.lse, scale=w.scale,
+            if self.packed:
+                cp.cp_attn_pack_v(self.vb[0], self.vb_att[0].data)
+            cp.cp_ring_attention(self.q_att, self.kb, self.vb_att, self.out, self.lse, scale=w.scale,
                                  flags=self.flags, workspace=self.ws)
             cp.cp_ulysses_pack_heads(self.recv2, self.back, self.heads, cp.CP_REGROUP_HEAD_TO_SEQ)
             return
@@ -156,8 +179,13 @@ class Problem:
             P = w.ulysses_degree
             cp.cp_ulysses_regroup(self.q, self.qr, P, cp.CP_REGROUP_SEQ_TO_HEAD)
             cp.cp_ulysses_regroup(self.k_own, self.kb[0], P, cp.CP_REGROUP_SEQ_TO_HEAD)
-            cp.cp_ulysses_regroup(self.v_own, self.vb[0], P, cp.CP_REGROUP_SEQ_TO_HEAD)
-        cp.cp_ring_attention(self.q_att, self.kb, self.vb, self.out, self.lse, scale=w.scale,
+            if self.packed:  # the regroup of V and its packing in one pass
+                cp.cp_ulysses_regroup_pack_v(self.v_own, self.vb_att[0].data, P)
+            else:
+                cp.cp_ulysses_regroup(self.v_own, self.vb[0], P, cp.CP_REGROUP_SEQ_TO_HEAD)
+        elif self.packed:
+            cp.cp_attn_pack_v(self.vb[0], self.vb_att[0].data)
+        cp.cp_ring_attention(self.q_att, self.kb, self.vb_att, self.out, self.lse, scale=w.scale,
                              flags=self.flags, workspace=self.ws)
         if w.ulysses_degree > 1:
             cp.cp_ulysses_regroup(self.out, self.back, w.ulysses_degree, cp.CP_REGROUP_HEAD_TO_SEQ)
@@ -172,7 +200,7 @@ class Problem:
         """
         torch, cp, w = self.torch, self.cp, self.w
         stream = torch.cuda.current_stream()
-        blocks = [(i, kb, vb) for i, (kb, vb) in enumerate(zip(self.kb, self.vb)) if kb.shape[1] > 0]
+        blocks = [(i, kb, vb) for i, (kb, vb) in enumerate(zip(self.kb, self.vb_att)) if kb.shape[1] > 0]
 
         def one_pass():
             for i, kb, vb in blocks:
@@ -231,8 +259,9 @@ def time_hbm_kernels(reps: int = 5):
 
     cp_lse_merge on the 32k-token ring-4 share (out [1, 8192, 24, 128] float32,
     in place), cp_ulysses_regroup SEQ_TO_HEAD of a [1, 16384, 24, 128] bf16
-    tensor at degree 2 and cp_ulysses_pack_heads of the same tensor into
-    uneven head groups (7, 6, 6, 5). Before each timed launch a 512 MiB buffer is read so
+    tensor at degree 2, cp_ulysses_pack_heads of the same tensor into
+    uneven head groups (7, 6, 6, 5) and cp_attn_pack_v of it (as one V block
+    of 16384 keys). Before each timed launch a 512 MiB buffer is read so
     that neither L2 nor the 256 MB Infinity Cache holds the operands; bytes are
     the algorithmic ones (every element read once, written once).
     """
@@ -270,12 +299,16 @@ def time_hbm_kernels(reps: int = 5):
     regroup_bytes = 2 * 2 * B * S_l * H * D
     pieces = torch.empty(x.numel(), dtype=torch.bfloat16, device="cuda")
     pack_ms = timed(lambda: cp.cp_ulysses_pack_heads(x, pieces, [7, 6, 6, 5], cp.CP_REGROUP_SEQ_TO_HEAD))
+    pv = torch.empty(cp.cp_attn_packed_v_bytes(B, H, D, S_l), dtype=torch.uint8, device="cuda")
+    packv_ms = timed(lambda: cp.cp_attn_pack_v(x, pv))
     out = {}
     for name, ms, nb, shape in (("lse_merge", merge_ms, merge_bytes, "out [1,8192,24,128] f32 + lse, in place"),
                                 ("ulysses_regroup", regroup_ms, regroup_bytes,
                                  "[1,16384,24,128] bf16 -> [1,32768,12,128], degree 2"),
                                 ("ulysses_pack_heads", pack_ms, regroup_bytes,
-                                 "[1,16384,24,128] bf16 -> pieces of 7, 6, 6, 5 heads")):
+                                 "[1,16384,24,128] bf16 -> pieces of 7, 6, 6, 5 heads"),
+                                ("pack_v", packv_ms, regroup_bytes,
+                                 "V [1,16384,24,128] bf16 -> packed tiles")):
         gbs = nb / (ms * 1e-3) / 1e9
         out[name] = {"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "us": round(ms * 1e3, 2),
                      "bytes": nb, "shape": shape}
@@ -367,7 +400,7 @@ def main():
         return 2
     w = workloads.by_name(args.workload)
     log(f"[bench] workload {w.name}: B={w.B} H={w.attn_H} D={w.D} Sq={w.Sq} blocks={list(w.block_lens)}")
-    prob = Problem(w, args.separate_merge)
+    prob = Problem(w, args.separate_merge, packed_v=not args.unpacked_v)
 
     for _ in range(args.warmup):
         prob.step()
@@ -429,6 +462,7 @@ def main():
                    "ulysses_degree": w.ulysses_degree,
                    **({"seq_counts": w.seq_counts, "head_counts": w.head_counts} if w.anything else {}),
                    "merge": "separate" if args.separate_merge else "fused",
+                   "v_layout": "packed" if prob.packed else "bshd",
                    "pct_of_bf16_peak": round(100 * tflops / PEAK_TFLOPS["bf16"], 2)},
         "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": hbm_traffic(w),

@@ -17,13 +17,14 @@ import math
 from typing import Optional, Sequence, Tuple
 
 from . import _lib
-from ._lib import (CP_BF16, CP_BLOCK_ACCUMULATE, CP_BWD_ACCUMULATE_DQ, CP_ERR_HIP, CP_ERR_INVALID_ARG,  # noqa: F401
-                   CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_F32, CP_OK, CP_REGROUP_HEAD_TO_SEQ,
-                   CP_REGROUP_SEQ_TO_HEAD, CP_RING_ANYTHING, CP_RING_SEPARATE_MERGE, STATUS_NAMES)
+from ._lib import (CP_BF16, CP_BLOCK_ACCUMULATE, CP_BLOCK_PACKED_V, CP_BWD_ACCUMULATE_DQ,  # noqa: F401
+                   CP_ERR_HIP, CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_F32, CP_OK,
+                   CP_REGROUP_HEAD_TO_SEQ, CP_REGROUP_SEQ_TO_HEAD, CP_RING_ANYTHING, CP_RING_PACKED_V,
+                   CP_RING_SEPARATE_MERGE, STATUS_NAMES)
 
 __all__ = [
-    "CpAttnError", "load", "cp_abi_version", "cp_last_error", "cp_attn_set_fwd_waves", "cp_attn_block_fwd",
-    "cp_lse_merge",
+    "CpAttnError", "load", "cp_abi_version", "cp_last_error", "cp_attn_set_fwd_waves", "cp_attn_fwd_waves", "cp_attn_block_fwd",
+    "cp_lse_merge", "PackedV", "cp_attn_packed_v_bytes", "cp_attn_pack_v", "pack_v", "cp_ulysses_regroup_pack_v",
     "cp_ring_attention", "cp_ring_attention_workspace_size", "cp_ulysses_regroup",
     "cp_ulysses_pack_heads", "cp_ulysses_concat_seq", "split_counts",
     "cp_attn_bwd_workspace_size", "cp_attn_bwd_prep", "cp_attn_block_bwd", "cp_ring_attention_bwd",
@@ -115,17 +116,92 @@ def cp_attn_set_fwd_waves(waves: int) -> int:
     return prev
 
 
+class PackedV:
+    """V of one bfloat16 block as written by cp_attn_pack_v: ``data`` is the packed device buffer,
+    ``shape`` the [B, Skv, H, D] shape of the V it holds (the layout is the kernel's own)."""
+
+    def __init__(self, data, shape):
+        self.data, self.shape = data, tuple(int(x) for x in shape)
+        self.dtype = _torch().bfloat16
+        self.device = data.device
+        self.is_cuda = data.is_cuda
+
+    def data_ptr(self) -> int:
+        return self.data.data_ptr()
+
+
+def cp_attn_packed_v_bytes(B: int, H: int, D: int, Skv: int) -> int:
+    return int(_lib.load().cp_attn_packed_v_bytes(B, H, D, Skv))
+
+
+def cp_attn_pack_v(v, packed, stream=None) -> PackedV:
+    """Write bfloat16 V [B, Skv, H, D] into the device buffer ``packed`` (any dtype, contiguous, at
+    least cp_attn_packed_v_bytes bytes); returns it as a PackedV. See cp_attn_pack_v in the header."""
+    torch = _torch()
+    lib = _lib.load()
+    dev = _gpu("v", _bshd("v", v)).device
+    _gpu("packed", packed, dev)
+    if v.dtype != torch.bfloat16:
+        raise TypeError("cp_attn_pack_v: v must be bfloat16")
+    if not packed.is_contiguous():
+        raise ValueError("cp_attn_pack_v: packed must be contiguous")
+    B, Skv, H, D = v.shape
+    st = lib.cp_attn_pack_v(v.data_ptr(), _strides(v), B, H, D, Skv, packed.data_ptr(),
+                            packed.numel() * packed.element_size(), _stream(stream))
+    _check(st, "cp_attn_pack_v")
+    return PackedV(packed, (B, Skv, H, D))
+
+
+def cp_ulysses_regroup_pack_v(inp, packed, degree: int, stream=None) -> PackedV:
+    """Regroup bfloat16 V [B, S_local, H, D] (contiguous) for the Ulysses degree and pack it, in one
+    pass, into ``packed``; returns the PackedV of the [B, degree*S_local, H/degree, D] tensor that
+    cp_ulysses_regroup would have produced. See cp_ulysses_regroup_pack_v in the header."""
+    torch = _torch()
+    lib = _lib.load()
+    dev = _gpu("in", _bshd("in", inp)).device
+    _gpu("packed", packed, dev)
+    if inp.dtype != torch.bfloat16 or not inp.is_contiguous():
+        raise ValueError("cp_ulysses_regroup_pack_v: in must be a contiguous bfloat16 tensor")
+    if not packed.is_contiguous():
+        raise ValueError("cp_ulysses_regroup_pack_v: packed must be contiguous")
+    B, S_l, H, D = inp.shape
+    st = lib.cp_ulysses_regroup_pack_v(inp.data_ptr(), B, S_l, H, D, int(degree), packed.data_ptr(),
+                                       packed.numel() * packed.element_size(), _stream(stream))
+    _check(st, "cp_ulysses_regroup_pack_v")
+    return PackedV(packed, (B, int(degree) * S_l, H // int(degree), D))
+
+
+def _v_operand(name, v, dev):
+    """(is_packed, v) for a V argument that is a [B, S, H, D] tensor or a PackedV."""
+    if isinstance(v, PackedV):
+        _gpu(name, v.data, dev)
+        return True, v
+    return False, _gpu(name, _bshd(name, v), dev)
+
+
+def cp_attn_fwd_waves(B: int, H: int, D: int, Sq: int) -> int:
+    """Workgroup shape (4, or 8 for the ping-pong kernel) of the bfloat16 block kernel at these sizes;
+    0 for sizes it does not run. Packed V (cp_attn_pack_v) pays off in the 8-wave shape."""
+    return int(_lib.load().cp_attn_fwd_waves(B, H, D, Sq))
+
+
 def cp_attn_block_fwd(q, k, v, out, lse, scale: Optional[float] = None, flags: int = 0, stream=None):
-    """Partial attention of q against one K/V block into (out, lse); see cp_attn_block_fwd in the header."""
+    """Partial attention of q against one K/V block into (out, lse); see cp_attn_block_fwd in the header.
+    ``v`` may be a PackedV (from cp_attn_pack_v), which sets CP_BLOCK_PACKED_V."""
     lib = _lib.load()
     dev = _gpu("q", _bshd("q", q)).device
-    _gpu("k", _bshd("k", k), dev); _gpu("v", _bshd("v", v), dev)
+    _gpu("k", _bshd("k", k), dev)
+    packed, v = _v_operand("v", v, dev)
     _gpu("out", _bshd("out", out), dev); _gpu("lse", lse, dev)
     B, Sq, H, D = q.shape
     Skv = k.shape[1]
     if tuple(k.shape) != (B, Skv, H, D) or tuple(v.shape) != (B, Skv, H, D):
         raise ValueError(f"k/v shapes {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
-    if k.stride() != v.stride():
+    if packed:
+        flags |= CP_BLOCK_PACKED_V
+    elif flags & CP_BLOCK_PACKED_V:
+        raise ValueError("CP_BLOCK_PACKED_V needs v from cp_attn_pack_v")
+    elif k.stride() != v.stride():
         raise ValueError("k and v must share strides")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share a dtype")
@@ -155,15 +231,21 @@ def cp_lse_merge(out_acc, lse_acc, out_blk, lse_blk, stream=None):
     _check(st, "cp_lse_merge")
 
 
-def _block_list(q, k_blocks, v_blocks, dev, dtype=None, what="K/V"):
-    """Check a list of [B, L_i, H, D] block pairs against q; returns (P, lens, shared stride triple)."""
+def _block_list(q, k_blocks, v_blocks, dev, dtype=None, what="K/V", allow_packed=False):
+    """Check a list of [B, L_i, H, D] block pairs against q; returns (P, lens, shared stride triple).
+    With allow_packed the V blocks may all be PackedV (their strides are then not compared)."""
     B, _, H, D = q.shape
     P = len(k_blocks)
     if P < 1 or len(v_blocks) != P:
         raise ValueError(f"need as many {what} blocks of each kind (>= 1)")
+    n_packed = sum(isinstance(vb, PackedV) for vb in v_blocks)
+    if n_packed and (not allow_packed or n_packed != P):
+        raise ValueError("V blocks must be all packed (cp_attn_pack_v) or all unpacked"
+                         if allow_packed else f"{what}: packed V blocks are not accepted here")
     stride0 = None
     for i, (kb, vb) in enumerate(zip(k_blocks, v_blocks)):
-        _gpu(f"{what} block {i}", _bshd(f"{what} block", kb), dev); _gpu(f"{what} block {i}", _bshd(f"{what} block", vb), dev)
+        _gpu(f"{what} block {i}", _bshd(f"{what} block", kb), dev)
+        _v_operand(f"{what} block {i}", vb, dev)
         L = kb.shape[1]
         if tuple(kb.shape) != (B, L, H, D) or tuple(vb.shape) != (B, L, H, D):
             raise ValueError(f"{what} block {i}: shapes {tuple(kb.shape)}/{tuple(vb.shape)} do not match q")
@@ -173,7 +255,7 @@ def _block_list(q, k_blocks, v_blocks, dev, dtype=None, what="K/V"):
         s = (kb.stride(0), kb.stride(1), kb.stride(2))
         if stride0 is None:
             stride0 = s
-        if s != stride0 or (vb.stride(0), vb.stride(1), vb.stride(2)) != stride0:
+        if s != stride0 or (not n_packed and (vb.stride(0), vb.stride(1), vb.stride(2)) != stride0):
             raise ValueError(f"every {what} block must share one stride triple")
     lens = (ctypes.c_int * P)(*[int(kb.shape[1]) for kb in k_blocks])
     return P, lens, stride0
@@ -195,13 +277,18 @@ def cp_ring_attention(q, k_blocks: Sequence, v_blocks: Sequence, out, lse, scale
     """One rank's ring share over resident K/V blocks into (out, lse); see cp_ring_attention.
 
     ``k_blocks[i]``/``v_blocks[i]`` are ``[B, L_i, H, D]`` views sharing one stride triple
-    (e.g. slices of one buffer, or of a padded ``[P, B, Lmax, H, D]`` gather).
+    (e.g. slices of one buffer, or of a padded ``[P, B, Lmax, H, D]`` gather). The V blocks may
+    instead all be PackedV (cp_attn_pack_v), which sets CP_RING_PACKED_V.
     """
     lib = _lib.load()
     dev = _gpu("q", _bshd("q", q)).device
     _gpu("out", _bshd("out", out), dev); _gpu("lse", lse, dev)
     B, Sq, H, D = q.shape
-    P, lens, stride0 = _block_list(q, k_blocks, v_blocks, dev)
+    P, lens, stride0 = _block_list(q, k_blocks, v_blocks, dev, allow_packed=True)
+    if isinstance(v_blocks[0], PackedV):
+        flags |= CP_RING_PACKED_V
+    elif flags & CP_RING_PACKED_V:
+        raise ValueError("CP_RING_PACKED_V needs V blocks from cp_attn_pack_v")
     if tuple(out.shape) != (B, Sq, H, D):
         raise ValueError("out must be [B, Sq, H, D]")
     _f32("out", out)
@@ -377,6 +464,15 @@ def cp_ring_attention_bwd(q, k_blocks: Sequence, v_blocks: Sequence, out, lse, d
 
 
 # ------------------------------------------------------- allocating helpers ---
+
+def pack_v(v, stream=None) -> PackedV:
+    """Allocate the packed buffer and run cp_attn_pack_v on bfloat16 V [B, Skv, H, D]."""
+    torch = _torch()
+    B, Skv, H, D = v.shape
+    nbytes = cp_attn_packed_v_bytes(B, H, D, Skv)
+    buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=v.device)
+    return cp_attn_pack_v(v, buf, stream=stream)
+
 
 def ring_attention(q, k_blocks, v_blocks, scale: Optional[float] = None, ring_anything: Optional[bool] = None,
                    separate_merge: bool = False, stream=None) -> Tuple:

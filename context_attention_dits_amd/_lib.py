@@ -27,8 +27,10 @@ CP_F32 = 0
 CP_BF16 = 1
 
 CP_BLOCK_ACCUMULATE = 0x1
+CP_BLOCK_PACKED_V = 0x2
 CP_RING_ANYTHING = 0x2
 CP_RING_SEPARATE_MERGE = 0x4
+CP_RING_PACKED_V = 0x8
 
 CP_BWD_ACCUMULATE_DQ = 0x1
 
@@ -43,9 +45,13 @@ _SIGNATURES = {
     "cp_abi_version": (_i, []),
     "cp_last_error": (ctypes.c_char_p, []),
     "cp_attn_set_fwd_waves": (_i, [_i]),
+    "cp_attn_fwd_waves": (_i, [_i, _i, _i, _i]),
     "cp_attn_block_fwd": (_i, [_vp, _i64p, _vp, _vp, _i64p, _i, _i, _i, _i, _i, _i, ctypes.c_float,
                                ctypes.c_uint, _vp, _i64p, _vp, _vp]),
     "cp_lse_merge": (_i, [_vp, _vp, _vp, _vp, _i64p, _i64p, _i, _i, _i, _i, _vp]),
+    "cp_attn_packed_v_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "cp_attn_pack_v": (_i, [_vp, _i64p, _i, _i, _i, _i, _vp, ctypes.c_size_t, _vp]),
+    "cp_ulysses_regroup_pack_v": (_i, [_vp, _i, _i, _i, _i, _i, _vp, ctypes.c_size_t, _vp]),
     "cp_ring_attention_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i, ctypes.c_uint]),
     "cp_ring_attention": (_i, [_vp, _i64p, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64p,
                                ctypes.POINTER(_i), _i, _i, _i, _i, _i, _i, ctypes.c_float, ctypes.c_uint,

@@ -100,8 +100,8 @@ cp_status_t check_kv(const void* k, const void* v, int Skv) {
 
 // One validated block: launches the attention (overwrite or accumulate) or the empty fill.
 cp_status_t run_block(const void* q, Strides qs, const void* k, const void* v, Strides kvs, int dtype,
-                      int B, int H, int D, int Sq, int Skv, float scale, bool accumulate, float* out,
-                      Strides os, float* lse, hipStream_t stream) {
+                      int B, int H, int D, int Sq, int Skv, float scale, bool accumulate, bool v_packed,
+                      float* out, Strides os, float* lse, hipStream_t stream) {
   if (Skv == 0) {
     if (accumulate) return CP_OK;
     return hip_status(cpattn::launch_fill_empty(out, os, lse, B, H, Sq, D, stream), "fill_empty");
@@ -113,6 +113,7 @@ cp_status_t run_block(const void* q, Strides qs, const void* k, const void* v, S
   a.scale = scale;
   a.accumulate = accumulate;
   a.waves = g_fwd_waves.load(std::memory_order_relaxed);
+  a.v_packed = v_packed;
   if (dtype == CP_BF16) return hip_status(cpattn::launch_attn_fwd_bf16(a, stream), "attn_fwd_bf16");
   return hip_status(cpattn::launch_attn_fwd_f32(a, stream), "attn_fwd_f32");
 }
@@ -131,6 +132,14 @@ int cp_abi_version(void) { return CP_ATTN_ABI_VERSION; }
 
 const char* cp_last_error(void) { return g_err.c_str(); }
 
+int cp_attn_fwd_waves(int B, int H, int D, int Sq) {
+  if (B <= 0 || H <= 0 || Sq <= 0 || (D != 64 && D != 128)) return 0;
+  cpattn::FwdArgs a{};
+  a.B = B; a.H = H; a.D = D; a.Sq = Sq;
+  a.waves = g_fwd_waves.load(std::memory_order_relaxed);
+  return cpattn::pick_waves(a);
+}
+
 int cp_attn_set_fwd_waves(int waves) {
   if (waves != 0 && waves != 4 && waves != 8) return -1;
   return g_fwd_waves.exchange(waves);
@@ -140,8 +149,11 @@ cp_status_t cp_attn_block_fwd(const void* q, const int64_t* q_strides, const voi
                               const int64_t* kv_strides, int dtype, int B, int H, int D, int Sq,
                               int Skv, float scale, unsigned flags, float* out,
                               const int64_t* out_strides, float* lse, void* stream) {
-  if (flags & ~CP_BLOCK_ACCUMULATE)
+  if (flags & ~(CP_BLOCK_ACCUMULATE | CP_BLOCK_PACKED_V))
     return fail(CP_ERR_INVALID_ARG, "cp_attn_block_fwd: unknown flags 0x%x", flags);
+  const bool packed = (flags & CP_BLOCK_PACKED_V) != 0;
+  if (packed && dtype != CP_BF16)
+    return fail(CP_ERR_UNSUPPORTED, "cp_attn_block_fwd: packed V is for CP_BF16 only");
   const Strides qs = resolve(q_strides, Sq, H, D);
   const Strides kvs = resolve(kv_strides, Skv, H, D);
   const Strides os = resolve(out_strides, Sq, H, D);
@@ -150,7 +162,7 @@ cp_status_t cp_attn_block_fwd(const void* q, const int64_t* q_strides, const voi
   if (B == 0 || H == 0 || Sq == 0) return CP_OK;
   if ((st = check_kv(k, v, Skv)) != CP_OK) return st;
   return run_block(q, qs, k, v, kvs, dtype, B, H, D, Sq, Skv, scale, (flags & CP_BLOCK_ACCUMULATE) != 0,
-                   out, os, lse, static_cast<hipStream_t>(stream));
+                   packed, out, os, lse, static_cast<hipStream_t>(stream));
 }
 
 cp_status_t cp_lse_merge(float* out_acc, float* lse_acc, const float* out_blk, const float* lse_blk,
@@ -179,6 +191,70 @@ cp_status_t cp_lse_merge(float* out_acc, float* lse_acc, const float* out_blk, c
                     "lse_merge");
 }
 
+size_t cp_attn_packed_v_bytes(int B, int H, int D, int Skv) {
+  if (B < 0 || H < 0 || Skv < 0 || (D != 64 && D != 128)) return 0;
+  return (size_t)cpattn::packed_v_bytes(B, H, D, Skv);
+}
+
+cp_status_t cp_attn_pack_v(const void* v, const int64_t* v_strides, int B, int H, int D, int Skv,
+                           void* packed, size_t packed_bytes, void* stream) {
+  if (D != 64 && D != 128)
+    return fail(CP_ERR_UNSUPPORTED, "cp_attn_pack_v: head dim D=%d is not supported (D = 64 or 128)", D);
+  if (B < 0 || H < 0 || Skv < 0)
+    return fail(CP_ERR_INVALID_ARG, "cp_attn_pack_v: sizes must be non-negative (B=%d H=%d Skv=%d)", B, H,
+                Skv);
+  if (B == 0 || H == 0 || Skv == 0) return CP_OK;
+  const size_t need = (size_t)cpattn::packed_v_bytes(B, H, D, Skv);
+  if (v == nullptr || packed == nullptr)
+    return fail(CP_ERR_INVALID_ARG, "cp_attn_pack_v: v and packed must be non-null");
+  if (packed_bytes < need)
+    return fail(CP_ERR_INVALID_ARG, "cp_attn_pack_v: packed buffer of %zu bytes needed, %zu given", need,
+                packed_bytes);
+  if (!aligned(v, 16) || !aligned(packed, 16))
+    return fail(CP_ERR_UNSUPPORTED, "cp_attn_pack_v: v and packed must be 16-byte aligned");
+  const Strides vs = resolve(v_strides, Skv, H, D);
+  cp_status_t st;
+  if ((st = check_strides("v", vs, 2, Skv, H, D)) != CP_OK) return st;
+  if ((int64_t)B * H * ((Skv + 63) / 64) > 0x7fffffff)
+    return fail(CP_ERR_UNSUPPORTED, "cp_attn_pack_v: B*H*ceil(Skv/64) must be below 2^31");
+  const char* src = static_cast<const char*>(v);
+  const char* dst = static_cast<const char*>(packed);
+  const int64_t v_end = ((B - 1) * vs.b + (int64_t)(Skv - 1) * vs.s + (H - 1) * vs.h + D) * 2;
+  if (dst < src + v_end && src < dst + need)
+    return fail(CP_ERR_INVALID_ARG, "cp_attn_pack_v: v and packed overlap");
+  return hip_status(cpattn::launch_pack_v(v, vs, packed, B, H, D, Skv, Skv, static_cast<hipStream_t>(stream)),
+                    "pack_v");
+}
+
+cp_status_t cp_ulysses_regroup_pack_v(const void* in, int B, int S_local, int H, int D, int degree,
+                                      void* packed, size_t packed_bytes, void* stream) {
+  const char* fn = "cp_ulysses_regroup_pack_v";
+  if (D != 64 && D != 128) return fail(CP_ERR_UNSUPPORTED, "%s: head dim D=%d is not supported (D = 64 or 128)", fn, D);
+  if (B < 0 || S_local < 0 || H < 0) return fail(CP_ERR_INVALID_ARG, "%s: sizes must be non-negative", fn);
+  if (degree < 1) return fail(CP_ERR_INVALID_ARG, "%s: degree must be >= 1 (got %d)", fn, degree);
+  if (H % degree != 0)
+    return fail(CP_ERR_INVALID_ARG, "%s: the number of heads H=%d must be divisible by the Ulysses degree %d", fn,
+                H, degree);
+  if ((int64_t)degree * S_local > 0x7fffffff) return fail(CP_ERR_UNSUPPORTED, "%s: degree*S_local too large", fn);
+  const int Hg = H / degree, S = degree * S_local;
+  if (B == 0 || S == 0 || Hg == 0) return CP_OK;
+  const size_t need = (size_t)cpattn::packed_v_bytes(B, Hg, D, S);
+  if (in == nullptr || packed == nullptr) return fail(CP_ERR_INVALID_ARG, "%s: pointers must be non-null", fn);
+  if (packed_bytes < need)
+    return fail(CP_ERR_INVALID_ARG, "%s: packed buffer of %zu bytes needed, %zu given", fn, need, packed_bytes);
+  if (!aligned(in, 16) || !aligned(packed, 16))
+    return fail(CP_ERR_UNSUPPORTED, "%s: in and packed must be 16-byte aligned", fn);
+  if ((int64_t)B * Hg * ((S + 63) / 64) > 0x7fffffff)
+    return fail(CP_ERR_UNSUPPORTED, "%s: B*(H/degree)*ceil(degree*S_local/64) must be below 2^31", fn);
+  const size_t in_bytes = (size_t)B * S_local * H * D * 2;
+  const char* a = static_cast<const char*>(in);
+  const char* b = static_cast<const char*>(packed);
+  if (b < a + in_bytes && a < b + need) return fail(CP_ERR_INVALID_ARG, "%s: in and packed overlap", fn);
+  const Strides is{(int64_t)S_local * H * D, (int64_t)H * D, (int64_t)D};
+  return hip_status(cpattn::launch_pack_v(in, is, packed, B, Hg, D, S, S_local, static_cast<hipStream_t>(stream)),
+                    "ulysses_regroup_pack_v");
+}
+
 size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned flags) {
   if (!(flags & CP_RING_SEPARATE_MERGE) || B <= 0 || H <= 0 || Sq <= 0 || D <= 0) return 0;
   return partial_bytes(B, H, Sq, D);
@@ -190,8 +266,11 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
                               int Sq, float scale, unsigned flags, float* out,
                               const int64_t* out_strides, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  if (flags & ~(CP_RING_ANYTHING | CP_RING_SEPARATE_MERGE))
+  if (flags & ~(CP_RING_ANYTHING | CP_RING_SEPARATE_MERGE | CP_RING_PACKED_V))
     return fail(CP_ERR_INVALID_ARG, "cp_ring_attention: unknown flags 0x%x", flags);
+  const bool packed = (flags & CP_RING_PACKED_V) != 0;
+  if (packed && dtype != CP_BF16)
+    return fail(CP_ERR_UNSUPPORTED, "cp_ring_attention: packed V is for CP_BF16 only");
   if (ring_degree < 1)
     return fail(CP_ERR_INVALID_ARG, "cp_ring_attention: ring_degree must be >= 1 (got %d)", ring_degree);
   if (!k_blocks || !v_blocks || !block_len)
@@ -242,17 +321,17 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
     if (block_len[i] == 0) continue;  // a block over no keys has weight 0 in the merge
     if (!have) {
       st = run_block(q, qs, k_blocks[i], v_blocks[i], kvs, dtype, B, H, D, Sq, block_len[i], scale, false,
-                     out, os, lse, s);
+                     packed, out, os, lse, s);
       have = true;
     } else if (separate) {
       st = run_block(q, qs, k_blocks[i], v_blocks[i], kvs, dtype, B, H, D, Sq, block_len[i], scale, false,
-                     ws_out, ws_s, ws_lse, s);
+                     packed, ws_out, ws_s, ws_lse, s);
       if (st == CP_OK)
         st = hip_status(cpattn::launch_lse_merge(out, lse, ws_out, ws_lse, os, ws_s, B, H, Sq, D, s),
                         "lse_merge");
     } else {
       st = run_block(q, qs, k_blocks[i], v_blocks[i], kvs, dtype, B, H, D, Sq, block_len[i], scale, true,
-                     out, os, lse, s);
+                     packed, out, os, lse, s);
     }
     if (st != CP_OK) return st;
   }

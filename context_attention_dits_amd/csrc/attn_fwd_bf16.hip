@@ -52,6 +52,11 @@
 //       only), separated by workgroup barriers, so each SIMD overlaps one
 //       wave's softmax with the other wave's MFMAs. Three LDS stages of K,
 //       raw V and V^T in fragment order (read with ds_read_b128).
+//   * Packed V (PACKED): V may arrive already rewritten by pack_v_kernel
+//     into the LDS image of its V^T fragments; tiles are then loaded with
+//     contiguous 1 KB DMA loads and need no transposition (the ping-pong
+//     kernel keeps no raw V stages). Same operands, same order: the results
+//     are bit-identical to unpacked V.
 //   * Workgroups are remapped so that consecutive query tiles of one head run
 //     on the same XCD (each XCD has its own L2) and share its K/V reads.
 //   * Keys beyond Skv are never read: the buffer descriptor's range ends at
@@ -186,20 +191,25 @@ struct Nothing {
   __device__ __forceinline__ void operator()(A...) const {}
 };
 
-template <int D, int QB, int NW, bool ACC>
+template <int D, int QB, int NW, bool ACC, bool PACKED>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                                amdgpu_waves_per_eu(CP_FWD_WPE)))
 attn_fwd_bf16_kernel(Params p) {
   using C = Cfg<D, QB, NW>;
+  // PACKED: p.v is V already in the tile / fragment order that the PV
+  // products read (pack_v_kernel), so V tiles need no transposition here.
   // Separate arrays per buffer, so the compiler can tell the buffers being
   // read from the ones the next tiles are being loaded into.
+  // vbuf*: raw V tiles (4 waves: V tiles as loaded, raw or packed; ping-pong:
+  // raw V awaiting transposition, none when PACKED).
+  constexpr int RAW_V = (C::PINGPONG && PACKED) ? 16 : C::V_BYTES;
   __shared__ __attribute__((aligned(1024))) char kbuf0[C::K_BYTES];
   __shared__ __attribute__((aligned(1024))) char kbuf1[C::K_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vbuf0[C::V_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[C::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[RAW_V];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[RAW_V];
   // ping-pong only: third stage, and V^T in MFMA fragment order (three stages)
   __shared__ __attribute__((aligned(1024))) char kbuf2[C::NBUF > 2 ? C::K_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char vbuf2[C::NBUF > 2 ? C::V_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char vbuf2[C::NBUF > 2 ? RAW_V : 16];
   __shared__ __attribute__((aligned(1024))) char vtb0[C::NBUF > 2 ? C::V_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char vtb1[C::NBUF > 2 ? C::V_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char vtb2[C::NBUF > 2 ? C::V_BYTES : 16];
@@ -215,8 +225,6 @@ attn_fwd_bf16_kernel(Params p) {
   const int h = bh % p.H, b = bh / p.H;
   const int qrow0 = qt * C::BM + wave * (QB * 32);
 
-  const uint16_t* kbase = p.k + b * p.kv_sb + h * p.kv_sh;
-  const uint16_t* vbase = p.v + b * p.kv_sb + h * p.kv_sh;
   // Kernel arguments used inside the tile loop, pinned in SGPRs: reloading
   // them from the argument segment there would make the next LDS wait also
   // wait for that scalar load.
@@ -224,6 +232,11 @@ attn_fwd_bf16_kernel(Params p) {
   float csc = p.c;
   asm volatile("" : "+s"(skv), "+s"(csc));
   const int n_tiles = (skv + C::BN - 1) / C::BN;
+
+  const uint16_t* kbase = p.k + b * p.kv_sb + h * p.kv_sh;
+  // packed V: n_tiles contiguous tiles of V_BYTES per (b, h), (b, h) in order
+  const uint16_t* vbase = PACKED ? p.v + (int64_t)bh * n_tiles * (C::V_BYTES / 2)
+                                 : p.v + b * p.kv_sb + h * p.kv_sh;
 
   // ---- Q (B operand of S^T = K Q^T): lane holds query l32, dims kk*16 + hi*8 .. +7
   bf16x8 qf[QB][C::KK];
@@ -282,11 +295,18 @@ attn_fwd_bf16_kernel(Params p) {
   auto issue_v = [&](int t, char* Vs) {
     const uint16_t* base;
     int nbytes;
-    tile_range(t, vbase, base, nbytes);
+    if constexpr (PACKED) {
+      // a packed tile is one contiguous V_BYTES block, its 1 KB fragments in
+      // LDS order; past the last tile the range is empty
+      base = vbase + (int64_t)min(t, n_tiles - 1) * (C::V_BYTES / 2);
+      nbytes = t < n_tiles ? C::V_BYTES : 0;
+    } else {
+      tile_range(t, vbase, base, nbytes);
+    }
 #pragma unroll
     for (int i = 0; i < C::V_PER_WAVE; ++i) {
       const int m = lw * C::V_PER_WAVE + i;
-      buffer_to_lds16(base, nbytes, v_voff[i], Vs + m * 1024);
+      buffer_to_lds16(base, nbytes, PACKED ? m * 1024 + lane * 16 : v_voff[i], Vs + m * 1024);
     }
   };
 
@@ -437,6 +457,32 @@ attn_fwd_bf16_kernel(Params p) {
   // Second half: O^T += V^T P^T with the V tile in v_read (V^T fragments via
   // transposing LDS reads).
   auto half_b = [&](const char* v_read) {
+    if constexpr (PACKED) {
+      // V^T fragments as packed: one ds_read_b128 each (fragment order below)
+      const char* vfrag = v_read + lane * 16;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int kk2 = 0; kk2 < 2; ++kk2) {
+            const int f = (db * C::KB + kb) * 2 + kk2;
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(vfrag + f * 1024);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][kk2], o[qb][db], 0, 0, 0);
+          }
+#if CP_FWD_SCHED_PV
+      // keep four fragments ahead of the MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < (D / 32) * C::KB * 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#endif
+      return;
+    }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const char* vb = v_read + (vlane ^ (db << 6));
@@ -609,20 +655,30 @@ attn_fwd_bf16_kernel(Params p) {
     // loads at the end of its MFMA half in 2j+2. Every barrier waits for the
     // wave's LDS accesses, so a transposed tile is complete one interval
     // after the second group wrote its share.
+    // With packed V there is no raw V and no transposition: V_{j+1}^T is
+    // loaded straight into its stage during the softmax of tile j, with
+    // K_{j+2}. Its stage last held V_{j-2}^T, read in interval 2j-2 at the
+    // latest, and it is first read in interval 2j+3, after the same waits as
+    // K_{j+2}.
     using PendL = std::integral_constant<int, C::K_PER_WAVE + C::V_PER_WAVE>;
     const bool grp_b = wave >= NW / 2;
     char* const kb3[3] = {kbuf0, kbuf1, kbuf2};
     char* const vb3[3] = {vbuf0, vbuf1, vbuf2};
     char* const vt3[3] = {vtb0, vtb1, vtb2};
-    // prologue: K_0, K_1 and raw V_0..V_2 loaded, V_0^T built, scores of tile 0
+    // prologue: K_0, K_1 and raw V_0..V_2 loaded, V_0^T built (packed: K_0,
+    // K_1 and V_0^T loaded), scores of tile 0
     issue_k(0, kbuf0);
     issue_k(1, kbuf1);
-    issue_v(0, vbuf0);
-    issue_v(1, vbuf1);
-    issue_v(2, vbuf2);
-    sync(Pend0{});
-    scores(kbuf0, sa);
-    {
+    if constexpr (PACKED) {
+      issue_v(0, vtb0);
+      sync(Pend0{});
+      scores(kbuf0, sa);
+    } else {
+      issue_v(0, vbuf0);
+      issue_v(1, vbuf1);
+      issue_v(2, vbuf2);
+      sync(Pend0{});
+      scores(kbuf0, sa);
       i16x8 fr[VT_PER_WAVE];
       read_vt(vbuf0, fr);
       write_vt(vtb0, fr);
@@ -635,17 +691,27 @@ attn_fwd_bf16_kernel(Params p) {
       const char* k_read = kb3[(c + 1) % 3];
       const char* vt_read = vt3[c];
       if constexpr (!LAST) {
-        i16x8 fr[VT_PER_WAVE];
-        half_a(
-            last_tag, Split{}, jj, sa, sa, k_read,
-            [&] {
-              issue_k(jj + 2, kb3[(c + 2) % 3]);
-              issue_v(jj + 3, vb3[c]);
-              read_vt(vb3[(c + 1) % 3], fr);
-            },
-            [&](int g) {
-              if (g == 0) write_vt(vt3[(c + 1) % 3], fr);
-            });
+        if constexpr (PACKED) {
+          half_a(
+              last_tag, Split{}, jj, sa, sa, k_read,
+              [&] {
+                issue_k(jj + 2, kb3[(c + 2) % 3]);
+                issue_v(jj + 1, vt3[(c + 1) % 3]);
+              },
+              Nothing{});
+        } else {
+          i16x8 fr[VT_PER_WAVE];
+          half_a(
+              last_tag, Split{}, jj, sa, sa, k_read,
+              [&] {
+                issue_k(jj + 2, kb3[(c + 2) % 3]);
+                issue_v(jj + 3, vb3[c]);
+                read_vt(vb3[(c + 1) % 3], fr);
+              },
+              [&](int g) {
+                if (g == 0) write_vt(vt3[(c + 1) % 3], fr);
+              });
+        }
         if (grp_b) sync(PendAll{});
         else sync(PendL{});
         half_m(last_tag, sa, k_read, vt_read);
@@ -722,7 +788,7 @@ attn_fwd_bf16_kernel(Params p) {
   }
 }
 
-template <int D, int NW, bool ACC>
+template <int D, int NW, bool ACC, bool PACKED>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   constexpr int QB = CP_FWD_QB;
   using C = Cfg<D, QB, NW>;
@@ -741,11 +807,108 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
   p.n_wg = (int)n_wg;
   p.c = a.scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, NW, ACC>), dim3(p.n_wg), dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, NW, ACC, PACKED>), dim3(p.n_wg), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
+template <int D, int NW>
+hipError_t launch_dw(const FwdArgs& a, hipStream_t stream) {
+  if (a.v_packed)
+    return a.accumulate ? launch_d<D, NW, true, true>(a, stream) : launch_d<D, NW, false, true>(a, stream);
+  return a.accumulate ? launch_d<D, NW, true, false>(a, stream) : launch_d<D, NW, false, false>(a, stream);
+}
+
+// V of one block in the order the PV products read it, for the kernel above
+// with PACKED: per (b, h), in (b, h) order, ceil(Skv / 64) tiles of 64 keys,
+// each D * 128 bytes: fragment f = (db * 2 + kb) * 2 + kk2 (db: 32 dims, kb:
+// 32 keys, kk2: 16 keys) is 1 KB in which lane l (l32 = l % 32, hi = l / 32)
+// has 8 values, element e being V[key][d] for d = 32 db + l32 and
+// key = 64 t + 32 kb + 16 kk2 + 8 (e / 4) + 4 hi + e % 4 -- the key order in
+// which the score accumulators hold the probabilities. Keys >= Skv are zero.
+// One workgroup per tile: the tile goes through LDS as rows (padded by 16
+// bytes, so that the two 32-lane halves of a gather, 4 keys apart, fall on
+// different banks), then each thread gathers whole 16-byte lanes.
+// Key `key` of head h is read at v + b sb + s ss + (g hg + h) sh with
+// g = key / piece, s = key % piece: piece = Skv for a plain V; for the
+// Ulysses regroup fused in, V is the regrouped [B, P * S_local, H / P, D]
+// read from the sequence-sharded [B, S_local, H, D] (piece = S_local, hg = H / P).
+template <int D>
+__global__ void __launch_bounds__(256) pack_v_kernel(const uint16_t* __restrict__ v, int64_t sb, int64_t ss,
+                                                     int64_t sh, uint16_t* __restrict__ out, int H, int Skv,
+                                                     int n_tiles, uint32_t piece, int hg) {
+  constexpr int RS = D + 8;            // LDS row stride, elements
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int NF = (D / 32) * 4;     // fragments per tile
+  constexpr int NLD = 64 * CPR / 256;  // 16-byte loads per thread
+  constexpr int NST = NF * 64 / 256;   // 16-byte stores per thread
+  __shared__ __attribute__((aligned(16))) uint16_t rows[64 * RS];
+  const int wg = blockIdx.x;
+  const int t = wg % n_tiles, bh = wg / n_tiles;
+  const int h = bh % H, b = bh / H;
+  const uint16_t* src = v + b * sb + h * sh;
+  // every load in flight before the first LDS store
+  uint4 x[NLD];
+#pragma unroll
+  for (int it = 0; it < NLD; ++it) {
+    const int i = threadIdx.x + it * 256;
+    const int key = t * 64 + i / CPR;
+    // rows past Skv load the last row (no branch around the load) and are zeroed
+    const uint32_t kc = (uint32_t)min(key, Skv - 1);
+    const uint32_t g = kc / piece, sk = kc - g * piece;
+    const uint4 y = *reinterpret_cast<const uint4*>(src + (int64_t)sk * ss + (int64_t)(g * hg) * sh + (i % CPR) * 8);
+    const bool in = key < Skv;
+    x[it] = make_uint4(in ? y.x : 0u, in ? y.y : 0u, in ? y.z : 0u, in ? y.w : 0u);
+  }
+#pragma unroll
+  for (int it = 0; it < NLD; ++it) {
+    const int i = threadIdx.x + it * 256;
+    *reinterpret_cast<uint4*>(rows + (i / CPR) * RS + (i % CPR) * 8) = x[it];
+  }
+  __syncthreads();
+  uint16_t* dst = out + ((int64_t)bh * n_tiles + t) * (NF * 512);
+#pragma unroll
+  for (int it = 0; it < NST; ++it) {
+    const int i = threadIdx.x + it * 256;
+    const int f = i / 64, l = i % 64;
+    const int db = f / 4, kb = (f / 2) % 2, kk2 = f % 2;
+    const int d = db * 32 + (l & 31), k0 = kb * 32 + kk2 * 16 + 4 * (l >> 5);
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = rows[(k0 + 8 * (j >> 2) + (j & 3)) * RS + d];
+    uint4 y;
+    y.x = e[0] | ((uint32_t)e[1] << 16);
+    y.y = e[2] | ((uint32_t)e[3] << 16);
+    y.z = e[4] | ((uint32_t)e[5] << 16);
+    y.w = e[6] | ((uint32_t)e[7] << 16);
+    *reinterpret_cast<uint4*>(dst + i * 8) = y;
+  }
+}
+
 }  // namespace
+
+int64_t packed_v_bytes(int B, int H, int D, int Skv) {
+  return (int64_t)B * H * ((Skv + 63) / 64) * 64 * D * 2;
+}
+
+hipError_t launch_pack_v(const void* v, Strides vs, void* packed, int B, int H, int D, int Skv, int piece,
+                         hipStream_t stream) {
+  const int n_tiles = (Skv + 63) / 64;
+  const int64_t n_wg = (int64_t)B * H * n_tiles;
+  if (n_wg == 0) return hipSuccess;
+  if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const uint16_t* src = static_cast<const uint16_t*>(v);
+  uint16_t* dst = static_cast<uint16_t*>(packed);
+  if (piece <= 0 || Skv % piece) return hipErrorInvalidValue;
+  if (D == 128)
+    hipLaunchKernelGGL(pack_v_kernel<128>, dim3((int)n_wg), dim3(256), 0, stream, src, vs.b, vs.s, vs.h, dst, H,
+                       Skv, n_tiles, (uint32_t)piece, H);
+  else if (D == 64)
+    hipLaunchKernelGGL(pack_v_kernel<64>, dim3((int)n_wg), dim3(256), 0, stream, src, vs.b, vs.s, vs.h, dst, H,
+                       Skv, n_tiles, (uint32_t)piece, H);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 // Workgroup shape for one launch. The ping-pong kernel (8 waves, 256 query
 // rows, one workgroup per CU) is the faster one per workgroup; the 4-wave
@@ -766,10 +929,9 @@ int pick_waves(const FwdArgs& a) {
 template <int D>
 hipError_t launch_dn(const FwdArgs& a, hipStream_t stream) {
   if constexpr (D == 128) {
-    if (pick_waves(a) == 8)
-      return a.accumulate ? launch_d<D, 8, true>(a, stream) : launch_d<D, 8, false>(a, stream);
+    if (pick_waves(a) == 8) return launch_dw<D, 8>(a, stream);
   }
-  return a.accumulate ? launch_d<D, 4, true>(a, stream) : launch_d<D, 4, false>(a, stream);
+  return launch_dw<D, 4>(a, stream);
 }
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {

@@ -45,7 +45,19 @@ struct FwdArgs {
   float scale;
   bool accumulate;  // merge into (out, lse) instead of overwriting
   int waves;        // bf16 workgroup shape: 4, 8, or 0 to choose per launch
+  bool v_packed;    // bf16: v is the output of launch_pack_v for this block (kvs is K's)
 };
+
+// V of one bf16 block rewritten in the tile / fragment order that the
+// attention kernel reads with v_packed (ceil(Skv / 64) * 64 keys per (b, h),
+// zeros past Skv); packed_v_bytes is its size. Keys come in Skv / piece
+// pieces: key j of head h is read at (j % piece) * vs.s + ((j / piece) * H
+// + h) * vs.h -- piece = Skv for a plain [B, Skv, H, D] tensor; for the
+// Ulysses regroup fused in, vs describes the sequence-sharded tensor, H is
+// the group's head count and piece = S_local.
+int64_t packed_v_bytes(int B, int H, int D, int Skv);
+hipError_t launch_pack_v(const void* v, Strides vs, void* packed, int B, int H, int D, int Skv, int piece,
+                         hipStream_t stream);
 
 // Backward of one ring block (bf16 inputs): dQ (+)= scale dS K, dK = scale dS^T Q,
 // dV = P^T dO with P from the global LSE and dS = P (dO V^T - delta).
@@ -71,6 +83,8 @@ hipError_t launch_attn_bwd_prep(const float* out, Strides os, const float* dout,
 
 // Partial attention of Q against one K/V block (Skv >= 1), float32 out + LSE.
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+// Workgroup shape (waves: 4, or 8 for the ping-pong kernel) the bf16 launch uses for a.
+int pick_waves(const FwdArgs& a);
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
 // out = 0, lse = -inf for every (b, s, h): attention over an empty key set.

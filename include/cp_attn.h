@@ -61,11 +61,16 @@ typedef enum cp_dtype { CP_F32 = 0, CP_BF16 = 1 } cp_dtype_t;
 
 /* cp_attn_block_fwd flag: merge this block into (out, lse) instead of overwriting them. */
 #define CP_BLOCK_ACCUMULATE 0x1u
+/* cp_attn_block_fwd flag: v is this block's V as written by cp_attn_pack_v (CP_BF16 only). */
+#define CP_BLOCK_PACKED_V 0x2u
 /* cp_ring_attention flag: allow unequal block lengths, zero included ([CP] Ring Anything). */
 #define CP_RING_ANYTHING 0x2u
 /* cp_ring_attention flag: write each block's partial into the workspace and merge it with
  * a separate cp_lse_merge pass, instead of merging inside the attention kernel. */
 #define CP_RING_SEPARATE_MERGE 0x4u
+/* cp_ring_attention flag: every v_blocks[i] is block i's V as written by cp_attn_pack_v
+ * (CP_BF16 only). */
+#define CP_RING_PACKED_V 0x8u
 
 /* cp_attn_block_bwd flag: add this block's dQ to dq instead of overwriting it. */
 #define CP_BWD_ACCUMULATE_DQ 0x1u
@@ -94,10 +99,14 @@ typedef enum cp_dtype { CP_F32 = 0, CP_BF16 = 1 } cp_dtype_t;
  *   out  [B, Sq, H, D]  float32, strides out_strides
  *   lse  [B, H, Sq]     float32, contiguous
  *   scale  > 0 and finite (the usual choice is 1/sqrt(D))
- *   flags  0 or CP_BLOCK_ACCUMULATE. With CP_BLOCK_ACCUMULATE, (out, lse)
- *          must already hold a partial result of the same queries over
- *          other keys; they are updated in place to the merge of that
- *          partial with this block (the cp_lse_merge formula).
+ *   flags  0, CP_BLOCK_ACCUMULATE, CP_BLOCK_PACKED_V or both. With
+ *          CP_BLOCK_ACCUMULATE, (out, lse) must already hold a partial result
+ *          of the same queries over other keys; they are updated in place to
+ *          the merge of that partial with this block (the cp_lse_merge
+ *          formula). With CP_BLOCK_PACKED_V (CP_BF16 only), v is the output
+ *          of cp_attn_pack_v for this block's V (same B, H, D, Skv; the
+ *          library cannot check its size) and kv_strides describe K only;
+ *          the result is bit-identical to passing the unpacked V.
  *
  * Skv == 0 is allowed: without CP_BLOCK_ACCUMULATE it writes out = 0 and
  * lse = -inf (attention over no keys); with it, it leaves (out, lse) as they
@@ -158,6 +167,8 @@ size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned fl
  *                       >= 1 (plain ring attention needs the sequence to
  *                       divide evenly by ring_degree).
  *                       CP_RING_SEPARATE_MERGE: see above; needs workspace.
+ *                       CP_RING_PACKED_V: v_blocks[i] is the output of
+ *                       cp_attn_pack_v for block i (as CP_BLOCK_PACKED_V).
  *   out, lse            as cp_attn_block_fwd; overwritten.
  *   workspace           device buffer of workspace_bytes (may be NULL when
  *                       cp_ring_attention_workspace_size() returns 0)
@@ -169,6 +180,50 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides,
                               int dtype, int B, int H, int D, int Sq, float scale, unsigned flags,
                               float* out, const int64_t* out_strides, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * cp_attn_packed_v_bytes, cp_attn_pack_v -- V of one K/V block, rewritten in
+ * the order the bf16 attention kernel's PV products read it.
+ *
+ * Not an operation of the pages: a layout change of the V operand of the
+ * block attention above ([CP] "Atencao em Anel"), so that the kernel loads V
+ * tiles straight into on-chip memory instead of transposing them on every
+ * compute unit. In a ring, a rank would pack its own V block once and every
+ * other rank would receive it packed; a block that is read by several
+ * launches is packed once.
+ *
+ *   v       [B, Skv, H, D] bf16, strides v_strides (NULL = contiguous),
+ *           16-byte aligned rows
+ *   packed  device buffer of packed_bytes >= cp_attn_packed_v_bytes(B, H, D,
+ *           Skv) = B * H * ceil(Skv / 64) * 64 * D * 2 bytes, 16-byte aligned,
+ *           not overlapping v. Layout (the kernel's, opaque to callers): per
+ *           (b, h) in (b, h) order, ceil(Skv / 64) tiles of 64 keys, each D/8
+ *           fragments of 1 KB; fragment 4 db + 2 kb + kk2 of tile t holds, for
+ *           lane l (l32 = l % 32, hi = l / 32) and element e < 8 (16 bytes per
+ *           lane), V[b, key, h, 32 db + l32] with key = 64 t + 32 kb + 16 kk2
+ *           + 8 (e / 4) + 4 hi + e % 4; keys >= Skv are 0.
+ * D must be 64 or 128 (cp_attn_packed_v_bytes returns 0 otherwise);
+ * B*H*ceil(Skv/64) must be below 2^31. Sizes of 0 enqueue nothing.
+ */
+size_t cp_attn_packed_v_bytes(int B, int H, int D, int Skv);
+cp_status_t cp_attn_pack_v(const void* v, const int64_t* v_strides, int B, int H, int D, int Skv,
+                           void* packed, size_t packed_bytes, void* stream);
+
+/*
+ * cp_ulysses_regroup_pack_v -- the Ulysses regroup of V and its packing in one pass.
+ *
+ * Writes into `packed` exactly what cp_ulysses_regroup(in, tmp, 2, B, S_local,
+ * H, D, degree, CP_REGROUP_SEQ_TO_HEAD) followed by cp_attn_pack_v(tmp, NULL,
+ * B, H / degree, D, degree * S_local, packed, ...) would, without the
+ * intermediate tensor: [CP] "Atencao Ulysses" -- after the first all-to-all a
+ * rank holds V of every token for its head group, which its attention then
+ * reads. in is the sequence-sharded V [B, S_local, H, D] bf16, contiguous,
+ * 16-byte aligned; degree >= 1 divides H; packed holds at least
+ * cp_attn_packed_v_bytes(B, H / degree, D, degree * S_local) bytes, 16-byte
+ * aligned, not overlapping in. D must be 64 or 128.
+ */
+cp_status_t cp_ulysses_regroup_pack_v(const void* in, int B, int S_local, int H, int D, int degree,
+                                      void* packed, size_t packed_bytes, void* stream);
 
 /*
  * cp_ulysses_regroup -- the Ulysses all-to-all's local permutation, loopback.
@@ -317,6 +372,13 @@ cp_status_t cp_ring_attention_bwd(const void* q, const int64_t* q_strides, const
  * previous setting; any other value is rejected with -1 and the setting is
  * left unchanged. Launches already enqueued are not affected. */
 int cp_attn_set_fwd_waves(int waves);
+
+/* The workgroup shape (4 or 8, as above) the bfloat16 block kernel will use
+ * for these sizes under the current setting; 0 if B, H or Sq is not positive
+ * or D is not 64 or 128. V packed by cp_attn_pack_v speeds up the 8-wave
+ * shape only (the 4-wave kernel reads V at the same speed either way), so a
+ * caller that has to pack V itself can skip it when this returns 4. */
+int cp_attn_fwd_waves(int B, int H, int D, int Sq);
 
 /* Message for the last non-CP_OK status returned on the calling thread ("" if none). */
 const char* cp_last_error(void);

@@ -259,3 +259,64 @@ def test_binding_refuses_host_tensors():
         cp.cp_attn_block_fwd(q, q, q, out, lse)
     with pytest.raises(ValueError, match="GPU"):
         cp.cp_ulysses_regroup(q, q.clone(), 2)
+
+
+def test_packed_v_size_and_rejects(lib):
+    """cp_attn_pack_v and the packed-V flags: every rejection happens on the host."""
+    assert lib.cp_attn_packed_v_bytes(1, 24, 128, 2304) == 24 * 36 * 64 * 128 * 2
+    assert lib.cp_attn_packed_v_bytes(2, 3, 64, 65) == 2 * 3 * 2 * 64 * 64 * 2  # padded to 64 keys
+    assert lib.cp_attn_packed_v_bytes(1, 2, 96, 8) == 0  # unsupported D
+    assert lib.cp_attn_packed_v_bytes(1, 2, 128, 0) == 0
+    need = lib.cp_attn_packed_v_bytes(1, 2, 128, 8)
+    big = FAKE + (1 << 30)
+    f = lib.cp_attn_pack_v
+    assert f(FAKE, None, 1, 2, 96, 8, big, need, None) == _lib.CP_ERR_UNSUPPORTED
+    assert f(FAKE, None, 1, -2, 128, 8, big, need, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(FAKE, None, 1, 2, 128, 8, big, need - 1, None) == _lib.CP_ERR_INVALID_ARG
+    assert "needed" in _err(lib)
+    assert f(0, None, 1, 2, 128, 8, big, need, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(FAKE + 8, None, 1, 2, 128, 8, big, need, None) == _lib.CP_ERR_UNSUPPORTED
+    assert f(FAKE, None, 1, 2, 128, 8, FAKE + 64, need, None) == _lib.CP_ERR_INVALID_ARG  # overlap
+    assert "overlap" in _err(lib)
+    bad = (ctypes.c_int64 * 3)(8 * 2 * 128, 2 * 128 + 1, 128)  # row stride not 16-byte aligned
+    assert f(FAKE, bad, 1, 2, 128, 8, big, need, None) == _lib.CP_ERR_UNSUPPORTED
+    assert f(FAKE, None, 1, 2, 128, 0, 0, 0, None) == _lib.CP_OK  # nothing to pack
+    # packed V is bf16 only, on both attention entry points
+    assert _block(lib, dtype=0, flags=_lib.CP_BLOCK_PACKED_V) == _lib.CP_ERR_UNSUPPORTED
+    assert "packed" in _err(lib)
+    assert _block(lib, flags=0x4) == _lib.CP_ERR_INVALID_ARG
+    assert _ring(lib, [8, 8], dtype=0, flags=_lib.CP_RING_PACKED_V) == _lib.CP_ERR_UNSUPPORTED
+    assert _ring(lib, [8, 8], flags=0x10) == _lib.CP_ERR_INVALID_ARG
+
+
+def test_regroup_pack_v_rejects(lib):
+    f = lib.cp_ulysses_regroup_pack_v
+    big = FAKE + (1 << 30)
+    need = lib.cp_attn_packed_v_bytes(1, 12, 128, 2 * 16)
+    assert f(FAKE, 1, 16, 24, 96, 2, big, need, None) == _lib.CP_ERR_UNSUPPORTED  # D
+    assert f(FAKE, 1, 16, 24, 128, 5, big, need, None) == _lib.CP_ERR_INVALID_ARG  # 5 does not divide 24
+    assert "divisible" in _err(lib)
+    assert f(FAKE, 1, 16, 24, 128, 0, big, need, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(FAKE, 1, 16, 24, 128, 2, big, need - 1, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(FAKE + 8, 1, 16, 24, 128, 2, big, need, None) == _lib.CP_ERR_UNSUPPORTED
+    assert f(FAKE, 1, 16, 24, 128, 2, FAKE + 1024, need, None) == _lib.CP_ERR_INVALID_ARG  # overlap
+    assert f(0, 1, 16, 24, 128, 2, big, need, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(FAKE, 1, 0, 24, 128, 2, 0, 0, None) == _lib.CP_OK  # nothing to do
+
+
+def test_fwd_waves_query(lib):
+    """The bf16 kernel's workgroup shape for the benchmark shapes, and its knob."""
+    q = lib.cp_attn_fwd_waves
+    assert lib.cp_attn_set_fwd_waves(0) in (0, 4, 8)
+    assert q(1, 24, 128, 2304) == 8   # 216 ping-pong workgroups: one round, mostly full
+    assert q(1, 12, 128, 4608) == 8
+    assert q(1, 24, 128, 8192) == 8
+    assert q(2, 24, 128, 1536) == 4   # 288: the second round would be nearly empty
+    assert q(1, 12, 128, 2304) == 4   # 108: under half a round
+    assert q(1, 24, 64, 8192) == 4    # D = 64 has the 4-wave kernel only
+    assert q(0, 24, 128, 2304) == 0 and q(1, 24, 96, 2304) == 0
+    prev = lib.cp_attn_set_fwd_waves(8)
+    try:
+        assert q(1, 12, 128, 2304) == 8 and q(1, 24, 64, 8192) == 4
+    finally:
+        lib.cp_attn_set_fwd_waves(prev)

@@ -1,0 +1,210 @@
+"""GPU tests of packed V: cp_attn_pack_v's layout, and attention over packed V blocks.
+
+The packed layout is checked element by element against the definition in the
+header, rebuilt here with numpy index arithmetic. Attention over packed V feeds
+the matrix cores the same operands in the same order as attention over the
+unpacked V, so the two must agree bit for bit; at the benchmark's full sizes the
+packed ring is also compared with the float64 oracle on sampled rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import SHAPES, TOL, assert_close, dev, fwd_waves, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def cp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import context_attention_dits_amd as m
+    m.load()  # raises if the HIP library is missing: no fallback
+    return m
+
+
+def _packed_reference(v_bits):
+    """The packed layout of uint16 V [B, Skv, H, D] as the header defines it: per (b, h), tiles
+    of 64 keys; fragment f = 4 db + 2 kb + kk2 of 64 lanes x 8 elements; lane l, element e
+    holds V[key][32 db + l % 32] with key = 64 t + 32 kb + 16 kk2 + 8 (e // 4) + 4 (l // 32)
+    + e % 4, and 0 past Skv."""
+    B, Skv, H, D = v_bits.shape
+    T = -(-Skv // 64)
+    padded = np.zeros((B, H, T * 64, D), dtype=np.uint16)
+    padded[:, :, :Skv] = v_bits.transpose(0, 2, 1, 3)
+    out = np.empty((B, H, T, D // 32, 2, 2, 64, 8), dtype=np.uint16)
+    lane = np.arange(64)[:, None]
+    e = np.arange(8)[None, :]
+    for db in range(D // 32):
+        for kb in range(2):
+            for kk2 in range(2):
+                key = 32 * kb + 16 * kk2 + 8 * (e // 4) + 4 * (lane // 32) + e % 4  # [64, 8]
+                d = 32 * db + lane % 32 + 0 * e
+                for t in range(T):
+                    out[:, :, t, db, kb, kk2] = padded[:, :, 64 * t + key, d]  # [B, H, 64, 8]
+    return out.reshape(-1)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("B,Skv,H,D,strided", [(1, 2304, 3, 128, False), (2, 100, 3, 128, True),
+                                                (2, 129, 2, 64, False), (1, 1, 2, 128, False),
+                                                (1, 64, 5, 64, True)])
+def test_pack_v_layout(cp, B, Skv, H, D, strided):
+    say("pack_v layout", B, Skv, H, D, "strided" if strided else "contiguous")
+    inp = workloads.make_custom(B, H, D, 1, (Skv,), "bf16", seed=40 + Skv)
+    v = dev(inp.v, "bf16")
+    if strided:  # a view with gaps between heads and between rows
+        big = torch.full((B, Skv, H + 2, D + 8), float("nan"), dtype=torch.bfloat16, device="cuda")
+        big[:, :, 1:H + 1, :D] = v
+        v = big[:, :, 1:H + 1, :D]
+    nbytes = cp.cp_attn_packed_v_bytes(B, H, D, Skv)
+    assert nbytes == B * H * (-(-Skv // 64)) * 64 * D * 2
+    buf = torch.full((nbytes // 2 + 64,), -1, dtype=torch.int16, device="cuda")  # with a guard tail
+    cp.cp_attn_pack_v(v, buf)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy().view(np.uint16)
+    want = _packed_reference(_bits(dev(inp.v, "bf16")).reshape(B, Skv, H, D))
+    assert np.array_equal(got[:nbytes // 2], want), "packed layout differs from its definition"
+    assert np.all(got[nbytes // 2:] == 0xFFFF), "cp_attn_pack_v wrote past its output"
+
+
+def _block_pair(cp, q, k, v, pv, scale, acc_from=None):
+    """(out, lse) of one block with unpacked and with packed V; with acc_from, both start from that
+    partial and merge the block in."""
+    res = []
+    for vv in (v, pv):
+        if acc_from is None:
+            out = torch.empty((q.shape[0], q.shape[1], q.shape[2], q.shape[3]), device="cuda")
+            lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), device="cuda")
+            flags = 0
+        else:
+            out, lse = acc_from[0].clone(), acc_from[1].clone()
+            flags = cp.CP_BLOCK_ACCUMULATE
+        cp.cp_attn_block_fwd(q, k, vv, out, lse, scale=scale, flags=flags)
+        res.append((out, lse))
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("waves", SHAPES)
+@pytest.mark.parametrize("D", [128, 64])
+def test_packed_matches_unpacked_bitwise(cp, waves, D):
+    """Every pipeline length from one partial tile up, both workgroup shapes, overwrite and merge."""
+    B, H, Sq = 1, 4, 300
+    with fwd_waves(cp, waves):
+        for Skv in (1, 63, 64, 100, 128, 129, 192, 257, 1000):
+            for seed in range(2):
+                say(f"packed vs unpacked waves={waves} D={D} Skv={Skv} seed={seed}")
+                inp = workloads.make_custom(B, H, D, Sq, (Skv, 77), "bf16", seed=500 + 7 * Skv + seed)
+                q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+                kb, vb = k[:, :Skv], v[:, :Skv]
+                pv = cp.pack_v(vb)
+                (o0, l0), (o1, l1) = _block_pair(cp, q, kb, vb, pv, inp.workload.scale)
+                assert torch.equal(o0, o1) and torch.equal(l0, l1), "overwrite: packed differs"
+                # merge the block into a partial over the other 77 keys
+                base = cp.ring_attention(q, [k[:, Skv:]], [v[:, Skv:]], scale=inp.workload.scale)
+                (o0, l0), (o1, l1) = _block_pair(cp, q, kb, vb, pv, inp.workload.scale, acc_from=base)
+                assert torch.equal(o0, o1) and torch.equal(l0, l1), "accumulate: packed differs"
+                if Skv in (129, 1000) and seed == 0:
+                    o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.workload.scale)
+                    assert_close("out", o1.cpu().numpy(), o_ref, TOL["bf16"]["o"])
+                    assert_close("lse", l1.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
+
+
+def _edges(n, tile=128):
+    e = []
+    for t in range(0, n, tile):
+        e += [t, t + tile - 1]
+    return e[:40] + [n - 1]
+
+
+@pytest.mark.parametrize("idx", [1, 3, 4])
+def test_packed_ring_workload_full_size(cp, idx):
+    """The ring share over packed V blocks, as the benchmark runs it: bit-identical to the ring
+    over unpacked blocks, and within tolerance of the oracle on sampled rows."""
+    w = workloads.WORKLOADS[idx]
+    say(w.name, "packed V, full size")
+    inp = workloads.make_inputs(w)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    offs = workloads.block_offsets(w.block_lens)
+    kb = [k[:, o:o + L] for o, L in zip(offs, w.block_lens)]
+    vb = [v[:, o:o + L] for o, L in zip(offs, w.block_lens)]
+    pvb = [cp.pack_v(x) for x in vb]
+    out0, lse0 = cp.ring_attention(q, kb, vb, scale=w.scale)
+    out1, lse1 = cp.ring_attention(q, kb, pvb, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1), "packed ring differs from unpacked"
+    rows = workloads.sample_rows(w.Sq, 48, seed=idx, must=_edges(w.Sq))
+    o_ref, l_ref = oracle.attention(inp.q[:, rows], inp.k, inp.v, w.scale)
+    assert_close(f"{w.name} out", out1.cpu().numpy()[:, rows], o_ref, TOL["bf16"]["o"])
+    assert_close(f"{w.name} lse", lse1.cpu().numpy()[:, :, rows], l_ref, TOL["bf16"]["lse"])
+
+
+def test_packed_rejects(cp):
+    """Misuse the binding and the library catch before anything runs."""
+    inp = workloads.make_custom(1, 2, 128, 10, (20,), "bf16", seed=3)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    pv = cp.pack_v(v)
+    out = torch.empty((1, 10, 2, 128), device="cuda")
+    lse = torch.empty((1, 2, 10), device="cuda")
+    with pytest.raises(ValueError):  # flag without a packed operand
+        cp.cp_attn_block_fwd(q, k, v, out, lse, flags=cp.CP_BLOCK_PACKED_V)
+    with pytest.raises(ValueError):  # packed and unpacked blocks mixed
+        cp.cp_ring_attention(q, [k, k], [pv, v], out, lse, flags=0)
+    small = torch.empty(cp.cp_attn_packed_v_bytes(1, 2, 128, 20) - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(cp.CpAttnError):  # buffer too small
+        cp.cp_attn_pack_v(v, small)
+    with pytest.raises(TypeError):
+        cp.cp_attn_pack_v(v.float(), small)
+    with pytest.raises(ValueError):  # packed V has no backward
+        cp.ring_attention_bwd(q, [k], [pv], out, lse, out)
+
+
+@pytest.mark.parametrize("B,S_l,H,D,P", [(1, 2304, 24, 128, 2), (2, 33, 12, 64, 3), (1, 100, 8, 128, 4),
+                                         (1, 64, 6, 128, 1)])
+def test_regroup_pack_v_is_regroup_then_pack(cp, B, S_l, H, D, P):
+    """The fused Ulysses regroup + pack writes the same bytes as the two passes."""
+    say("regroup_pack_v", B, S_l, H, D, P)
+    inp = workloads.make_custom(B, H, D, 1, (S_l,), "bf16", seed=60 + S_l)
+    v = dev(inp.v, "bf16")
+    rg = torch.empty((B, P * S_l, H // P, D), dtype=torch.bfloat16, device="cuda")
+    cp.cp_ulysses_regroup(v, rg, P, cp.CP_REGROUP_SEQ_TO_HEAD)
+    two = cp.pack_v(rg)
+    nbytes = cp.cp_attn_packed_v_bytes(B, H // P, D, P * S_l)
+    buf = torch.full((nbytes + 256,), 0xAB, dtype=torch.uint8, device="cuda")
+    one = cp.cp_ulysses_regroup_pack_v(v, buf, P)
+    torch.cuda.synchronize()
+    assert one.shape == (B, P * S_l, H // P, D)
+    assert torch.equal(buf[:nbytes], two.data[:nbytes]), "fused regroup + pack differs from the two passes"
+    assert bool((buf[nbytes:] == 0xAB).all()), "wrote past its output"
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_bench_step_packed_equals_unpacked(cp, idx):
+    """The benchmark's step with packed V (its default where the block kernel runs its 8-wave
+    shape) gives the same bits as the step with unpacked V: ring shares, and the Ulysses share
+    with the fused regroup + pack."""
+    import bench
+    w = workloads.WORKLOADS[idx]
+    say(w.name, "bench step, packed vs unpacked V")
+    assert cp.cp_attn_fwd_waves(w.B, w.attn_H, w.D, w.Sq) == 8
+    res = []
+    for packed in (False, True):
+        prob = bench.Problem(w, False, packed_v=packed)
+        assert prob.packed == packed
+        prob.step()
+        torch.cuda.synchronize()
+        got = [prob.out.clone(), prob.lse.clone()]
+        if hasattr(prob, "back"):
+            got.append(prob.back.clone())
+        res.append(got)
+        del prob
+    for a, b in zip(*res):
+        assert torch.equal(a, b), f"{w.name}: packed step differs from unpacked"
