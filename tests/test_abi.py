@@ -320,3 +320,24 @@ def test_fwd_waves_query(lib):
         assert q(1, 12, 128, 2304) == 8 and q(1, 24, 64, 8192) == 4
     finally:
         lib.cp_attn_set_fwd_waves(prev)
+
+
+def test_plain_c_consumer(tmp_path):
+    """tests/c/abi_consumer.c, built with gcc as strict C99 against include/cp_attn.h and linked
+    to libcpattn.so, runs its size and validation checks (no GPU, no Python in the process)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(_lib.library_path())
+    exe = str(tmp_path / "abi_consumer")
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(root, "include"),
+           os.path.join(root, "tests", "c", "abi_consumer.c"), _lib.library_path(),
+           f"-Wl,-rpath,{libdir}", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all checks passed" in r.stdout
