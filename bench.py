@@ -14,9 +14,10 @@ pass V to the attention kernel packed (cp_attn_pack_v), and the
 step includes the packing a rank does itself: a ring rank packs its own V block
 (the other ranks' blocks arrive packed by their owners, so they are packed once
 at setup, as the peers would have done); a Ulysses rank packs the V it received
-(its regrouped V: the regroup and the packing run as one pass,
-cp_ulysses_regroup_pack_v). ``--unpacked-v`` runs the same step with V as
-[B, S, H, D].
+(its regrouped V), a pass of its own after the regroup, as it would be after a
+real exchange (cp_ulysses_regroup_pack_v, which fuses the two on one GPU, would
+skip the send buffer a real all-to-all needs). ``--unpacked-v`` runs the same
+step with V as [B, S, H, D].
 
 Prints ONE JSON line on stdout. ``value`` is attention TFLOP/s over the whole
 step, counting 4*B*H*Sq*Skv*D flops; ``roofline`` prices the dominant kernel
@@ -179,11 +180,8 @@ class Problem:
             P = w.ulysses_degree
             cp.cp_ulysses_regroup(self.q, self.qr, P, cp.CP_REGROUP_SEQ_TO_HEAD)
             cp.cp_ulysses_regroup(self.k_own, self.kb[0], P, cp.CP_REGROUP_SEQ_TO_HEAD)
-            if self.packed:  # the regroup of V and its packing in one pass
-                cp.cp_ulysses_regroup_pack_v(self.v_own, self.vb_att[0].data, P)
-            else:
-                cp.cp_ulysses_regroup(self.v_own, self.vb[0], P, cp.CP_REGROUP_SEQ_TO_HEAD)
-        elif self.packed:
+            cp.cp_ulysses_regroup(self.v_own, self.vb[0], P, cp.CP_REGROUP_SEQ_TO_HEAD)
+        if self.packed:
             cp.cp_attn_pack_v(self.vb[0], self.vb_att[0].data)
         cp.cp_ring_attention(self.q_att, self.kb, self.vb_att, self.out, self.lse, scale=w.scale,
                              flags=self.flags, workspace=self.ws)

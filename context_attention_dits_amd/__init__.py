@@ -175,6 +175,12 @@ def _v_operand(name, v, dev):
     """(is_packed, v) for a V argument that is a [B, S, H, D] tensor or a PackedV."""
     if isinstance(v, PackedV):
         _gpu(name, v.data, dev)
+        if not v.data.is_contiguous():
+            raise ValueError(f"{name}: the packed buffer must be contiguous")
+        B, S, H, D = v.shape
+        need = cp_attn_packed_v_bytes(B, H, D, S)
+        if v.data.numel() * v.data.element_size() < need:
+            raise ValueError(f"{name}: packed buffer of {need} bytes needed for V of shape {v.shape}")
         return True, v
     return False, _gpu(name, _bshd(name, v), dev)
 

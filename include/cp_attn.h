@@ -217,7 +217,10 @@ cp_status_t cp_attn_pack_v(const void* v, const int64_t* v_strides, int B, int H
  * B, H / degree, D, degree * S_local, packed, ...) would, without the
  * intermediate tensor: [CP] "Atencao Ulysses" -- after the first all-to-all a
  * rank holds V of every token for its head group, which its attention then
- * reads. in is the sequence-sharded V [B, S_local, H, D] bf16, contiguous,
+ * reads. This fuses the loopback regroup (which stands in for the send buffer
+ * of that exchange) with the packing, so it is for one-GPU use; across GPUs
+ * the receiver packs what arrives with cp_attn_pack_v.
+ * in is the sequence-sharded V [B, S_local, H, D] bf16, contiguous,
  * 16-byte aligned; degree >= 1 divides H; packed holds at least
  * cp_attn_packed_v_bytes(B, H / degree, D, degree * S_local) bytes, 16-byte
  * aligned, not overlapping in. D must be 64 or 128.

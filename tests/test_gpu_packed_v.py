@@ -165,6 +165,8 @@ def test_packed_rejects(cp):
         cp.cp_attn_pack_v(v.float(), small)
     with pytest.raises(ValueError):  # packed V has no backward
         cp.ring_attention_bwd(q, [k], [pv], out, lse, out)
+    with pytest.raises(ValueError):  # a PackedV whose buffer is too small for its shape
+        cp.cp_attn_block_fwd(q, k, cp.PackedV(pv.data[:-16], pv.shape), out, lse)
 
 
 @pytest.mark.parametrize("B,S_l,H,D,P", [(1, 2304, 24, 128, 2), (2, 33, 12, 64, 3), (1, 100, 8, 128, 4),
@@ -190,7 +192,7 @@ def test_regroup_pack_v_is_regroup_then_pack(cp, B, S_l, H, D, P):
 def test_bench_step_packed_equals_unpacked(cp, idx):
     """The benchmark's step with packed V (its default where the block kernel runs its 8-wave
     shape) gives the same bits as the step with unpacked V: ring shares, and the Ulysses share
-    with the fused regroup + pack."""
+    (regroup, then pack)."""
     import bench
     w = workloads.WORKLOADS[idx]
     say(w.name, "bench step, packed vs unpacked V")
