@@ -210,3 +210,52 @@ def test_bench_step_packed_equals_unpacked(cp, idx):
         del prob
     for a, b in zip(*res):
         assert torch.equal(a, b), f"{w.name}: packed step differs from unpacked"
+
+
+def test_pack_and_ring_replay_in_a_graph(cp):
+    """Packing V and the ring over packed blocks only enqueue kernels, so they can be captured
+    in a HIP graph; replays (with eager work between them, and V changed in place between the
+    second and third) must give exactly the eager results."""
+    B, H, D, Sq, lens = 1, 4, 128, 300, (256, 200)
+    say("graph capture pack_v + packed ring")
+    inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=82)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    offs = workloads.block_offsets(lens)
+    kb = [k[:, a:a + L] for a, L in zip(offs, lens)]
+    vb = [v[:, a:a + L] for a, L in zip(offs, lens)]
+    bufs = [torch.empty(cp.cp_attn_packed_v_bytes(B, H, D, L), dtype=torch.uint8, device="cuda") for L in lens]
+    out = torch.empty((B, Sq, H, D), device="cuda")
+    lse = torch.empty((B, H, Sq), device="cuda")
+
+    def step():
+        pvb = [cp.cp_attn_pack_v(x, buf) for x, buf in zip(vb, bufs)]
+        cp.cp_ring_attention(q, kb, pvb, out, lse, scale=inp.workload.scale, flags=cp.CP_RING_ANYTHING)
+
+    def eager():
+        o, l_ = cp.ring_attention(q, kb, vb, scale=inp.workload.scale)
+        torch.cuda.synchronize()
+        return o, l_
+
+    step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        if rep == 2:
+            v.mul_(-0.5)  # new V values: the captured pack must pick them up
+        want_o, want_l = eager()
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        for buf in bufs:
+            buf.fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want_o) and torch.equal(lse, want_l), f"replay {rep} differs from eager"
+    say("graph replays of pack + packed ring match the eager unpacked ring bit for bit")
