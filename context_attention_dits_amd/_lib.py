@@ -82,6 +82,10 @@ def load() -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     path = library_path()
+    try:  # torch's HIP runtime first, so that the library binds to the same one
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(path):
         raise RuntimeError(
             f"HIP library not found at {path}. Build it first: "
