@@ -114,15 +114,21 @@ class Problem:
         H = w.attn_H
         # V as the attention kernel reads it: block 0 (this rank's own block, or the V it received)
         # is packed in every step, the others once here
-        # (only where the kernel runs its 8-wave shape: the 4-wave kernel gains nothing from it)
-        self.packed = packed_v and w.dtype == "bf16" and cp.cp_attn_fwd_waves(B, H, D, w.Sq) == 8
+        # (where the block kernel runs its 8-wave shape, or the packed ring runs as one launch;
+        # the 4-wave kernel on its own gains nothing from it)
+        lens = [kb.shape[1] for kb in self.kb]
+        self.packed = packed_v and w.dtype == "bf16" and (
+            cp.cp_attn_fwd_waves(B, H, D, w.Sq) == 8
+            or cp.cp_ring_attention_one_launch(cp.CP_BF16, B, H, D, w.Sq, lens))
         self.vb_att = list(self.vb)
         if self.packed:
             self.vb_att = [cp.pack_v(x) for x in self.vb]
             torch.cuda.synchronize()
         self.out = torch.empty((B, w.Sq, H, D), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((B, H, w.Sq), dtype=torch.float32, device="cuda")
-        nbytes = cp.cp_ring_attention_workspace_size(B, H, w.Sq, D, self.flags)
+        # with packed V the workspace also lets the ring run as one launch
+        nbytes = cp.cp_ring_attention_workspace_size(B, H, w.Sq, D,
+                                                     self.flags | (cp.CP_RING_PACKED_V if self.packed else 0))
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
 
     def _setup_anything(self, tdt):
@@ -194,11 +200,32 @@ class Problem:
         Block 0 is written, later blocks are merged in by the kernel epilogue.
         The launches of `reps` ring passes run back to back between two HIP
         events on the stream they are launched on; the mean is the region's
-        time over the number of launches.
+        time over the number of launches. Where the step runs the ring as one
+        launch (packed V, cp_ring_attention_one_launch), that launch (and the
+        flag reset before it) is what is timed, with the flops of all blocks.
         """
         torch, cp, w = self.torch, self.cp, self.w
         stream = torch.cuda.current_stream()
         blocks = [(i, kb, vb) for i, (kb, vb) in enumerate(zip(self.kb, self.vb_att)) if kb.shape[1] > 0]
+        lens = [kb.shape[1] for kb in self.kb]
+        if self.packed and self.ws is not None and cp.cp_ring_attention_one_launch(
+                cp.CP_BF16, w.B, w.attn_H, w.D, w.Sq, lens):
+            # the step runs the whole ring as one launch (after a flag reset): time that
+            def one_pass():
+                cp.cp_ring_attention(self.q_att, self.kb, self.vb_att, self.out, self.lse, scale=w.scale,
+                                     flags=self.flags, workspace=self.ws)
+
+            one_pass()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                one_pass()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            self.block_launch = "one launch for all blocks"
+            return e0.elapsed_time(e1) / reps, w.flops
+        self.block_launch = "one launch per block"
 
         def one_pass():
             for i, kb, vb in blocks:
@@ -465,7 +492,7 @@ def main():
         "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": hbm_traffic(w),
                      "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel",
-                     "us_per_launch": round(k_ms * 1e3, 2)},
+                     "us_per_launch": round(k_ms * 1e3, 2), "launches": prob.block_launch},
         "cpu_baseline": cpu,
         "hbm_kernels": hbm,
         "backward": bwd,

@@ -23,7 +23,8 @@ from ._lib import (CP_BF16, CP_BLOCK_ACCUMULATE, CP_BLOCK_PACKED_V, CP_BWD_ACCUM
                    CP_RING_SEPARATE_MERGE, STATUS_NAMES)
 
 __all__ = [
-    "CpAttnError", "load", "cp_abi_version", "cp_last_error", "cp_attn_set_fwd_waves", "cp_attn_fwd_waves", "cp_attn_block_fwd",
+    "CpAttnError", "load", "cp_abi_version", "cp_last_error", "cp_attn_set_fwd_waves", "cp_attn_fwd_waves",
+    "cp_ring_attention_one_launch", "cp_attn_block_fwd",
     "cp_lse_merge", "PackedV", "cp_attn_packed_v_bytes", "cp_attn_pack_v", "pack_v", "cp_ulysses_regroup_pack_v",
     "cp_ring_attention", "cp_ring_attention_workspace_size", "cp_ulysses_regroup",
     "cp_ulysses_pack_heads", "cp_ulysses_concat_seq", "split_counts",
@@ -189,6 +190,12 @@ def cp_attn_fwd_waves(B: int, H: int, D: int, Sq: int) -> int:
     """Workgroup shape (4, or 8 for the ping-pong kernel) of the bfloat16 block kernel at these sizes;
     0 for sizes it does not run. Packed V (cp_attn_pack_v) pays off in the 8-wave shape."""
     return int(_lib.load().cp_attn_fwd_waves(B, H, D, Sq))
+
+
+def cp_ring_attention_one_launch(dtype: int, B: int, H: int, D: int, Sq: int, block_lens) -> bool:
+    """Whether cp_ring_attention with packed V and a workspace runs these blocks as one launch."""
+    lens = (ctypes.c_int * len(block_lens))(*[int(x) for x in block_lens])
+    return bool(_lib.load().cp_ring_attention_one_launch(dtype, B, H, D, Sq, lens, len(block_lens)))
 
 
 def cp_attn_block_fwd(q, k, v, out, lse, scale: Optional[float] = None, flags: int = 0, stream=None):
@@ -491,6 +498,8 @@ def ring_attention(q, k_blocks, v_blocks, scale: Optional[float] = None, ring_an
     if ring_anything is None:
         ring_anything = len(set(lens)) > 1 or 0 in lens
     flags = (CP_RING_ANYTHING if ring_anything else 0) | (CP_RING_SEPARATE_MERGE if separate_merge else 0)
+    if any(isinstance(vb, PackedV) for vb in v_blocks):
+        flags |= CP_RING_PACKED_V  # (the workspace then holds the one-launch ring's flags)
     ws = None
     nbytes = cp_ring_attention_workspace_size(B, H, Sq, D, flags)
     if nbytes:

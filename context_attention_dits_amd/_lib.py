@@ -46,6 +46,7 @@ _SIGNATURES = {
     "cp_last_error": (ctypes.c_char_p, []),
     "cp_attn_set_fwd_waves": (_i, [_i]),
     "cp_attn_fwd_waves": (_i, [_i, _i, _i, _i]),
+    "cp_ring_attention_one_launch": (_i, [_i, _i, _i, _i, _i, ctypes.POINTER(_i), _i]),
     "cp_attn_block_fwd": (_i, [_vp, _i64p, _vp, _vp, _i64p, _i, _i, _i, _i, _i, _i, ctypes.c_float,
                                ctypes.c_uint, _vp, _i64p, _vp, _vp]),
     "cp_lse_merge": (_i, [_vp, _vp, _vp, _vp, _i64p, _i64p, _i, _i, _i, _i, _vp]),

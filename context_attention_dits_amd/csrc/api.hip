@@ -120,6 +120,27 @@ cp_status_t run_block(const void* q, Strides qs, const void* k, const void* v, S
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Does a packed-V ring with a workspace run as one launch? When the blocks'
+// own launches would use the 4-wave kernel (a grid too small, or with a
+// nearly empty last round, for the ping-pong one) and there are 2 .. the
+// kernel's maximum non-empty blocks: then the one launch runs every block's
+// partial in parallel on ping-pong workgroups. Bigger grids keep one launch
+// per block, which measured as fast or faster. (The output's byte offsets
+// must also fit the kernel's 32-bit buffer offsets; checked by the caller
+// through o_end.)
+bool one_launch_ring(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree) {
+  if (dtype != CP_BF16 || D != 128 || B <= 0 || H <= 0 || Sq <= 0) return false;
+  const int waves = g_fwd_waves.load(std::memory_order_relaxed);
+  if (waves == 4) return false;
+  cpattn::FwdArgs a{};
+  a.B = B; a.H = H; a.D = D; a.Sq = Sq;
+  a.waves = waves;
+  if (waves == 0 && cpattn::pick_waves(a) == 8) return false;
+  int n = 0;
+  for (int i = 0; i < ring_degree; ++i) n += block_len[i] > 0;
+  return n >= 2 && n <= cpattn::ring_max_blocks();
+}
+
 size_t partial_bytes(int B, int H, int Sq, int D) {
   return align_up((size_t)B * Sq * H * D * sizeof(float), 256) + align_up((size_t)B * H * Sq * sizeof(float), 256);
 }
@@ -138,6 +159,13 @@ int cp_attn_fwd_waves(int B, int H, int D, int Sq) {
   a.B = B; a.H = H; a.D = D; a.Sq = Sq;
   a.waves = g_fwd_waves.load(std::memory_order_relaxed);
   return cpattn::pick_waves(a);
+}
+
+int cp_ring_attention_one_launch(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree) {
+  if (block_len == nullptr || ring_degree < 1) return 0;
+  for (int i = 0; i < ring_degree; ++i)
+    if (block_len[i] < 0) return 0;
+  return one_launch_ring(dtype, B, H, D, Sq, block_len, ring_degree) ? 1 : 0;
 }
 
 int cp_attn_set_fwd_waves(int waves) {
@@ -256,8 +284,11 @@ cp_status_t cp_ulysses_regroup_pack_v(const void* in, int B, int S_local, int H,
 }
 
 size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned flags) {
-  if (!(flags & CP_RING_SEPARATE_MERGE) || B <= 0 || H <= 0 || Sq <= 0 || D <= 0) return 0;
-  return partial_bytes(B, H, Sq, D);
+  if (B <= 0 || H <= 0 || Sq <= 0 || D <= 0) return 0;
+  if (flags & CP_RING_SEPARATE_MERGE) return partial_bytes(B, H, Sq, D);
+  if (D == 128 && (flags & CP_RING_PACKED_V))
+    return align_up((size_t)cpattn::ring_flag_count(B, H, Sq) * sizeof(int), 256);
+  return 0;
 }
 
 cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const void* const* k_blocks,
@@ -301,6 +332,16 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
   const bool separate = (flags & CP_RING_SEPARATE_MERGE) != 0;
   float* ws_out = nullptr;
   float* ws_lse = nullptr;
+  int* ws_flags = nullptr;  // one launch for all blocks (see cp_ring_attention_workspace_size)
+  if (!separate && workspace != nullptr && B > 0 && H > 0 && Sq > 0) {
+    const size_t need = cp_ring_attention_workspace_size(B, H, Sq, D, flags);
+    if (workspace_bytes < need)
+      return fail(CP_ERR_WORKSPACE, "cp_ring_attention: workspace of %zu bytes needed, %zu given", need,
+                  workspace_bytes);
+    if (!aligned(workspace, 256))
+      return fail(CP_ERR_UNSUPPORTED, "cp_ring_attention: workspace must be 256-byte aligned");
+    if (need > 0) ws_flags = static_cast<int*>(workspace);
+  }
   if (separate && B > 0 && H > 0 && Sq > 0) {
     const size_t need = partial_bytes(B, H, Sq, D);
     if (workspace == nullptr || workspace_bytes < need)
@@ -315,6 +356,32 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
   if (B == 0 || H == 0 || Sq == 0) return CP_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ws_flags != nullptr && packed && one_launch_ring(dtype, B, H, D, Sq, block_len, ring_degree)) {
+    const void* kb[16];
+    const void* vb[16];
+    int len[16];
+    int n = 0;
+    for (int i = 0; i < ring_degree; ++i) {
+      if (block_len[i] == 0) continue;
+      kb[n] = k_blocks[i];
+      vb[n] = v_blocks[i];
+      len[n] = block_len[i];
+      ++n;
+    }
+    const int64_t o_end = ((int64_t)(B - 1) * os.b + (int64_t)(Sq - 1) * os.s + (int64_t)(H - 1) * os.h + D) * 4;
+    if (o_end < 0x7fffffff) {
+      cpattn::FwdArgs a;
+      a.q = q; a.k = nullptr; a.v = nullptr; a.out = out; a.lse = lse;
+      a.qs = qs; a.kvs = kvs; a.os = os;
+      a.B = B; a.H = H; a.D = D; a.Sq = Sq; a.Skv = 0;
+      a.scale = scale;
+      a.accumulate = false;
+      a.waves = 8;
+      a.v_packed = packed;
+      const cpattn::RingBlocks rb{n, kb, vb, len};
+      return hip_status(cpattn::launch_ring_bf16(a, rb, ws_flags, s), "attn_fwd_bf16 (ring)");
+    }
+  }
   const Strides ws_s = resolve(nullptr, Sq, H, D);
   bool have = false;  // does (out, lse) hold a partial yet?
   for (int i = 0; i < ring_degree; ++i) {

@@ -83,6 +83,9 @@
 #ifndef CP_FWD_SCHED_PV
 #define CP_FWD_SCHED_PV 1  // pipeline the transposing V reads ahead of the PV MFMAs
 #endif
+#ifndef CP_RING_SC1
+#define CP_RING_SC1 0  // one-launch ring: device-scope (1) or L2-coherent (0) out/lse accesses
+#endif
 #ifndef CP_FWD_LAZY
 #define CP_FWD_LAZY 8.0f  // rescale threshold on the row maximum, log2 units
 #endif
@@ -104,6 +107,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Word 3 of a raw (unswizzled, untyped) buffer descriptor on gfx9-family GPUs.
 constexpr int kBufferFlags = 0x00020000;
+// Cache-policy operand of buffer loads/stores for device scope (sc1): the
+// access bypasses the caches that are not coherent across XCDs.
+constexpr int kDeviceScope = 16;
+
+// One launch over several ring blocks: at most this many (more run as one launch each).
+constexpr int kMaxRingBlocks = 16;
 
 struct Params {
   const uint16_t* q;
@@ -116,8 +125,16 @@ struct Params {
   int64_t o_sb, o_ss, o_sh;
   int B, H, Sq, Skv;
   int n_qt;  // query tiles per (b, h)
-  int n_wg;  // total workgroups
+  int n_wg;  // total workgroups (ring launch: query tiles, i.e. workgroups per block)
   float c;   // scale * log2(e)
+  // Ring launch only: workgroup i works on block i / u8 (u8 = n_wg rounded up
+  // to a multiple of 8, so that a query tile has the same XCD in every block);
+  // flags[tile] = index of the last block merged into (out, lse) for that tile.
+  int n_blk, u8, spin_limit;
+  int* flags;
+  const uint16_t* kblk[kMaxRingBlocks];
+  const uint16_t* vblk[kMaxRingBlocks];
+  int lblk[kMaxRingBlocks];
 };
 
 // Both 32-lane halves of a wave64 end up with max/sum over the pair (l, l^32).
@@ -191,7 +208,7 @@ struct Nothing {
   __device__ __forceinline__ void operator()(A...) const {}
 };
 
-template <int D, int QB, int NW, bool ACC, bool PACKED>
+template <int D, int QB, int NW, bool ACC, bool PACKED, bool RING>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                                amdgpu_waves_per_eu(CP_FWD_WPE)))
 attn_fwd_bf16_kernel(Params p) {
@@ -219,7 +236,16 @@ attn_fwd_bf16_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
-  const int tile = xcd_remap(blockIdx.x, p.n_wg);
+  // RING: this workgroup's block (uniform) and query tile; padding workgroups
+  // (tiles n_wg .. u8-1 of a block) exit at once.
+  int blk = 0, tile;
+  if constexpr (RING) {
+    blk = blockIdx.x / p.u8;
+    tile = xcd_remap(blockIdx.x - blk * p.u8, p.u8);
+    if (tile >= p.n_wg) return;
+  } else {
+    tile = xcd_remap(blockIdx.x, p.n_wg);
+  }
   const int qt = tile % p.n_qt;
   const int bh = tile / p.n_qt;
   const int h = bh % p.H, b = bh / p.H;
@@ -228,15 +254,17 @@ attn_fwd_bf16_kernel(Params p) {
   // Kernel arguments used inside the tile loop, pinned in SGPRs: reloading
   // them from the argument segment there would make the next LDS wait also
   // wait for that scalar load.
-  int skv = p.Skv;
+  int skv = RING ? p.lblk[blk] : p.Skv;
   float csc = p.c;
   asm volatile("" : "+s"(skv), "+s"(csc));
   const int n_tiles = (skv + C::BN - 1) / C::BN;
 
-  const uint16_t* kbase = p.k + b * p.kv_sb + h * p.kv_sh;
+  const uint16_t* kblock = RING ? p.kblk[blk] : p.k;
+  const uint16_t* vblock = RING ? p.vblk[blk] : p.v;
+  const uint16_t* kbase = kblock + b * p.kv_sb + h * p.kv_sh;
   // packed V: n_tiles contiguous tiles of V_BYTES per (b, h), (b, h) in order
-  const uint16_t* vbase = PACKED ? p.v + (int64_t)bh * n_tiles * (C::V_BYTES / 2)
-                                 : p.v + b * p.kv_sb + h * p.kv_sh;
+  const uint16_t* vbase = PACKED ? vblock + (int64_t)bh * n_tiles * (C::V_BYTES / 2)
+                                 : vblock + b * p.kv_sb + h * p.kv_sh;
 
   // ---- Q (B operand of S^T = K Q^T): lane holds query l32, dims kk*16 + hi*8 .. +7
   bf16x8 qf[QB][C::KK];
@@ -746,6 +774,60 @@ attn_fwd_bf16_kernel(Params p) {
   }
 
   // ---- epilogue: normalise, LSE, optional merge into the accumulator
+  // RING: block 0 writes, later blocks merge, each after the previous block's
+  // workgroup for the same query tile has published its (out, lse): it waits
+  // for flags[tile] == blk - 1. (out, lse) and the flags go through
+  // device-scope accesses, which bypass the caches that are not coherent
+  // across XCDs, so a reader sees what the writer's completed stores left in
+  // memory. The wait is bounded; it cannot deadlock: the awaited workgroup
+  // has the same index modulo u8, so it runs on the same XCD, which starts
+  // workgroups in index order, and it waits only on earlier ones itself.
+  bool acc = ACC;
+  if constexpr (RING) {
+    acc = blk > 0;
+    if (acc) {
+      if (threadIdx.x == 0) {
+        int n = 0;
+        while (__hip_atomic_load(p.flags + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != blk - 1 &&
+               ++n < p.spin_limit)
+          __builtin_amdgcn_s_sleep(1);
+      }
+      __syncthreads();
+    }
+  }
+  // accesses to out and lse (RING_SC1: device scope, bypassing the caches;
+  // otherwise plain, coherent through the XCD's L2 that all workgroups of a
+  // query tile share)
+  const __amdgpu_buffer_rsrc_t orsrc =
+      __builtin_amdgcn_make_buffer_rsrc(p.out, (short)0, 0x7fffffff, kBufferFlags);
+  auto o_load = [&](const float* ptr) -> f32x4 {
+    if constexpr (RING && CP_RING_SC1) {
+      return __builtin_amdgcn_raw_buffer_load_b128(orsrc, (int)((ptr - p.out) * 4), 0, kDeviceScope);
+    } else {
+      return *reinterpret_cast<const f32x4*>(ptr);
+    }
+  };
+  auto o_store = [&](float* ptr, f32x4 v) {
+    if constexpr (RING && CP_RING_SC1) {
+      __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (int)((ptr - p.out) * 4), 0, kDeviceScope);
+    } else {
+      *reinterpret_cast<f32x4*>(ptr) = v;
+    }
+  };
+  auto l_load = [&](const float* ptr) -> float {
+    if constexpr (RING && CP_RING_SC1) {
+      return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      return *ptr;
+    }
+  };
+  auto l_store = [&](float* ptr, float v) {
+    if constexpr (RING && CP_RING_SC1) {
+      __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      *ptr = v;
+    }
+  };
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qrow0 + qb * 32 + l32;
@@ -755,8 +837,8 @@ attn_fwd_bf16_kernel(Params p) {
     if (row < p.Sq) {
       float* orow = p.out + b * p.o_sb + (int64_t)row * p.o_ss + h * p.o_sh;
       float* lrow = p.lse + ((int64_t)b * p.H + h) * p.Sq + row;
-      if constexpr (ACC) {
-        const float la2 = *lrow * kLog2e;
+      if (acc) {
+        const float la2 = l_load(lrow) * kLog2e;
         const float M = fmaxf(la2, lse2);
         const float wa = fast_exp2(la2 - M);  // 0 when the accumulator is empty (-inf)
         const float wb = fast_exp2(lse2 - M);
@@ -766,13 +848,13 @@ attn_fwd_bf16_kernel(Params p) {
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            f32x4* dst = reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi);
+            float* dst = orow + db * 32 + 8 * g + 4 * hi;
             const f32x4 ob = {o[qb][db][4 * g], o[qb][db][4 * g + 1], o[qb][db][4 * g + 2],
                               o[qb][db][4 * g + 3]};
-            const f32x4 oa = *dst;
-            *dst = (wa > 0.f) ? (fa * oa + fb * ob) : (fb * ob);
+            const f32x4 oa = o_load(dst);
+            o_store(dst, (wa > 0.f) ? (fa * oa + fb * ob) : (fb * ob));
           }
-        if (hi == 0) *lrow = (M + fast_log2(tot)) * kLn2;
+        if (hi == 0) l_store(lrow, (M + fast_log2(tot)) * kLn2);
       } else {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -780,11 +862,17 @@ attn_fwd_bf16_kernel(Params p) {
           for (int g = 0; g < 4; ++g) {
             const f32x4 ob = {o[qb][db][4 * g], o[qb][db][4 * g + 1], o[qb][db][4 * g + 2],
                               o[qb][db][4 * g + 3]};
-            *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi) = ob * inv;
+            o_store(orow + db * 32 + 8 * g + 4 * hi, ob * inv);
           }
-        if (hi == 0) *lrow = lse2 * kLn2;
+        if (hi == 0) l_store(lrow, lse2 * kLn2);
       }
     }
+  }
+  if constexpr (RING) {
+    // publish: every wave's stores have completed, then the flag
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt: no wait
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(p.flags + tile, blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -807,7 +895,56 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
   p.n_wg = (int)n_wg;
   p.c = a.scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, NW, ACC, PACKED>), dim3(p.n_wg), dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, NW, ACC, PACKED, false>), dim3(p.n_wg), dim3(C::NT), 0, stream,
+                     p);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) fill_flags_kernel(int* flags, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) flags[i] = -1;
+}
+
+// One launch for a ring of blocks (ping-pong shape, D = 128): n_blk * u8
+// workgroups, block-major; see the kernel's epilogue for the ordering of the
+// merges. flags: n_wg ints, reset here by a fill kernel (no memset, so the
+// pair can be captured in a graph).
+template <bool PACKED>
+hipError_t launch_ring_128(const FwdArgs& a, const RingBlocks& rb, int* flags, hipStream_t stream) {
+  constexpr int QB = CP_FWD_QB;
+  using C = Cfg<128, QB, 8>;
+  Params p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = nullptr;
+  p.v = nullptr;
+  p.out = a.out;
+  p.lse = a.lse;
+  p.q_sb = a.qs.b; p.q_ss = a.qs.s; p.q_sh = a.qs.h;
+  p.kv_sb = a.kvs.b; p.kv_ss = a.kvs.s; p.kv_sh = a.kvs.h;
+  p.o_sb = a.os.b; p.o_ss = a.os.s; p.o_sh = a.os.h;
+  p.B = a.B; p.H = a.H; p.Sq = a.Sq; p.Skv = 0;
+  p.n_qt = (a.Sq + C::BM - 1) / C::BM;
+  const int64_t n_wg = (int64_t)p.n_qt * a.H * a.B;
+  const int64_t u8 = (n_wg + 7) / 8 * 8;
+  if (rb.n < 1 || rb.n > kMaxRingBlocks || u8 * rb.n > 0x7fffffff) return hipErrorInvalidConfiguration;
+  p.n_wg = (int)n_wg;
+  p.u8 = (int)u8;
+  p.n_blk = rb.n;
+  p.spin_limit = 1 << 22;
+  p.flags = flags;
+  p.c = a.scale * kLog2e;
+  for (int i = 0; i < kMaxRingBlocks; ++i) {
+    p.kblk[i] = i < rb.n ? static_cast<const uint16_t*>(rb.k[i]) : nullptr;
+    p.vblk[i] = i < rb.n ? static_cast<const uint16_t*>(rb.v[i]) : nullptr;
+    p.lblk[i] = i < rb.n ? rb.len[i] : 0;
+  }
+  if (a.accumulate) return hipErrorInvalidValue;  // the ring launch writes block 0
+  hipLaunchKernelGGL(fill_flags_kernel, dim3((unsigned)((n_wg + 255) / 256)), dim3(256), 0, stream, flags,
+                     (int)n_wg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, QB, 8, false, PACKED, true>), dim3((unsigned)(u8 * rb.n)),
+                     dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -932,6 +1069,21 @@ hipError_t launch_dn(const FwdArgs& a, hipStream_t stream) {
     if (pick_waves(a) == 8) return launch_dw<D, 8>(a, stream);
   }
   return launch_dw<D, 4>(a, stream);
+}
+
+// With L2-coherent out/lse accesses a merging workgroup must not find a
+// stale copy of its tile's output in its CU's L1: the L1 only holds lines the
+// CU has read, and with at most 3 blocks a tile is merged at most twice, the
+// second time by a CU that has either not read the tile before or written it
+// itself since. More blocks run as one launch per block.
+int ring_max_blocks() { return CP_RING_SC1 ? kMaxRingBlocks : 3; }
+
+int64_t ring_flag_count(int B, int H, int Sq) { return (int64_t)((Sq + 255) / 256) * H * B; }
+
+hipError_t launch_ring_bf16(const FwdArgs& a, const RingBlocks& rb, int* flags, hipStream_t stream) {
+  // packed V only: with V transposed in the kernel the ring variant spills heavily
+  if (a.D != 128 || !a.v_packed) return hipErrorInvalidValue;
+  return launch_ring_128<true>(a, rb, flags, stream);
 }
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {

@@ -85,6 +85,22 @@ hipError_t launch_attn_bwd_prep(const float* out, Strides os, const float* dout,
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 // Workgroup shape (waves: 4, or 8 for the ping-pong kernel) the bf16 launch uses for a.
 int pick_waves(const FwdArgs& a);
+
+// One launch for all the (non-empty) blocks of a ring, bf16, D = 128, packed V: the
+// blocks' partials are computed in parallel and merged into (out, lse) in
+// block order, each query tile's merges ordered through flags[tile]
+// (ring_flag_count ints of caller memory, 4-byte aligned; reset by the
+// launch). a.k, a.v, a.Skv and a.accumulate are not used; a.kvs is the blocks'
+// shared stride triple and a.v_packed says whether every v[i] is packed.
+struct RingBlocks {
+  int n;
+  const void* const* k;
+  const void* const* v;
+  const int* len;
+};
+int ring_max_blocks();
+int64_t ring_flag_count(int B, int H, int Sq);
+hipError_t launch_ring_bf16(const FwdArgs& a, const RingBlocks& rb, int* flags, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
 // out = 0, lse = -inf for every (b, s, h): attention over an empty key set.

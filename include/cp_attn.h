@@ -141,8 +141,11 @@ cp_status_t cp_lse_merge(float* out_acc, float* lse_acc, const float* out_blk, c
 
 /*
  * cp_ring_attention_workspace_size -- bytes of workspace cp_ring_attention
- * needs for these sizes and flags: 0 unless CP_RING_SEPARATE_MERGE is set,
- * then room for one float32 partial output [B, Sq, H, D] and its LSE.
+ * uses for these sizes and flags. With CP_RING_SEPARATE_MERGE: one float32
+ * partial output [B, Sq, H, D] and its LSE (required). Otherwise, with
+ * CP_RING_PACKED_V and D = 128: one int per 256-row query tile of each (b, h),
+ * rounded up to 256 bytes (optional: with it, bf16 rings of 2..16 non-empty
+ * blocks run as one launch; without it, as one launch per block). Else 0.
  */
 size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned flags);
 
@@ -170,8 +173,16 @@ size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned fl
  *                       CP_RING_PACKED_V: v_blocks[i] is the output of
  *                       cp_attn_pack_v for block i (as CP_BLOCK_PACKED_V).
  *   out, lse            as cp_attn_block_fwd; overwritten.
- *   workspace           device buffer of workspace_bytes (may be NULL when
- *                       cp_ring_attention_workspace_size() returns 0)
+ *   workspace           device buffer of workspace_bytes, 256-byte aligned,
+ *                       at least cp_ring_attention_workspace_size(); may be
+ *                       NULL unless CP_RING_SEPARATE_MERGE is set.
+ * One launch for the whole ring (packed V with a workspace, bf16, D = 128,
+ * 2 or 3 non-empty blocks, and a grid the per-block launches would run on the
+ * 4-wave kernel; cp_ring_attention_one_launch says whether a call qualifies):
+ * the partials of all blocks are computed in parallel, and each query tile's
+ * merges still run in block order through the same epilogue arithmetic, so
+ * the result is the same, bit for bit, as one launch per block. Calls that
+ * share a workspace must not overlap.
  * If every block is empty the result is out = 0, lse = -inf.
  */
 cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides,
@@ -227,6 +238,12 @@ cp_status_t cp_attn_pack_v(const void* v, const int64_t* v_strides, int B, int H
  */
 cp_status_t cp_ulysses_regroup_pack_v(const void* in, int B, int S_local, int H, int D, int degree,
                                       void* packed, size_t packed_bytes, void* stream);
+
+/* 1 if cp_ring_attention, given these sizes and block lengths with packed V
+ * (CP_RING_PACKED_V) and a workspace, runs the whole ring as one launch (see
+ * cp_ring_attention), else 0. A caller that packs V only for speed can use
+ * this and cp_attn_fwd_waves to decide whether to. */
+int cp_ring_attention_one_launch(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree);
 
 /*
  * cp_ulysses_regroup -- the Ulysses all-to-all's local permutation, loopback.

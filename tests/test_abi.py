@@ -341,3 +341,43 @@ def test_plain_c_consumer(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "all checks passed" in r.stdout
+
+
+def test_ring_one_launch_workspace_rules(lib):
+    """With packed V (bf16, D = 128) the ring can run as one launch, whose per-query-tile flags
+    live in the workspace: one int per 256-row tile of each (b, h), in 256-byte units. Without
+    a workspace the ring still runs, one launch per block; a workspace that is too small or
+    misaligned is rejected."""
+    pk = _lib.CP_RING_PACKED_V
+    assert lib.cp_ring_attention_workspace_size(1, 24, 2304, 128, pk) == 1024   # 9 * 24 ints -> 256-byte units
+    assert lib.cp_ring_attention_workspace_size(2, 24, 1536, 128, pk | _lib.CP_RING_ANYTHING) == 1280
+    assert lib.cp_ring_attention_workspace_size(1, 24, 2304, 64, pk) == 0
+    assert lib.cp_ring_attention_workspace_size(1, 24, 2304, 128, 0) == 0
+    need = lib.cp_ring_attention_workspace_size(1, 2, 8, 128, pk)
+    assert need == 256
+    assert _ring(lib, [8, 8], flags=pk, ws=FAKE, ws_bytes=need - 4) == _lib.CP_ERR_WORKSPACE
+    assert _ring(lib, [8, 8], flags=pk, ws=FAKE + 16, ws_bytes=need) == _lib.CP_ERR_UNSUPPORTED
+
+
+def test_ring_one_launch_query(lib):
+    """Which packed rings run as one launch: 2 or 3 non-empty blocks, bf16, D = 128, on grids the
+    per-block launches would run on the 4-wave kernel."""
+    def q(dtype, B, H, D, Sq, lens):
+        arr = (ctypes.c_int * len(lens))(*lens)
+        return lib.cp_ring_attention_one_launch(dtype, B, H, D, Sq, arr, len(lens))
+    prev = lib.cp_attn_set_fwd_waves(0)
+    try:
+        assert q(1, 2, 24, 128, 1536, [1536, 1536, 1535]) == 1   # ring-anything share
+        assert q(1, 1, 12, 128, 2304, [2304, 2304]) == 1         # USP share
+        assert q(1, 1, 24, 128, 2304, [2304, 2304]) == 0         # FLUX ring-2: 8-wave per block
+        assert q(1, 2, 24, 128, 1536, [1536, 0, 1535]) == 1      # empty blocks do not count
+        assert q(1, 2, 24, 128, 1536, [1536] * 4) == 0           # more than 3 blocks
+        assert q(1, 2, 24, 128, 1536, [1536, 0, 0]) == 0         # one block
+        assert q(0, 2, 24, 128, 1536, [1536, 1536]) == 0         # float32
+        assert q(1, 2, 24, 64, 1536, [1536, 1536]) == 0          # D = 64
+        lib.cp_attn_set_fwd_waves(8)
+        assert q(1, 1, 24, 128, 2304, [2304, 2304]) == 1
+        lib.cp_attn_set_fwd_waves(4)
+        assert q(1, 1, 12, 128, 2304, [2304, 2304]) == 0
+    finally:
+        lib.cp_attn_set_fwd_waves(prev)

@@ -188,15 +188,16 @@ def test_regroup_pack_v_is_regroup_then_pack(cp, B, S_l, H, D, P):
     assert bool((buf[nbytes:] == 0xAB).all()), "wrote past its output"
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
 def test_bench_step_packed_equals_unpacked(cp, idx):
     """The benchmark's step with packed V (its default where the block kernel runs its 8-wave
-    shape) gives the same bits as the step with unpacked V: ring shares, and the Ulysses share
-    (regroup, then pack)."""
+    shape or the ring runs as one launch) gives the same bits as the step with unpacked V: ring
+    shares, the Ulysses share (regroup, then pack), and the ring-anything and USP shares, whose
+    packed step is one launch of 8-wave workgroups where the unpacked one runs each block on the
+    4-wave kernel (same arithmetic per row, in the same order)."""
     import bench
     w = workloads.WORKLOADS[idx]
     say(w.name, "bench step, packed vs unpacked V")
-    assert cp.cp_attn_fwd_waves(w.B, w.attn_H, w.D, w.Sq) == 8
     res = []
     for packed in (False, True):
         prob = bench.Problem(w, False, packed_v=packed)
@@ -212,12 +213,14 @@ def test_bench_step_packed_equals_unpacked(cp, idx):
         assert torch.equal(a, b), f"{w.name}: packed step differs from unpacked"
 
 
-def test_pack_and_ring_replay_in_a_graph(cp):
-    """Packing V and the ring over packed blocks only enqueue kernels, so they can be captured
-    in a HIP graph; replays (with eager work between them, and V changed in place between the
-    second and third) must give exactly the eager results."""
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_pack_and_ring_replay_in_a_graph(cp, one_launch):
+    """Packing V and the ring over packed blocks only enqueue kernels (the one-launch ring's flag
+    reset is a kernel too), so they can be captured in a HIP graph; replays (with eager work
+    between them, and V changed in place between the second and third) must give exactly the
+    eager results."""
     B, H, D, Sq, lens = 1, 4, 128, 300, (256, 200)
-    say("graph capture pack_v + packed ring")
+    say("graph capture pack_v + packed ring", "one launch" if one_launch else "one launch per block")
     inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=82)
     q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
     offs = workloads.block_offsets(lens)
@@ -226,10 +229,16 @@ def test_pack_and_ring_replay_in_a_graph(cp):
     bufs = [torch.empty(cp.cp_attn_packed_v_bytes(B, H, D, L), dtype=torch.uint8, device="cuda") for L in lens]
     out = torch.empty((B, Sq, H, D), device="cuda")
     lse = torch.empty((B, H, Sq), device="cuda")
+    ws = None
+    if one_launch:
+        n = cp.cp_ring_attention_workspace_size(B, H, Sq, D, cp.CP_RING_PACKED_V)
+        assert n > 0
+        ws = torch.full((n,), 0x55, dtype=torch.uint8, device="cuda")
 
     def step():
         pvb = [cp.cp_attn_pack_v(x, buf) for x, buf in zip(vb, bufs)]
-        cp.cp_ring_attention(q, kb, pvb, out, lse, scale=inp.workload.scale, flags=cp.CP_RING_ANYTHING)
+        cp.cp_ring_attention(q, kb, pvb, out, lse, scale=inp.workload.scale, flags=cp.CP_RING_ANYTHING,
+                             workspace=ws)
 
     def eager():
         o, l_ = cp.ring_attention(q, kb, vb, scale=inp.workload.scale)
@@ -259,3 +268,50 @@ def test_pack_and_ring_replay_in_a_graph(cp):
         torch.cuda.synchronize()
         assert torch.equal(out, want_o) and torch.equal(lse, want_l), f"replay {rep} differs from eager"
     say("graph replays of pack + packed ring match the eager unpacked ring bit for bit")
+
+
+def _ring_pair(cp, q, kb, vb, scale, flags=0):
+    """(out, lse) of the packed ring as one launch (with a workspace) and as one launch per block."""
+    B, Sq, H, D = q.shape
+    pvb = [cp.pack_v(x) for x in vb]
+    n = cp.cp_ring_attention_workspace_size(B, H, Sq, D, cp.CP_RING_PACKED_V | flags)
+    ws = torch.full((max(n, 1),), 0x7F, dtype=torch.uint8, device="cuda")  # stale flag values
+    res = []
+    for w in (ws, None):
+        out = torch.full((B, Sq, H, D), float("nan"), device="cuda")
+        lse = torch.full((B, H, Sq), float("nan"), device="cuda")
+        cp.cp_ring_attention(q, kb, pvb, out, lse, scale=scale, flags=flags, workspace=w)
+        res.append((out, lse))
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("waves,B,H,Sq,lens", [(8, 1, 4, 300, (256, 200)), (8, 2, 3, 1000, (1536, 1536, 1535)),
+                                               (8, 1, 24, 2304, (2304, 2304)), (8, 1, 2, 513, (100, 0, 77, 64)),
+                                               (8, 1, 2, 260, (64,) * 4), (0, 1, 12, 2304, (2304, 2304)),
+                                               (0, 2, 24, 1536, (1536, 1536, 1535)), (0, 1, 24, 2304, (2304, 2304))])
+def test_ring_one_launch_matches_per_block(cp, waves, B, H, Sq, lens):
+    """The one-launch ring (every block's partial in parallel, the merges ordered per query tile
+    through flags) gives the same bits as one launch per block, twice on one workspace. Forcing
+    the 8-wave kernel makes every ring of 2 or 3 non-empty blocks run as one launch; with the
+    automatic choice only grids that the per-block launches would run on 4 waves do (the USP and
+    ring-anything shares), the FLUX ring-2 share does not; 4 blocks never do."""
+    D = 128
+    n_nonempty = sum(1 for L in lens if L > 0)
+    with fwd_waves(cp, waves):
+        one = cp.cp_ring_attention_one_launch(cp.CP_BF16, B, H, D, Sq, lens)
+        assert one == (2 <= n_nonempty <= 3 and (waves == 8 or (B, H, Sq) != (1, 24, 2304)))
+        say("one-launch ring", "waves", waves, B, H, Sq, lens, "one launch" if one else "per block")
+        inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=700 + len(lens) + Sq)
+        q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+        offs = workloads.block_offsets(lens)
+        kb = [k[:, a:a + L] for a, L in zip(offs, lens)]
+        vb = [v[:, a:a + L] for a, L in zip(offs, lens)]
+        flags = cp.CP_RING_ANYTHING if (len(set(lens)) > 1 or 0 in lens) else 0
+        for rep in range(2):
+            (o1, l1), (o0, l0) = _ring_pair(cp, q, kb, vb, inp.workload.scale, flags)
+            assert torch.equal(o1, o0) and torch.equal(l1, l0), f"one launch differs from per-block launches ({rep})"
+    if B * H * Sq <= 2 * 3 * 1000:
+        o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.workload.scale)
+        assert_close("out", o1.cpu().numpy(), o_ref, TOL["bf16"]["o"])
+        assert_close("lse", l1.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
