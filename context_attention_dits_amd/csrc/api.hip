@@ -124,10 +124,12 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // own launches would use the 4-wave kernel (a grid too small, or with a
 // nearly empty last round, for the ping-pong one) and there are 2 .. the
 // kernel's maximum non-empty blocks: then the one launch runs every block's
-// partial in parallel on ping-pong workgroups. Bigger grids keep one launch
-// per block, which measured as fast or faster. (The output's byte offsets
-// must also fit the kernel's 32-bit buffer offsets; checked by the caller
-// through o_end.)
+// partial in parallel on ping-pong workgroups. A single block of at least two
+// 64-key tiles is split at a tile boundary into two halves that run the same
+// way (the ring's own method, one level finer: two partials merged by their
+// LSE). Bigger grids keep one launch per block, which measured as fast or
+// faster. (The output's byte offsets must also fit the kernel's 32-bit buffer
+// offsets; checked by the caller through o_end.)
 bool one_launch_ring(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree) {
   if (dtype != CP_BF16 || D != 128 || B <= 0 || H <= 0 || Sq <= 0) return false;
   const int waves = g_fwd_waves.load(std::memory_order_relaxed);
@@ -136,8 +138,13 @@ bool one_launch_ring(int dtype, int B, int H, int D, int Sq, const int* block_le
   a.B = B; a.H = H; a.D = D; a.Sq = Sq;
   a.waves = waves;
   if (waves == 0 && cpattn::pick_waves(a) == 8) return false;
-  int n = 0;
-  for (int i = 0; i < ring_degree; ++i) n += block_len[i] > 0;
+  int n = 0, only = 0;
+  for (int i = 0; i < ring_degree; ++i)
+    if (block_len[i] > 0) {
+      ++n;
+      only = block_len[i];
+    }
+  if (n == 1) return only >= 128;
   return n >= 2 && n <= cpattn::ring_max_blocks();
 }
 
@@ -359,14 +366,26 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
   if (ws_flags != nullptr && packed && one_launch_ring(dtype, B, H, D, Sq, block_len, ring_degree)) {
     const void* kb[16];
     const void* vb[16];
-    int len[16];
+    int len[16], vt0[16], vnt[16];
     int n = 0;
     for (int i = 0; i < ring_degree; ++i) {
       if (block_len[i] == 0) continue;
       kb[n] = k_blocks[i];
       vb[n] = v_blocks[i];
       len[n] = block_len[i];
+      vt0[n] = 0;
+      vnt[n] = (block_len[i] + 63) / 64;
       ++n;
+    }
+    if (n == 1) {  // two halves of the one block, split at a 64-key tile boundary
+      const int L = len[0], L0 = ((L + 1) / 2 + 63) / 64 * 64;
+      kb[1] = static_cast<const char*>(kb[0]) + (int64_t)L0 * kvs.s * 2;
+      vb[1] = vb[0];
+      len[0] = L0;
+      len[1] = L - L0;
+      vt0[1] = L0 / 64;
+      vnt[1] = vnt[0];
+      n = 2;
     }
     const int64_t o_end = ((int64_t)(B - 1) * os.b + (int64_t)(Sq - 1) * os.s + (int64_t)(H - 1) * os.h + D) * 4;
     if (o_end < 0x7fffffff) {
@@ -378,7 +397,7 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
       a.accumulate = false;
       a.waves = 8;
       a.v_packed = packed;
-      const cpattn::RingBlocks rb{n, kb, vb, len};
+      const cpattn::RingBlocks rb{n, kb, vb, len, vt0, vnt};
       return hip_status(cpattn::launch_ring_bf16(a, rb, ws_flags, s), "attn_fwd_bf16 (ring)");
     }
   }

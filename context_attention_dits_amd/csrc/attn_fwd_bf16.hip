@@ -135,6 +135,10 @@ struct Params {
   const uint16_t* kblk[kMaxRingBlocks];
   const uint16_t* vblk[kMaxRingBlocks];
   int lblk[kMaxRingBlocks];
+  // packed V of block i: vblk[i] points at its first tile within (b, h) = 0
+  // of a buffer with vnt[i] tiles per (b, h) (a block may be a tile-aligned
+  // part of a larger packed block)
+  int vnt[kMaxRingBlocks];
 };
 
 // Both 32-lane halves of a wave64 end up with max/sum over the pair (l, l^32).
@@ -263,8 +267,9 @@ attn_fwd_bf16_kernel(Params p) {
   const uint16_t* vblock = RING ? p.vblk[blk] : p.v;
   const uint16_t* kbase = kblock + b * p.kv_sb + h * p.kv_sh;
   // packed V: n_tiles contiguous tiles of V_BYTES per (b, h), (b, h) in order
-  const uint16_t* vbase = PACKED ? vblock + (int64_t)bh * n_tiles * (C::V_BYTES / 2)
-                                 : vblock + b * p.kv_sb + h * p.kv_sh;
+  // (RING: this block's tiles within its buffer's (b, h) row of vnt tiles)
+  const int64_t v_tile0 = (int64_t)bh * (RING ? p.vnt[blk] : n_tiles);
+  const uint16_t* vbase = PACKED ? vblock + v_tile0 * (C::V_BYTES / 2) : vblock + b * p.kv_sb + h * p.kv_sh;
 
   // ---- Q (B operand of S^T = K Q^T): lane holds query l32, dims kk*16 + hi*8 .. +7
   bf16x8 qf[QB][C::KK];
@@ -795,21 +800,23 @@ attn_fwd_bf16_kernel(Params p) {
       __syncthreads();
     }
   }
-  // accesses to out and lse (RING_SC1: device scope, bypassing the caches;
-  // otherwise plain, coherent through the XCD's L2 that all workgroups of a
-  // query tile share)
+  // accesses to out and lse. RING: through a buffer descriptor with 32-bit
+  // offsets (fewer address registers than 64-bit pointers), with device
+  // scope (CP_RING_SC1: bypassing the caches) or plain (coherent through the
+  // XCD's L2 that all workgroups of a query tile share).
   const __amdgpu_buffer_rsrc_t orsrc =
       __builtin_amdgcn_make_buffer_rsrc(p.out, (short)0, 0x7fffffff, kBufferFlags);
+  constexpr int kRingPolicy = CP_RING_SC1 ? kDeviceScope : 0;
   auto o_load = [&](const float* ptr) -> f32x4 {
-    if constexpr (RING && CP_RING_SC1) {
-      return __builtin_amdgcn_raw_buffer_load_b128(orsrc, (int)((ptr - p.out) * 4), 0, kDeviceScope);
+    if constexpr (RING) {
+      return __builtin_amdgcn_raw_buffer_load_b128(orsrc, (int)((ptr - p.out) * 4), 0, kRingPolicy);
     } else {
       return *reinterpret_cast<const f32x4*>(ptr);
     }
   };
   auto o_store = [&](float* ptr, f32x4 v) {
-    if constexpr (RING && CP_RING_SC1) {
-      __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (int)((ptr - p.out) * 4), 0, kDeviceScope);
+    if constexpr (RING) {
+      __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (int)((ptr - p.out) * 4), 0, kRingPolicy);
     } else {
       *reinterpret_cast<f32x4*>(ptr) = v;
     }
@@ -935,8 +942,9 @@ hipError_t launch_ring_128(const FwdArgs& a, const RingBlocks& rb, int* flags, h
   p.c = a.scale * kLog2e;
   for (int i = 0; i < kMaxRingBlocks; ++i) {
     p.kblk[i] = i < rb.n ? static_cast<const uint16_t*>(rb.k[i]) : nullptr;
-    p.vblk[i] = i < rb.n ? static_cast<const uint16_t*>(rb.v[i]) : nullptr;
+    p.vblk[i] = i < rb.n ? static_cast<const uint16_t*>(rb.v[i]) + (int64_t)rb.vt0[i] * (C::V_BYTES / 2) : nullptr;
     p.lblk[i] = i < rb.n ? rb.len[i] : 0;
+    p.vnt[i] = i < rb.n ? rb.vnt[i] : 0;
   }
   if (a.accumulate) return hipErrorInvalidValue;  // the ring launch writes block 0
   hipLaunchKernelGGL(fill_flags_kernel, dim3((unsigned)((n_wg + 255) / 256)), dim3(256), 0, stream, flags,

@@ -94,9 +94,11 @@ int pick_waves(const FwdArgs& a);
 // shared stride triple and a.v_packed says whether every v[i] is packed.
 struct RingBlocks {
   int n;
-  const void* const* k;
-  const void* const* v;
-  const int* len;
+  const void* const* k;  // K of block i at its first key (kvs strides)
+  const void* const* v;  // packed V buffer holding block i
+  const int* len;        // keys of block i
+  const int* vt0;        // block i's first tile in its packed buffer (0 unless part of a larger block)
+  const int* vnt;        // tiles per (b, h) of that buffer
 };
 int ring_max_blocks();
 int64_t ring_flag_count(int B, int H, int Sq);

@@ -181,8 +181,11 @@ size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned fl
  * 4-wave kernel; cp_ring_attention_one_launch says whether a call qualifies):
  * the partials of all blocks are computed in parallel, and each query tile's
  * merges still run in block order through the same epilogue arithmetic, so
- * the result is the same, bit for bit, as one launch per block. Calls that
- * share a workspace must not overlap.
+ * the result is the same, bit for bit, as one launch per block. A single
+ * non-empty block of at least 128 keys on such a grid is split at a 64-key
+ * tile boundary into two halves run the same way (two partials merged by
+ * their LSE: equal to one pass up to rounding). Calls that share a workspace
+ * must not overlap.
  * If every block is empty the result is out = 0, lse = -inf.
  */
 cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides,

@@ -372,7 +372,10 @@ def test_ring_one_launch_query(lib):
         assert q(1, 1, 24, 128, 2304, [2304, 2304]) == 0         # FLUX ring-2: 8-wave per block
         assert q(1, 2, 24, 128, 1536, [1536, 0, 1535]) == 1      # empty blocks do not count
         assert q(1, 2, 24, 128, 1536, [1536] * 4) == 0           # more than 3 blocks
-        assert q(1, 2, 24, 128, 1536, [1536, 0, 0]) == 0         # one block
+        assert q(1, 2, 24, 128, 1536, [1536, 0, 0]) == 1         # one block: split in two halves
+        assert q(1, 1, 6, 128, 4481, [4481]) == 1                # the Ulysses Anything share, split
+        assert q(1, 1, 12, 128, 4608, [4608]) == 0               # Ulysses-2: 8-wave per block
+        assert q(1, 1, 6, 128, 4481, [127]) == 0                 # under two tiles: not split
         assert q(0, 2, 24, 128, 1536, [1536, 1536]) == 0         # float32
         assert q(1, 2, 24, 64, 1536, [1536, 1536]) == 0          # D = 64
         lib.cp_attn_set_fwd_waves(8)

@@ -315,3 +315,23 @@ def test_ring_one_launch_matches_per_block(cp, waves, B, H, Sq, lens):
         o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.workload.scale)
         assert_close("out", o1.cpu().numpy(), o_ref, TOL["bf16"]["o"])
         assert_close("lse", l1.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
+
+
+@pytest.mark.parametrize("B,H,Sq,L", [(1, 6, 4481, 4481), (1, 2, 300, 129), (2, 3, 260, 200), (1, 4, 100, 128)])
+def test_ring_one_launch_splits_a_single_block(cp, B, H, Sq, L):
+    """A single block on a grid the block kernel would run on 4 waves is split at a 64-key tile
+    boundary into two halves computed in parallel and merged by their LSE (the ring's own method,
+    one level finer); the result matches the oracle, and one launch per block, to tolerance."""
+    D = 128
+    assert cp.cp_ring_attention_one_launch(cp.CP_BF16, B, H, D, Sq, [L])
+    say("one-launch split", B, H, Sq, L)
+    inp = workloads.make_custom(B, H, D, Sq, (L,), "bf16", seed=900 + L + Sq)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    for rep in range(2):
+        (o1, l1), (o0, l0) = _ring_pair(cp, q, [k], [v], inp.workload.scale)
+        assert_close("split vs per-block out", o1.cpu().numpy(), o0.cpu().numpy(), TOL["bf16"]["o"])
+        assert_close("split vs per-block lse", l1.cpu().numpy(), l0.cpu().numpy(), TOL["bf16"]["lse"])
+    rows = workloads.sample_rows(Sq, 64, seed=L, must=_edges(Sq))
+    o_ref, l_ref = oracle.attention(inp.q[:, rows], inp.k, inp.v, inp.workload.scale)
+    assert_close("out", o1.cpu().numpy()[:, rows], o_ref, TOL["bf16"]["o"])
+    assert_close("lse", l1.cpu().numpy()[:, :, rows], l_ref, TOL["bf16"]["lse"])
