@@ -57,6 +57,12 @@
 //     contiguous 1 KB DMA loads and need no transposition (the ping-pong
 //     kernel keeps no raw V stages). Same operands, same order: the results
 //     are bit-identical to unpacked V.
+//   * One launch for a ring (RING, ping-pong shape, packed V): workgroups
+//     are block-major, each computes one block's partial for one query tile,
+//     and the epilogues of a tile merge into (out, lse) in block order, each
+//     waiting for a per-tile flag that the previous block's workgroup sets
+//     after its stores. Same epilogue arithmetic in the same order as one
+//     launch per block, so the same bits.
 //   * Workgroups are remapped so that consecutive query tiles of one head run
 //     on the same XCD (each XCD has its own L2) and share its K/V reads.
 //   * Keys beyond Skv are never read: the buffer descriptor's range ends at
