@@ -7,12 +7,14 @@
 // so that it stays within float32 rounding of the exact result. It serves
 // small float32 problems; large workloads use the bf16 matrix-core kernel.
 //
-// Layout: a workgroup of 128 threads owns 64 query rows of one (b, h); each
-// row is split over a thread pair, each thread holding half of D of the
-// query and of the output accumulator. K/V are staged through LDS in tiles of
-// 32 keys (zero-filled past Skv). Scores of a tile are formed by a partial
-// dot product per thread plus one exchange with the partner lane; both
-// partners then hold identical scores, maxima and sums.
+// Layout: a workgroup of 128 threads owns 16 query rows of one (b, h); each
+// row is split over a group of 8 consecutive lanes, each holding an eighth of
+// D of the query and of the output accumulator. K/V are staged through LDS in
+// tiles of 64 keys (zero-filled past Skv) and read back as float4 vectors.
+// Scores of a tile are partial dot products per lane plus three exchanges
+// within the group (lane ^ 1, ^ 2, ^ 4), after which all eight lanes hold the
+// same scores, maxima and sums. The work per lane, which sets the latency of
+// these small problems, is an eighth of the row's.
 #include <stdint.h>
 
 #include "kernels.h"
@@ -24,9 +26,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kRows = 64;   // query rows per workgroup
-constexpr int kTile = 32;   // keys per LDS tile
+constexpr int kRows = 16;   // query rows per workgroup
+constexpr int kTile = 64;   // keys per LDS tile
 constexpr int kThreads = 128;
+constexpr int kLanesPerRow = 8;
 
 struct Params {
   const float* q;
@@ -43,28 +46,28 @@ struct Params {
 
 template <int D, bool ACC>
 __global__ void __launch_bounds__(kThreads) attn_fwd_f32_kernel(Params p) {
-  constexpr int DH = D / 2;
+  constexpr int DQ = D / kLanesPerRow;  // dims per lane
   __shared__ __attribute__((aligned(16))) float Ks[kTile][D];
   __shared__ __attribute__((aligned(16))) float Vs[kTile][D];
 
   const int tid = threadIdx.x;
-  const int qi = tid >> 1, half = tid & 1;
+  const int qi = tid / kLanesPerRow, part = tid % kLanesPerRow;
   const int qt = blockIdx.x % p.n_qt;
   const int bh = blockIdx.x / p.n_qt;
   const int h = bh % p.H, b = bh / p.H;
   const int row = qt * kRows + qi;
 
-  float qv[DH], o[DH];
+  float qv[DQ], o[DQ];
   {
-    const float* qp = p.q + b * p.q_sb + (int64_t)row * p.q_ss + h * p.q_sh + half * DH;
+    const float* qp = p.q + b * p.q_sb + (int64_t)row * p.q_ss + h * p.q_sh + part * DQ;
 #pragma unroll
-    for (int i = 0; i < DH; i += 4) {
+    for (int i = 0; i < DQ; i += 4) {
       const f32x4 x = (row < p.Sq) ? *reinterpret_cast<const f32x4*>(qp + i) : f32x4{};
       qv[i] = x[0]; qv[i + 1] = x[1]; qv[i + 2] = x[2]; qv[i + 3] = x[3];
     }
   }
 #pragma unroll
-  for (int i = 0; i < DH; ++i) o[i] = 0.f;
+  for (int i = 0; i < DQ; ++i) o[i] = 0.f;
   float m = -INFINITY, l = 0.f;
 
   const float* kbase = p.k + b * p.kv_sb + h * p.kv_sh;
@@ -72,7 +75,9 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_f32_kernel(Params p) {
 
   for (int key0 = 0; key0 < p.Skv; key0 += kTile) {
     __syncthreads();
-    for (int idx = tid; idx < kTile * (D / 4); idx += kThreads) {
+#pragma unroll
+    for (int it = 0; it < kTile * (D / 4) / kThreads; ++it) {
+      const int idx = tid + it * kThreads;
       const int n = idx / (D / 4), c4 = idx % (D / 4);
       const int key = key0 + n;
       f32x4 kx{}, vx{};
@@ -89,10 +94,19 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_f32_kernel(Params p) {
     float mt = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
-      float part = 0.f;
+      float part_sum = 0.f;
 #pragma unroll
-      for (int i = 0; i < DH; ++i) part = fmaf(qv[i], Ks[j][half * DH + i], part);
-      const float full = part + __shfl_xor(part, 1);
+      for (int i = 0; i < DQ; i += 4) {
+        const f32x4 kx = *reinterpret_cast<const f32x4*>(&Ks[j][part * DQ + i]);
+        part_sum = fmaf(qv[i], kx[0], part_sum);
+        part_sum = fmaf(qv[i + 1], kx[1], part_sum);
+        part_sum = fmaf(qv[i + 2], kx[2], part_sum);
+        part_sum = fmaf(qv[i + 3], kx[3], part_sum);
+      }
+      // the group's eight partial sums, added pairwise: the same value in every lane
+      const float s01 = part_sum + __shfl_xor(part_sum, 1);
+      const float s03 = s01 + __shfl_xor(s01, 2);
+      const float full = s03 + __shfl_xor(s03, 4);
       sc[j] = (key0 + j < p.Skv) ? full * p.c : -INFINITY;
       mt = fmaxf(mt, sc[j]);
     }
@@ -101,20 +115,26 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_f32_kernel(Params p) {
     m = m_new;
     l *= alpha;
 #pragma unroll
-    for (int i = 0; i < DH; ++i) o[i] *= alpha;
+    for (int i = 0; i < DQ; ++i) o[i] *= alpha;
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
       const float pj = __builtin_amdgcn_exp2f(sc[j] - m_new);
       l += pj;
 #pragma unroll
-      for (int i = 0; i < DH; ++i) o[i] = fmaf(pj, Vs[j][half * DH + i], o[i]);
+      for (int i = 0; i < DQ; i += 4) {
+        const f32x4 vx = *reinterpret_cast<const f32x4*>(&Vs[j][part * DQ + i]);
+        o[i] = fmaf(pj, vx[0], o[i]);
+        o[i + 1] = fmaf(pj, vx[1], o[i + 1]);
+        o[i + 2] = fmaf(pj, vx[2], o[i + 2]);
+        o[i + 3] = fmaf(pj, vx[3], o[i + 3]);
+      }
     }
   }
 
   if (row >= p.Sq) return;
   const float lse2 = m + __builtin_amdgcn_logf(l);
   const float inv = 1.0f / l;
-  float* orow = p.out + b * p.o_sb + (int64_t)row * p.o_ss + h * p.o_sh + half * DH;
+  float* orow = p.out + b * p.o_sb + (int64_t)row * p.o_ss + h * p.o_sh + part * DQ;
   float* lrow = p.lse + ((int64_t)b * p.H + h) * p.Sq + row;
   if constexpr (ACC) {
     const float la2 = *lrow * kLog2e;
@@ -124,20 +144,22 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_f32_kernel(Params p) {
     const float tot = wa + wb;
     const float fa = wa / tot, fb = (wb / tot) * inv;
 #pragma unroll
-    for (int i = 0; i < DH; i += 4) {
+    for (int i = 0; i < DQ; i += 4) {
       f32x4* dst = reinterpret_cast<f32x4*>(orow + i);
       const f32x4 ob = {o[i], o[i + 1], o[i + 2], o[i + 3]};
       const f32x4 oa = *dst;
       *dst = (wa > 0.f) ? (fa * oa + fb * ob) : (fb * ob);
     }
-    if (half == 0) *lrow = (M + __builtin_amdgcn_logf(tot)) * kLn2;
+    // every lane of the group read lse above; only lane 0 writes it, after
+    // the group's reads (they come first in program order within the wave)
+    if (part == 0) *lrow = (M + __builtin_amdgcn_logf(tot)) * kLn2;
   } else {
 #pragma unroll
-    for (int i = 0; i < DH; i += 4) {
+    for (int i = 0; i < DQ; i += 4) {
       const f32x4 ob = {o[i], o[i + 1], o[i + 2], o[i + 3]};
       *reinterpret_cast<f32x4*>(orow + i) = ob * inv;
     }
-    if (half == 0) *lrow = lse2 * kLn2;
+    if (part == 0) *lrow = lse2 * kLn2;
   }
 }
 
