@@ -26,7 +26,11 @@ the launch stream; ``cpu_baseline`` times the float64 CPU oracle on a bounded
 sample of the same workload on this host. ``backward`` times the ring
 share's backward (bf16 workloads) on the same inputs, outside the step.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Before the W warm-up steps, untimed steps run for --prewarm-seconds (default
+1 s) so that the K timed steps see the clock the GPU holds under sustained
+load rather than its ramp; the JSON line reports how many ran.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-seconds S] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -56,8 +60,11 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prewarm-seconds", type=float, default=1.0,
+                    help="untimed steps run for this long before the warm-up steps, so that the timed "
+                         "steps see the clock the GPU settles at under sustained load (0 disables it)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=[w.name for w in workloads.WORKLOADS])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample (0 disables it)")
@@ -427,6 +434,16 @@ def main():
     log(f"[bench] workload {w.name}: B={w.B} H={w.attn_H} D={w.D} Sq={w.Sq} blocks={list(w.block_lens)}")
     prob = Problem(w, args.separate_merge, packed_v=not args.unpacked_v)
 
+    # A burst of a few milliseconds runs on a GPU that is still changing its clock: the first
+    # ~30 ms of steps of the FLUX ring-2 share take ~15% longer than later ones. Untimed steps
+    # for prewarm_seconds first, then the warm-up steps, so the timed steps are steady-state.
+    prewarm_steps, pw0 = 0, time.perf_counter()
+    while time.perf_counter() - pw0 < args.prewarm_seconds:
+        for _ in range(10):
+            prob.step()
+        prewarm_steps += 10
+        torch.cuda.synchronize()
+    prewarm_s = time.perf_counter() - pw0
     for _ in range(args.warmup):
         prob.step()
     torch.cuda.synchronize()
@@ -476,6 +493,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm": {"seconds": round(prewarm_s, 3), "steps": prewarm_steps},
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
