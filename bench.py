@@ -30,7 +30,11 @@ Before the W warm-up steps, untimed steps run for --prewarm-seconds (default
 1 s) so that the K timed steps see the clock the GPU holds under sustained
 load rather than its ramp; the JSON line reports how many ran.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-seconds S] [--workload NAME]
+``--graph`` captures the K timed steps into one HIP graph and times its
+replay: for launch-bound workloads (the tiny float32 ring) the host's
+enqueue rate, not the GPU, otherwise sets the step time.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-seconds S] [--graph] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -68,6 +72,9 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=[w.name for w in workloads.WORKLOADS])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample (0 disables it)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K timed steps into one HIP graph and time its replay (launch-bound "
+                         "workloads: the host no longer enqueues each launch)")
     ap.add_argument("--unpacked-v", action="store_true",
                     help="pass V as [B, S, H, D] instead of packed (bf16 workloads)")
     ap.add_argument("--separate-merge", action="store_true",
@@ -201,37 +208,65 @@ class Problem:
         if w.ulysses_degree > 1:
             cp.cp_ulysses_regroup(self.out, self.back, w.ulysses_degree, cp.CP_REGROUP_HEAD_TO_SEQ)
 
-    def time_block_kernels(self, reps: int):
+    def _timed_passes(self, one_pass, reps: int, graph: bool) -> float:
+        """ms for `reps` back-to-back calls of one_pass between two HIP events on the launch
+        stream; with graph, the reps are captured as one HIP graph whose replay is timed."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        one_pass()
+        torch.cuda.synchronize()
+        g = None
+        if graph:
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                one_pass()
+            stream.wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    one_pass()
+            g.replay()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if g is not None:
+            g.replay()
+        else:
+            for _ in range(reps):
+                one_pass()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def time_block_kernels(self, reps: int, graph: bool = False):
         """Average duration of one block-attention launch, as the ring issues them.
 
         Block 0 is written, later blocks are merged in by the kernel epilogue.
         The launches of `reps` ring passes run back to back between two HIP
-        events on the stream they are launched on; the mean is the region's
-        time over the number of launches. Where the step runs the ring as one
+        events on the stream they are launched on (with graph, captured as one
+        HIP graph whose replay is timed); the mean is the region's time over
+        the number of launches. Where the step runs the ring as one
         launch (packed V, cp_ring_attention_one_launch), that launch (and the
-        flag reset before it) is what is timed, with the flops of all blocks.
+        flag reset before it) is what is timed, with the flops of all blocks; so
+        too for a float32 ring of 2 to 4 non-empty blocks, which always runs as
+        one launch.
         """
-        torch, cp, w = self.torch, self.cp, self.w
-        stream = torch.cuda.current_stream()
+        cp, w = self.cp, self.w
         blocks = [(i, kb, vb) for i, (kb, vb) in enumerate(zip(self.kb, self.vb_att)) if kb.shape[1] > 0]
         lens = [kb.shape[1] for kb in self.kb]
-        if self.packed and self.ws is not None and cp.cp_ring_attention_one_launch(
-                cp.CP_BF16, w.B, w.attn_H, w.D, w.Sq, lens):
+        f32_one = (w.dtype == "f32" and not self.flags & cp.CP_RING_SEPARATE_MERGE
+                   and 2 <= sum(1 for L in lens if L > 0) <= 4)
+        if f32_one or (self.packed and self.ws is not None and cp.cp_ring_attention_one_launch(
+                cp.CP_BF16, w.B, w.attn_H, w.D, w.Sq, lens)):
             # the step runs the whole ring as one launch (after a flag reset): time that
             def one_pass():
                 cp.cp_ring_attention(self.q_att, self.kb, self.vb_att, self.out, self.lse, scale=w.scale,
                                      flags=self.flags, workspace=self.ws)
 
-            one_pass()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                one_pass()
-            e1.record(stream)
-            torch.cuda.synchronize()
+            ms = self._timed_passes(one_pass, reps, graph)
             self.block_launch = "one launch for all blocks"
-            return e0.elapsed_time(e1) / reps, w.flops
+            return ms / reps, w.flops
         self.block_launch = "one launch per block"
 
         def one_pass():
@@ -239,16 +274,9 @@ class Problem:
                 cp.cp_attn_block_fwd(self.q_att, kb, vb, self.out, self.lse, scale=w.scale,
                                      flags=cp.CP_BLOCK_ACCUMULATE if i > 0 else 0)
 
-        one_pass()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            one_pass()
-        e1.record(stream)
-        torch.cuda.synchronize()
+        ms = self._timed_passes(one_pass, reps, graph)
         flops = sum(4 * w.B * w.attn_H * w.Sq * kb.shape[1] * w.D for _, kb, _ in blocks) / len(blocks)
-        return e0.elapsed_time(e1) / (reps * len(blocks)), flops
+        return ms / (reps * len(blocks)), flops
 
 
     def time_backward(self, reps: int):
@@ -448,12 +476,30 @@ def main():
         prob.step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    graph = None
+    if args.graph:
+        # the library only enqueues kernels on the caller's stream: capture the K steps as
+        # one graph (after a run on the capture stream), replay it once untimed
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            prob.step()
+        stream.wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                prob.step()
+        graph.replay()
+        torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for _ in range(args.steps):
-        prob.step()
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(args.steps):
+            prob.step()
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -461,7 +507,7 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us/step)")
     tflops = w.flops / (ms_step * 1e-3) / 1e12
 
-    k_ms, k_flops = prob.time_block_kernels(max(5, min(args.steps, 50)))
+    k_ms, k_flops = prob.time_block_kernels(max(5, min(args.steps, 50)), graph=args.graph)
     achieved = k_flops / (k_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     log(f"[bench] block kernel: {k_ms * 1e3:.1f} us/launch, {achieved:.1f} TFLOP/s ({achieved / peak:.1%} of {peak})")
@@ -494,6 +540,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "prewarm": {"seconds": round(prewarm_s, 3), "steps": prewarm_steps},
+        "launch": "hip graph of the timed steps" if args.graph else "eager",
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -401,6 +401,34 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
       return hip_status(cpattn::launch_ring_bf16(a, rb, ws_flags, s), "attn_fwd_bf16 (ring)");
     }
   }
+  if (dtype == CP_F32 && !separate) {
+    // 2..4 non-empty float32 blocks: one launch computes and merges them all
+    const void* kb[cpattn::kMaxF32RingBlocks];
+    const void* vb[cpattn::kMaxF32RingBlocks];
+    int len[cpattn::kMaxF32RingBlocks];
+    int n = 0;
+    for (int i = 0; i < ring_degree && n <= cpattn::kMaxF32RingBlocks; ++i) {
+      if (block_len[i] == 0) continue;
+      if (n < cpattn::kMaxF32RingBlocks) {
+        kb[n] = k_blocks[i];
+        vb[n] = v_blocks[i];
+        len[n] = block_len[i];
+      }
+      ++n;
+    }
+    if (n >= 2 && n <= cpattn::kMaxF32RingBlocks) {
+      cpattn::FwdArgs a;
+      a.q = q; a.k = nullptr; a.v = nullptr; a.out = out; a.lse = lse;
+      a.qs = qs; a.kvs = kvs; a.os = os;
+      a.B = B; a.H = H; a.D = D; a.Sq = Sq; a.Skv = 0;
+      a.scale = scale;
+      a.accumulate = false;
+      a.waves = 0;
+      a.v_packed = false;
+      const cpattn::RingBlocks rb{n, kb, vb, len, nullptr, nullptr};
+      return hip_status(cpattn::launch_ring_f32(a, rb, s), "attn_fwd_f32 (ring)");
+    }
+  }
   const Strides ws_s = resolve(nullptr, Sq, H, D);
   bool have = false;  // does (out, lse) hold a partial yet?
   for (int i = 0; i < ring_degree; ++i) {

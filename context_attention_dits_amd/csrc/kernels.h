@@ -105,6 +105,13 @@ int64_t ring_flag_count(int B, int H, int Sq);
 hipError_t launch_ring_bf16(const FwdArgs& a, const RingBlocks& rb, int* flags, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
+// One launch for a ring of 2..kMaxF32RingBlocks non-empty float32 blocks
+// (rb.vt0 / rb.vnt unused; a.k, a.v, a.Skv and a.accumulate not used): each
+// workgroup computes every block's partial for its query rows and merges them
+// in block order into (out, lse), which are overwritten.
+constexpr int kMaxF32RingBlocks = 4;
+hipError_t launch_ring_f32(const FwdArgs& a, const RingBlocks& rb, hipStream_t stream);
+
 // out = 0, lse = -inf for every (b, s, h): attention over an empty key set.
 hipError_t launch_fill_empty(float* out, Strides os, float* lse, int B, int H, int Sq, int D,
                              hipStream_t stream);

@@ -186,6 +186,10 @@ size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned fl
  * tile boundary into two halves run the same way (two partials merged by
  * their LSE: equal to one pass up to rounding). Calls that share a workspace
  * must not overlap.
+ * CP_F32 with 2 to 4 non-empty blocks (and no CP_RING_SEPARATE_MERGE) also
+ * runs as one launch, without workspace: each workgroup computes every
+ * block's partial for its query rows and merges them in block order with the
+ * same LSE arithmetic as the per-block launches.
  * If every block is empty the result is out = 0, lse = -inf.
  */
 cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides,
