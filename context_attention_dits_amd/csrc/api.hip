@@ -7,10 +7,15 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <string>
 
 #include "cp_attn.h"
 #include "kernels.h"
+
+#ifndef CP_BWD_SIDE_STREAM
+#define CP_BWD_SIDE_STREAM 1  // backward: dq kernels on a second stream, concurrent with dkv (0: one stream)
+#endif
 
 namespace {
 
@@ -491,11 +496,89 @@ cp_status_t check_bwd_common(const char* fn, int dtype, int B, int H, int D, int
   return CP_OK;
 }
 
+// A second stream per device for the backward's dq kernels, which then run
+// concurrently with the dkv kernels on the caller's stream (each kind alone
+// leaves workgroup slots idle on the FLUX-sized shares). Created on first use
+// outside graph capture (non-blocking, default priority) and kept for the
+// life of the process. A call forks it from the caller's stream with an event
+// and joins it back with another before returning, so the caller sees one
+// stream-ordered operation, also when capturing a graph (the side stream then
+// joins the capture through the fork event). The fork-join sequence is
+// enqueued under a lock, since the events are shared per device.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;  // creation failed once: run single-stream from then on
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// Whether the backward's dq and dkv kernels should share the GPU. Each kind
+// runs 4-wave workgroups, two per CU. Measured on MI355X, running them
+// concurrently pays when a kernel alone would leave a quarter or more of its
+// last round of workgroup slots idle (ring-anything share: 1018 -> 855 us per
+// pass; USP share 430 -> 343 us), and costs where every round is full (32k
+// ring-4 share: 10.56 -> 11.38 ms, the two kernels' workgroups then compete
+// for each XCD's L2) or nearly so (FLUX ring-2 and Ulysses-2 shares: within
+// 2%). n_dq, n_dkv: workgroups of one launch of each kernel.
+bool bwd_concurrent(int64_t n_dq, int64_t n_dkv) {
+  if (!CP_BWD_SIDE_STREAM) return false;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return false;
+  }
+  const int64_t slots = 2 * (int64_t)cus;
+  auto idle_quarter = [&](int64_t n) {
+    if (n <= 0) return false;
+    const int64_t cap = (n + slots - 1) / slots * slots;
+    return 4 * (cap - n) >= cap;
+  };
+  return idle_quarter(n_dq) || idle_quarter(n_dkv);
+}
+
+// Under g_side_mu: the device's side stream forked from s, or nullptr to run
+// everything on s (no device id, creation failed, or first use while s is
+// being captured).
+hipStream_t side_fork(hipStream_t s) {
+  if (!CP_BWD_SIDE_STREAM) return nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (ss.failed) return nullptr;
+  if (ss.s == nullptr) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      ss.failed = true;
+      (void)hipGetLastError();
+      return nullptr;
+    }
+  }
+  if (hipEventRecord(ss.fork, s) != hipSuccess) return nullptr;
+  if (hipStreamWaitEvent(ss.s, ss.fork, 0) != hipSuccess) return nullptr;
+  return ss.s;
+}
+
+// Under g_side_mu: s waits for everything enqueued on the side stream.
+hipError_t side_join(hipStream_t s) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  SideStream& ss = g_side[dev];
+  if ((e = hipEventRecord(ss.join, ss.s)) != hipSuccess) return e;
+  return hipStreamWaitEvent(s, ss.join, 0);
+}
+
 // Arguments of one block's backward once the common checks passed.
 cp_status_t run_block_bwd(const void* q, Strides qs, const void* k, const void* v, Strides kvs, int B, int H,
                           int D, int Sq, int Skv, float scale, bool accumulate_dq, const float* lse,
                           const BwdWorkspace& w, float* dq, Strides dqs, float* dk, float* dv, Strides dkvs,
-                          hipStream_t stream) {
+                          hipStream_t stream, hipStream_t dq_stream = nullptr) {
   if (Skv == 0 && accumulate_dq) return CP_OK;  // no keys: nothing to add
   cpattn::BwdArgs a;
   a.q = q; a.k = k; a.v = v;
@@ -505,6 +588,7 @@ cp_status_t run_block_bwd(const void* q, Strides qs, const void* k, const void* 
   a.B = B; a.H = H; a.D = D; a.Sq = Sq; a.Skv = Skv;
   a.scale = scale;
   a.accumulate_dq = accumulate_dq;
+  a.dq_stream = dq_stream;
   return hip_status(cpattn::launch_attn_bwd_bf16(a, stream), "attn_bwd_bf16");
 }
 
@@ -577,8 +661,20 @@ cp_status_t cp_attn_block_bwd(const void* q, const int64_t* q_strides, const voi
   BwdWorkspace w{nullptr, nullptr};  // with no queries the kernels read no dO and no delta
   if (Sq > 0 && (st = bwd_workspace(fn, const_cast<void*>(workspace), workspace_bytes, B, H, Sq, D, &w)) != CP_OK)
     return st;
-  return run_block_bwd(q, qs, k, v, kvs, B, H, D, Sq, Skv, scale, (flags & CP_BWD_ACCUMULATE_DQ) != 0, lse, w,
-                       dq, dqs, dk, dv, dkvs, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (Sq == 0 || Skv == 0)  // one kernel at most
+    return run_block_bwd(q, qs, k, v, kvs, B, H, D, Sq, Skv, scale, (flags & CP_BWD_ACCUMULATE_DQ) != 0, lse, w,
+                         dq, dqs, dk, dv, dkvs, s);
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  const int64_t bh = (int64_t)B * H;
+  hipStream_t side = bwd_concurrent(bh * ((Sq + 127) / 128), bh * ((Skv + 127) / 128)) ? side_fork(s) : nullptr;
+  st = run_block_bwd(q, qs, k, v, kvs, B, H, D, Sq, Skv, scale, (flags & CP_BWD_ACCUMULATE_DQ) != 0, lse, w, dq,
+                     dqs, dk, dv, dkvs, s, side);
+  if (side != nullptr) {
+    const cp_status_t sj = hip_status(side_join(s), "attn_bwd_bf16 (join)");
+    if (st == CP_OK) st = sj;
+  }
+  return st;
 }
 
 cp_status_t cp_ring_attention_bwd(const void* q, const int64_t* q_strides, const void* const* k_blocks,
@@ -638,12 +734,26 @@ cp_status_t cp_ring_attention_bwd(const void* q, const int64_t* q_strides, const
       return st;
   }  // with no queries every dK, dV is zero (the dkv kernel still writes them) and no workspace is read
   bool have_dq = false;
-  for (int i = 0; i < ring_degree; ++i) {
-    if (block_len[i] == 0) continue;
-    st = run_block_bwd(q, qs, k_blocks[i], v_blocks[i], kvs, B, H, D, Sq, block_len[i], scale, have_dq, lse, w, dq,
-                       dqs, dk_blocks[i], dv_blocks[i], dkvs, s);
+  {
+    // dq kernels (a chain: each block adds into dQ) on the side stream, dkv
+    // kernels on s; with no queries only the dkv kernels run
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    int longest = 0;
+    for (int i = 0; i < ring_degree; ++i) longest = block_len[i] > longest ? block_len[i] : longest;
+    const int64_t bh = (int64_t)B * H;
+    const bool conc = Sq > 0 && bwd_concurrent(bh * ((Sq + 127) / 128), bh * ((longest + 127) / 128));
+    hipStream_t side = conc ? side_fork(s) : nullptr;
+    for (int i = 0; i < ring_degree && st == CP_OK; ++i) {
+      if (block_len[i] == 0) continue;
+      st = run_block_bwd(q, qs, k_blocks[i], v_blocks[i], kvs, B, H, D, Sq, block_len[i], scale, have_dq, lse, w,
+                         dq, dqs, dk_blocks[i], dv_blocks[i], dkvs, s, side);
+      have_dq = true;
+    }
+    if (side != nullptr) {
+      const cp_status_t sj = hip_status(side_join(s), "attn_bwd_bf16 (join)");
+      if (st == CP_OK) st = sj;
+    }
     if (st != CP_OK) return st;
-    have_dq = true;
   }
   if (!have_dq && Sq > 0)  // every block empty: dQ = 0 (the dq kernel over no keys writes zeros)
     return run_block_bwd(q, qs, nullptr, nullptr, kvs, B, H, D, Sq, 0, scale, false, lse, w, dq, dqs, nullptr,

@@ -568,10 +568,11 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
   p.n_wg = (int)n;
   if (p.n_wg > 0) {  // no queries: no dQ
+    hipStream_t sq = a.dq_stream ? a.dq_stream : stream;
     if (a.accumulate_dq) {
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), dim3(p.n_wg), dim3(NW * 64), 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), dim3(p.n_wg), dim3(NW * 64), 0, sq, p);
     } else {
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), dim3(p.n_wg), dim3(NW * 64), 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), dim3(p.n_wg), dim3(NW * 64), 0, sq, p);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -75,6 +75,10 @@ struct BwdArgs {
   int B, H, D, Sq, Skv;
   float scale;
   bool accumulate_dq;
+  // Stream of the dq kernel (nullptr: the launch stream). The dq and dkv
+  // kernels of a block read the same inputs and write disjoint outputs, so
+  // they may run concurrently; the caller orders dq_stream against stream.
+  hipStream_t dq_stream;
 };
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 // delta = rowsum(dO * O) and dO rounded to bf16 (contiguous [B, Sq, H, D]).

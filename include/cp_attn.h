@@ -331,6 +331,16 @@ cp_status_t cp_ulysses_concat_seq(const void* in, void* out, int elem_bytes, int
  * Workspace (caller-owned, 256-byte aligned): dO rounded to bfloat16
  * ([B, Sq, H, D], contiguous) and D ([B, H, Sq] float32), written by
  * cp_attn_bwd_prep and read by cp_attn_block_bwd.
+ *
+ * Streams: where one launch of the dQ kernel or of the dK/dV kernel alone
+ * would leave a quarter or more of the GPU's last round of workgroup slots
+ * idle, cp_attn_block_bwd and cp_ring_attention_bwd run the dQ kernels on a
+ * second stream that the library creates once per device (non-blocking,
+ * default priority; never while the caller's stream is capturing a graph),
+ * forked from the caller's stream by an event and joined back before the
+ * call returns. The caller sees one stream-ordered operation on its stream,
+ * also under graph capture; calls on one device from several host threads
+ * are serialised while they enqueue.
  */
 
 /* Bytes of backward workspace for these sizes (0 if any size is <= 0). */
