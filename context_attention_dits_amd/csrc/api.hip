@@ -540,12 +540,19 @@ bool bwd_concurrent(int64_t n_dq, int64_t n_dkv) {
 }
 
 // Under g_side_mu: the device's side stream forked from s, or nullptr to run
-// everything on s (no device id, creation failed, or first use while s is
-// being captured).
+// everything on s (no device id, s belongs to another device than the
+// current one, creation failed, or first use while s is being captured).
 hipStream_t side_fork(hipStream_t s) {
   if (!CP_BWD_SIDE_STREAM) return nullptr;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (s != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess || sdev != dev) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+  }
   SideStream& ss = g_side[dev];
   if (ss.failed) return nullptr;
   if (ss.s == nullptr) {
