@@ -153,6 +153,24 @@ bool one_launch_ring(int dtype, int B, int H, int D, int Sq, const int* block_le
   return n >= 2 && n <= cpattn::ring_max_blocks();
 }
 
+// Whether cp_ring_attention with packed V runs the blocks in turn within one
+// launch of the 8-wave kernel (the grid the per-block launches would run on
+// the 8-wave shape, 2 .. seq_max_blocks() non-empty blocks): saves the fixed
+// cost of every launch after the first (on the FLUX ring-2 share ~12-17 us of
+// a ~66 us launch).
+bool seq_ring(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree) {
+  if (dtype != CP_BF16 || D != 128 || B <= 0 || H <= 0 || Sq <= 0) return false;
+  const int waves = g_fwd_waves.load(std::memory_order_relaxed);
+  if (waves == 4) return false;
+  cpattn::FwdArgs a{};
+  a.B = B; a.H = H; a.D = D; a.Sq = Sq;
+  a.waves = waves;
+  if (cpattn::pick_waves(a) != 8) return false;
+  int n = 0;
+  for (int i = 0; i < ring_degree; ++i) n += block_len[i] > 0;
+  return n >= 2 && n <= cpattn::seq_max_blocks();
+}
+
 size_t partial_bytes(int B, int H, int Sq, int D) {
   return align_up((size_t)B * Sq * H * D * sizeof(float), 256) + align_up((size_t)B * H * Sq * sizeof(float), 256);
 }
@@ -177,7 +195,10 @@ int cp_ring_attention_one_launch(int dtype, int B, int H, int D, int Sq, const i
   if (block_len == nullptr || ring_degree < 1) return 0;
   for (int i = 0; i < ring_degree; ++i)
     if (block_len[i] < 0) return 0;
-  return one_launch_ring(dtype, B, H, D, Sq, block_len, ring_degree) ? 1 : 0;
+  return (one_launch_ring(dtype, B, H, D, Sq, block_len, ring_degree) ||
+          seq_ring(dtype, B, H, D, Sq, block_len, ring_degree))
+             ? 1
+             : 0;
 }
 
 int cp_attn_set_fwd_waves(int waves) {
@@ -405,6 +426,31 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
       const cpattn::RingBlocks rb{n, kb, vb, len, vt0, vnt};
       return hip_status(cpattn::launch_ring_bf16(a, rb, ws_flags, s), "attn_fwd_bf16 (ring)");
     }
+  }
+  if (packed && !separate && seq_ring(dtype, B, H, D, Sq, block_len, ring_degree)) {
+    const void* kb[16];
+    const void* vb[16];
+    int len[16], vt0[16], vnt[16];
+    int n = 0;
+    for (int i = 0; i < ring_degree && n < 16; ++i) {
+      if (block_len[i] == 0) continue;
+      kb[n] = k_blocks[i];
+      vb[n] = v_blocks[i];
+      len[n] = block_len[i];
+      vt0[n] = 0;
+      vnt[n] = (block_len[i] + 63) / 64;
+      ++n;
+    }
+    cpattn::FwdArgs a;
+    a.q = q; a.k = nullptr; a.v = nullptr; a.out = out; a.lse = lse;
+    a.qs = qs; a.kvs = kvs; a.os = os;
+    a.B = B; a.H = H; a.D = D; a.Sq = Sq; a.Skv = 0;
+    a.scale = scale;
+    a.accumulate = false;
+    a.waves = 8;
+    a.v_packed = true;
+    const cpattn::RingBlocks rb{n, kb, vb, len, vt0, vnt};
+    return hip_status(cpattn::launch_ring_seq_bf16(a, rb, s), "attn_fwd_bf16 (blocks in turn)");
   }
   if (dtype == CP_F32 && !separate) {
     // 2..4 non-empty float32 blocks: one launch computes and merges them all

@@ -92,6 +92,9 @@
 #ifndef CP_RING_SC1
 #define CP_RING_SC1 0  // one-launch ring: device-scope (1) or L2-coherent (0) out/lse accesses
 #endif
+#ifndef CP_FWD_SEQ
+#define CP_FWD_SEQ 1  // rings of 2+ blocks on the 8-wave shape: one launch, blocks in turn per workgroup
+#endif
 #ifndef CP_FWD_LAZY
 #define CP_FWD_LAZY 8.0f  // rescale threshold on the row maximum, log2 units
 #endif
@@ -218,7 +221,7 @@ struct Nothing {
   __device__ __forceinline__ void operator()(A...) const {}
 };
 
-template <int D, int QB, int NW, bool ACC, bool PACKED, bool RING>
+template <int D, int QB, int NW, bool ACC, bool PACKED, bool RING, bool SEQ = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                                amdgpu_waves_per_eu(CP_FWD_WPE)))
 attn_fwd_bf16_kernel(Params p) {
@@ -261,20 +264,38 @@ attn_fwd_bf16_kernel(Params p) {
   const int h = bh % p.H, b = bh / p.H;
   const int qrow0 = qt * C::BM + wave * (QB * 32);
 
+  // SEQ: the workgroup takes its query tile through every block in turn
+  // (block 0 written, later blocks merged by the epilogue); between blocks a
+  // workgroup barrier keeps the next block's first loads out of LDS stages the
+  // other wave group may still be reading. Each lane keeps its row's LSE (as
+  // stored) in a register; the output it merges is what the same lane wrote.
+  // Q is loaded again for every block, as by one launch per block.
+  float lse_keep[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) lse_keep[qb] = 0.f;
+  // (The block loop is a backward jump that only the SEQ instantiation has,
+  // so the other shapes compile exactly as without it.)
+  int sblk = 0;
+seq_next_block:
+  if constexpr (SEQ) {
+    blk = sblk;
+    if (sblk > 0) __syncthreads();
+  }
+
   // Kernel arguments used inside the tile loop, pinned in SGPRs: reloading
   // them from the argument segment there would make the next LDS wait also
   // wait for that scalar load.
-  int skv = RING ? p.lblk[blk] : p.Skv;
+  int skv = (RING || SEQ) ? p.lblk[blk] : p.Skv;
   float csc = p.c;
   asm volatile("" : "+s"(skv), "+s"(csc));
   const int n_tiles = (skv + C::BN - 1) / C::BN;
 
-  const uint16_t* kblock = RING ? p.kblk[blk] : p.k;
-  const uint16_t* vblock = RING ? p.vblk[blk] : p.v;
+  const uint16_t* kblock = (RING || SEQ) ? p.kblk[blk] : p.k;
+  const uint16_t* vblock = (RING || SEQ) ? p.vblk[blk] : p.v;
   const uint16_t* kbase = kblock + b * p.kv_sb + h * p.kv_sh;
   // packed V: n_tiles contiguous tiles of V_BYTES per (b, h), (b, h) in order
   // (RING: this block's tiles within its buffer's (b, h) row of vnt tiles)
-  const int64_t v_tile0 = (int64_t)bh * (RING ? p.vnt[blk] : n_tiles);
+  const int64_t v_tile0 = (int64_t)bh * ((RING || SEQ) ? p.vnt[blk] : n_tiles);
   const uint16_t* vbase = PACKED ? vblock + v_tile0 * (C::V_BYTES / 2) : vblock + b * p.kv_sb + h * p.kv_sh;
 
   // ---- Q (B operand of S^T = K Q^T): lane holds query l32, dims kk*16 + hi*8 .. +7
@@ -793,7 +814,7 @@ attn_fwd_bf16_kernel(Params p) {
   // memory. The wait is bounded; it cannot deadlock: the awaited workgroup
   // has the same index modulo u8, so it runs on the same XCD, which starts
   // workgroups in index order, and it waits only on earlier ones itself.
-  bool acc = ACC;
+  bool acc = ACC || (SEQ && sblk > 0);
   if constexpr (RING) {
     acc = blk > 0;
     if (acc) {
@@ -851,7 +872,7 @@ attn_fwd_bf16_kernel(Params p) {
       float* orow = p.out + b * p.o_sb + (int64_t)row * p.o_ss + h * p.o_sh;
       float* lrow = p.lse + ((int64_t)b * p.H + h) * p.Sq + row;
       if (acc) {
-        const float la2 = l_load(lrow) * kLog2e;
+        const float la2 = (SEQ ? lse_keep[qb] : l_load(lrow)) * kLog2e;
         const float M = fmaxf(la2, lse2);
         const float wa = fast_exp2(la2 - M);  // 0 when the accumulator is empty (-inf)
         const float wb = fast_exp2(lse2 - M);
@@ -867,7 +888,9 @@ attn_fwd_bf16_kernel(Params p) {
             const f32x4 oa = o_load(dst);
             o_store(dst, (wa > 0.f) ? (fa * oa + fb * ob) : (fb * ob));
           }
-        if (hi == 0) l_store(lrow, (M + fast_log2(tot)) * kLn2);
+        const float lse_new = (M + fast_log2(tot)) * kLn2;
+        if constexpr (SEQ) lse_keep[qb] = lse_new;
+        if (hi == 0) l_store(lrow, lse_new);
       } else {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -877,6 +900,7 @@ attn_fwd_bf16_kernel(Params p) {
                               o[qb][db][4 * g + 3]};
             o_store(orow + db * 32 + 8 * g + 4 * hi, ob * inv);
           }
+        if constexpr (SEQ) lse_keep[qb] = lse2 * kLn2;
         if (hi == 0) l_store(lrow, lse2 * kLn2);
       }
     }
@@ -886,6 +910,9 @@ attn_fwd_bf16_kernel(Params p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt: no wait
     __syncthreads();
     if (threadIdx.x == 0) __hip_atomic_store(p.flags + tile, blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if constexpr (SEQ) {
+    if (++sblk < p.n_blk) goto seq_next_block;
   }
 }
 
@@ -958,6 +985,47 @@ hipError_t launch_ring_128(const FwdArgs& a, const RingBlocks& rb, int* flags, h
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, QB, 8, false, PACKED, true>), dim3((unsigned)(u8 * rb.n)),
+                     dim3(C::NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+// One launch for a ring of blocks on the ping-pong shape, blocks in turn
+// within each workgroup (SEQ): the per-block launches' grid, block 0 written
+// and later blocks merged in the epilogue, in block order, by the workgroup
+// that owns the query tile. No flags and no workspace.
+hipError_t launch_seq_128(const FwdArgs& a, const RingBlocks& rb, hipStream_t stream) {
+  constexpr int QB = CP_FWD_QB;
+  using C = Cfg<128, QB, 8>;
+  Params p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = nullptr;
+  p.v = nullptr;
+  p.out = a.out;
+  p.lse = a.lse;
+  p.q_sb = a.qs.b; p.q_ss = a.qs.s; p.q_sh = a.qs.h;
+  p.kv_sb = a.kvs.b; p.kv_ss = a.kvs.s; p.kv_sh = a.kvs.h;
+  p.o_sb = a.os.b; p.o_ss = a.os.s; p.o_sh = a.os.h;
+  p.B = a.B; p.H = a.H; p.Sq = a.Sq; p.Skv = 0;
+  p.n_qt = (a.Sq + C::BM - 1) / C::BM;
+  const int64_t n_wg = (int64_t)p.n_qt * a.H * a.B;
+  if (rb.n < 1 || rb.n > kMaxRingBlocks || n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (a.accumulate || !a.v_packed) return hipErrorInvalidValue;
+  p.n_wg = (int)n_wg;
+  p.u8 = 0;
+  p.n_blk = rb.n;
+  p.spin_limit = 0;
+  p.flags = nullptr;
+  p.c = a.scale * kLog2e;
+  for (int i = 0; i < kMaxRingBlocks; ++i) {
+    const bool in = i < rb.n;
+    if (in && rb.len[i] < 1) return hipErrorInvalidValue;
+    p.kblk[i] = in ? static_cast<const uint16_t*>(rb.k[i]) : nullptr;
+    p.vblk[i] = in ? static_cast<const uint16_t*>(rb.v[i]) + (int64_t)rb.vt0[i] * (C::V_BYTES / 2) : nullptr;
+    p.lblk[i] = in ? rb.len[i] : 0;
+    p.vnt[i] = in ? rb.vnt[i] : 0;
+  }
+  if (n_wg == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, QB, 8, false, true, false, true>), dim3((unsigned)n_wg),
                      dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
@@ -1091,6 +1159,13 @@ hipError_t launch_dn(const FwdArgs& a, hipStream_t stream) {
 // second time by a CU that has either not read the tile before or written it
 // itself since. More blocks run as one launch per block.
 int ring_max_blocks() { return CP_RING_SC1 ? kMaxRingBlocks : 3; }
+
+int seq_max_blocks() { return CP_FWD_SEQ ? kMaxRingBlocks : 0; }
+
+hipError_t launch_ring_seq_bf16(const FwdArgs& a, const RingBlocks& rb, hipStream_t stream) {
+  if (a.D != 128 || !a.v_packed || !CP_FWD_SEQ) return hipErrorInvalidValue;
+  return launch_seq_128(a, rb, stream);
+}
 
 int64_t ring_flag_count(int B, int H, int Sq) { return (int64_t)((Sq + 255) / 256) * H * B; }
 

@@ -107,6 +107,14 @@ struct RingBlocks {
 int ring_max_blocks();
 int64_t ring_flag_count(int B, int H, int Sq);
 hipError_t launch_ring_bf16(const FwdArgs& a, const RingBlocks& rb, int* flags, hipStream_t stream);
+// One launch for 2..seq_max_blocks() non-empty blocks (bf16, D = 128, packed V,
+// 8-wave shape): each workgroup takes its query tile through the blocks in
+// turn, block 0 written and later blocks merged in its epilogue (the
+// per-block launches' arithmetic in the same order: the same bits). No
+// flags; a.k, a.v, a.Skv, a.accumulate unused. seq_max_blocks() is 0 when the
+// library is built without it.
+int seq_max_blocks();
+hipError_t launch_ring_seq_bf16(const FwdArgs& a, const RingBlocks& rb, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
 // One launch for a ring of 2..kMaxF32RingBlocks non-empty float32 blocks

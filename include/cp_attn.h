@@ -186,6 +186,11 @@ size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned fl
  * tile boundary into two halves run the same way (two partials merged by
  * their LSE: equal to one pass up to rounding). Calls that share a workspace
  * must not overlap.
+ * Otherwise, with packed V on the 8-wave shape (cp_attn_fwd_waves), 2 to 16
+ * non-empty blocks run as one launch without workspace in which each
+ * workgroup takes its query tile through the blocks in order, writing block
+ * 0's partial and merging the others in its epilogue: the same bits as one
+ * launch per block.
  * CP_F32 with 2 to 4 non-empty blocks (and no CP_RING_SEPARATE_MERGE) also
  * runs as one launch, without workspace: each workgroup computes every
  * block's partial for its query rows and merges them in block order with the
@@ -247,8 +252,8 @@ cp_status_t cp_ulysses_regroup_pack_v(const void* in, int B, int S_local, int H,
                                       void* packed, size_t packed_bytes, void* stream);
 
 /* 1 if cp_ring_attention, given these sizes and block lengths with packed V
- * (CP_RING_PACKED_V) and a workspace, runs the whole ring as one launch (see
- * cp_ring_attention), else 0. A caller that packs V only for speed can use
+ * (CP_RING_PACKED_V) and a workspace, runs the whole ring as one launch
+ * (either form; see cp_ring_attention), else 0. A caller that packs V only for speed can use
  * this and cp_attn_fwd_waves to decide whether to. */
 int cp_ring_attention_one_launch(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree);
 

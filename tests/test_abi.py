@@ -360,8 +360,9 @@ def test_ring_one_launch_workspace_rules(lib):
 
 
 def test_ring_one_launch_query(lib):
-    """Which packed rings run as one launch: 2 or 3 non-empty blocks, bf16, D = 128, on grids the
-    per-block launches would run on the 4-wave kernel."""
+    """Which packed rings run as one launch (bf16, D = 128): 2 or 3 non-empty blocks in parallel
+    on grids the per-block launches would run on the 4-wave kernel (one block: split in two), and
+    2 to 16 non-empty blocks in turn per workgroup on the 8-wave shape."""
     def q(dtype, B, H, D, Sq, lens):
         arr = (ctypes.c_int * len(lens))(*lens)
         return lib.cp_ring_attention_one_launch(dtype, B, H, D, Sq, arr, len(lens))
@@ -369,9 +370,12 @@ def test_ring_one_launch_query(lib):
     try:
         assert q(1, 2, 24, 128, 1536, [1536, 1536, 1535]) == 1   # ring-anything share
         assert q(1, 1, 12, 128, 2304, [2304, 2304]) == 1         # USP share
-        assert q(1, 1, 24, 128, 2304, [2304, 2304]) == 0         # FLUX ring-2: 8-wave per block
+        assert q(1, 1, 24, 128, 2304, [2304, 2304]) == 1         # FLUX ring-2: 8-wave, blocks in turn
+        assert q(1, 1, 24, 128, 2304, [2304] * 4) == 1           # 8-wave: up to 16 blocks in turn
+        assert q(1, 1, 24, 128, 2304, [2304] * 16 + [0]) == 1
+        assert q(1, 1, 24, 128, 2304, [2304] * 17) == 0          # more: one launch per block
         assert q(1, 2, 24, 128, 1536, [1536, 0, 1535]) == 1      # empty blocks do not count
-        assert q(1, 2, 24, 128, 1536, [1536] * 4) == 0           # more than 3 blocks
+        assert q(1, 2, 24, 128, 1536, [1536] * 4) == 0           # 4-wave grid: more than 3 blocks
         assert q(1, 2, 24, 128, 1536, [1536, 0, 0]) == 1         # one block: split in two halves
         assert q(1, 1, 6, 128, 4481, [4481]) == 1                # the Ulysses Anything share, split
         assert q(1, 1, 12, 128, 4608, [4608]) == 0               # Ulysses-2: 8-wave per block

@@ -1,0 +1,107 @@
+"""GPU parity of the ring run as one launch with the blocks in turn per workgroup.
+
+With packed V on the 8-wave (ping-pong) shape, cp_ring_attention runs 2 to 16
+non-empty blocks as one launch in which each workgroup takes its query tile
+through the blocks in order: block 0's partial is written, each later block is
+merged into (out, lse) by the same epilogue arithmetic as one launch per block.
+So the result must equal the per-block launches bit for bit, and the float64
+oracle within the bf16 tolerances (out 1e-2, LSE 1e-3). Small shapes force the
+8-wave shape and pass no workspace (with a workspace and a forced 8-wave shape,
+the other one-launch form, partials in parallel, is taken); the FLUX ring-2
+share takes this path with the library's own shape choice. Cases: ragged query
+and key tails, one-key and empty blocks, 5 and 16 blocks, and 17 blocks, which
+run one launch per block.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import TOL, assert_close, dev, fwd_waves, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def cp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import context_attention_dits_amd as m
+    m.load()  # raises if the HIP library is missing: no fallback
+    return m
+
+
+def _per_block(cp, q, kb, vp, scale):
+    B, Sq, H, D = q.shape
+    out = torch.empty((B, Sq, H, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
+    first = True
+    for k, v in zip(kb, vp):
+        if k.shape[1] == 0:
+            continue
+        cp.cp_attn_block_fwd(q, k, v, out, lse, scale=scale, flags=0 if first else cp.CP_BLOCK_ACCUMULATE)
+        first = False
+    return out, lse
+
+
+CASES = [
+    # B, H, D, Sq, block_lens
+    (1, 3, 128, 300, (256, 200)),
+    (2, 2, 128, 513, (64, 130, 1)),
+    (1, 1, 128, 100, (0, 70, 0, 31)),
+    (1, 2, 128, 257, (128, 128, 128, 128, 128)),
+    (1, 2, 128, 64, (64,) * 16),
+    (1, 1, 128, 40, (33,) * 17),
+]
+
+
+@pytest.mark.parametrize("B,H,D,Sq,lens", CASES)
+def test_seq_ring_equals_per_block(cp, B, H, D, Sq, lens):
+    say("seq ring", B, H, D, Sq, lens)
+    inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=5000 + B + H + Sq + sum(lens))
+    scale = inp.workload.scale
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    offs = workloads.block_offsets(lens)
+    kb = [k[:, o:o + L] for o, L in zip(offs, lens)]
+    vp = [cp.pack_v(v[:, o:o + L].contiguous()) for o, L in zip(offs, lens)]
+    anything = len(set(lens)) > 1 or 0 in lens
+    flags = cp.CP_RING_ANYTHING if anything else 0
+    with fwd_waves(cp, 8):
+        one = cp.cp_ring_attention_one_launch(cp.CP_BF16, B, H, D, Sq, lens)
+        assert one == (2 <= sum(1 for L in lens if L) <= 16), one
+        out = torch.empty((B, Sq, H, D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
+        cp.cp_ring_attention(q, kb, vp, out, lse, scale=scale, flags=flags)  # no workspace
+        out_b, lse_b = _per_block(cp, q, kb, vp, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_b) and torch.equal(lse, lse_b), \
+        (float((out - out_b).abs().max()), float((lse - lse_b).abs().max()))
+    say("one launch equals the per-block launches bit for bit")
+    o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, scale)
+    assert_close("out", out.cpu().numpy(), o_ref, TOL["bf16"]["o"])
+    assert_close("lse", lse.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
+
+
+def test_seq_ring_flux_ring2_share(cp):
+    """The FLUX 1024px ring-2 share (216 workgroups) takes this path on the library's own shape
+    choice; bit-equal to the per-block launches, and sampled rows against the oracle."""
+    w = workloads.by_name("flux1024_ring2_bf16")
+    say("seq ring flux ring-2 share")
+    inp = workloads.make_inputs(w)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    offs = workloads.block_offsets(w.block_lens)
+    kb = [k[:, o:o + L] for o, L in zip(offs, w.block_lens)]
+    vp = [cp.pack_v(v[:, o:o + L].contiguous()) for o, L in zip(offs, w.block_lens)]
+    assert cp.cp_attn_fwd_waves(w.B, w.H, w.D, w.Sq) == 8
+    assert cp.cp_ring_attention_one_launch(cp.CP_BF16, w.B, w.H, w.D, w.Sq, w.block_lens)
+    out, lse = cp.ring_attention(q, kb, vp, scale=w.scale)
+    out_b, lse_b = _per_block(cp, q, kb, vp, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_b) and torch.equal(lse, lse_b)
+    rows = np.random.default_rng(3).choice(w.Sq, 24, replace=False)
+    rows = np.concatenate([rows, [0, w.Sq - 1]])
+    o_ref, l_ref = oracle.attention(inp.q[:, rows], inp.k, inp.v, w.scale)
+    assert_close("out rows", out.cpu().numpy()[:, rows], o_ref, TOL["bf16"]["o"])
+    assert_close("lse rows", lse.cpu().numpy()[:, :, rows], l_ref, TOL["bf16"]["lse"])
