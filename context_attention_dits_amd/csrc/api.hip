@@ -13,6 +13,9 @@
 #include "cp_attn.h"
 #include "kernels.h"
 
+#ifndef CP_BWD_MULTI
+#define CP_BWD_MULTI 1  // ring backward: dQ over all blocks in one launch, dK/dV of all blocks in one grid
+#endif
 #ifndef CP_BWD_SIDE_STREAM
 #define CP_BWD_SIDE_STREAM 1  // backward: dq kernels on a second stream, concurrent with dkv (0: one stream)
 #endif
@@ -791,12 +794,53 @@ cp_status_t cp_ring_attention_bwd(const void* q, const int64_t* q_strides, const
     // dq kernels (a chain: each block adds into dQ) on the side stream, dkv
     // kernels on s; with no queries only the dkv kernels run
     std::lock_guard<std::mutex> lock(g_side_mu);
-    int longest = 0;
-    for (int i = 0; i < ring_degree; ++i) longest = block_len[i] > longest ? block_len[i] : longest;
+    int longest = 0, n_nonempty = 0;
+    for (int i = 0; i < ring_degree; ++i) {
+      longest = block_len[i] > longest ? block_len[i] : longest;
+      n_nonempty += block_len[i] > 0;
+    }
+    // Where one launch of either kernel fills its slots (no second stream), the
+    // whole ring runs as two launches (dQ through the blocks in turn, dK/dV of
+    // all blocks in one grid): FLUX ring-2 share 635 -> 608 us per pass, 32k
+    // ring-4 10.77 -> 10.65 ms. With the second stream the per-block pairs
+    // overlap better (USP share 346 us per block pair vs 384 as two launches:
+    // the long dQ workgroups hold their slots and push part of the dK/dV grid
+    // into a second round).
     const int64_t bh = (int64_t)B * H;
     const bool conc = Sq > 0 && bwd_concurrent(bh * ((Sq + 127) / 128), bh * ((longest + 127) / 128));
+    const bool multi =
+        CP_BWD_MULTI && !conc && Sq > 0 && n_nonempty >= 2 && n_nonempty <= cpattn::kMaxBwdBlocks;
     hipStream_t side = conc ? side_fork(s) : nullptr;
-    for (int i = 0; i < ring_degree && st == CP_OK; ++i) {
+    if (multi) {
+      const void* kb[cpattn::kMaxBwdBlocks];
+      const void* vb[cpattn::kMaxBwdBlocks];
+      float* dkb[cpattn::kMaxBwdBlocks];
+      float* dvb[cpattn::kMaxBwdBlocks];
+      int len[cpattn::kMaxBwdBlocks];
+      int n = 0;
+      for (int i = 0; i < ring_degree; ++i) {
+        if (block_len[i] == 0) continue;
+        kb[n] = k_blocks[i];
+        vb[n] = v_blocks[i];
+        dkb[n] = dk_blocks[i];
+        dvb[n] = dv_blocks[i];
+        len[n] = block_len[i];
+        ++n;
+      }
+      cpattn::BwdArgs a;
+      a.q = q; a.k = nullptr; a.v = nullptr;
+      a.dout_b = w.dout_b; a.lse = lse; a.delta = w.delta;
+      a.dq = dq; a.dk = nullptr; a.dv = nullptr;
+      a.qs = qs; a.kvs = kvs; a.dqs = dqs; a.dkvs = dkvs;
+      a.B = B; a.H = H; a.D = D; a.Sq = Sq; a.Skv = 0;
+      a.scale = scale;
+      a.accumulate_dq = false;
+      a.dq_stream = side;
+      const cpattn::BwdBlocks bb{n, kb, vb, dkb, dvb, len};
+      st = hip_status(cpattn::launch_attn_bwd_ring_bf16(a, bb, s), "attn_bwd_bf16 (ring)");
+      have_dq = true;
+    }
+    for (int i = 0; i < ring_degree && st == CP_OK && !multi; ++i) {
       if (block_len[i] == 0) continue;
       st = run_block_bwd(q, qs, k_blocks[i], v_blocks[i], kvs, B, H, D, Sq, block_len[i], scale, have_dq, lse, w,
                          dq, dqs, dk_blocks[i], dv_blocks[i], dkvs, s, side);

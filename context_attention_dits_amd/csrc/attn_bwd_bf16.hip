@@ -147,6 +147,17 @@ struct BwdParams {
   int n_wg;
   float c;   // scale * log2(e)
   float scale;
+  // MULTI launches (all of a ring's non-empty blocks at once; the single-block
+  // fields k, v, dk, dv, Skv unused): block i's K, V, dK, dV at its first key
+  // (shared strides) and its length; dkv: wg0[i] = first workgroup of block i
+  // in the remapped order, wg0[n_blk] = n_wg.
+  int n_blk;
+  const uint16_t* kblk[kMaxBwdBlocks];
+  const uint16_t* vblk[kMaxBwdBlocks];
+  float* dkblk[kMaxBwdBlocks];
+  float* dvblk[kMaxBwdBlocks];
+  int lblk[kMaxBwdBlocks];
+  int wg0[kMaxBwdBlocks + 1];
 };
 
 // Global -> LDS loads of one 32-row tile starting at row r0 of a [rows, D]
@@ -198,7 +209,7 @@ __device__ __forceinline__ int range_bytes(int rows_left, int64_t row_bytes) {
 // dQ += K_t^T dS_t. Three LDS stages: in iteration t the waves read tile t+1's
 // fragments and tile t's row-major K, while tile t+2 is being loaded.
 
-template <int D, bool ACC>
+template <int D, bool ACC, bool MULTI = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
 attn_bwd_dq_kernel(BwdParams p) {
   using T = TileCfg<D>;
@@ -236,16 +247,31 @@ attn_bwd_dq_kernel(BwdParams p) {
   const float dlt = valid ? p.delta[stat] : 0.f;
 
   const int64_t row_bytes = p.kv_ss * 2;
-  const uint16_t* kbase = p.k + b * p.kv_sb + h * p.kv_sh;
-  const uint16_t* vbase = p.v + b * p.kv_sb + h * p.kv_sh;
   TileLoader<D> ld;
   ld.init(wave, lane, row_bytes);
   const int tr_lane = tr_lane_offset<D>(lane);
-  const int n_tiles = (p.Skv + TR - 1) / TR;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+  // MULTI: the blocks in turn, dQ accumulated in registers across them and
+  // written once; a workgroup barrier before each later block's first loads
+  // (the other waves may still read the previous block's last stages). The
+  // loop is a backward jump only that instantiation has.
+  int sblk = 0;
+dq_next_block:
+  if constexpr (MULTI) {
+    if (sblk > 0) __syncthreads();
+  }
+  const int skv = MULTI ? p.lblk[sblk] : p.Skv;
+  const uint16_t* kbase = (MULTI ? p.kblk[sblk] : p.k) + b * p.kv_sb + h * p.kv_sh;
+  const uint16_t* vbase = (MULTI ? p.vblk[sblk] : p.v) + b * p.kv_sb + h * p.kv_sh;
+  const int n_tiles = (skv + TR - 1) / TR;
 
   auto issue = [&](int t, char* kf, char* vf, char* kr) {
     const int64_t off = (int64_t)t * TR * p.kv_ss;
-    const int nb = range_bytes(p.Skv - t * TR, row_bytes);
+    const int nb = range_bytes(skv - t * TR, row_bytes);
     ld.frag(kbase + off, nb, kf);
     ld.frag(vbase + off, nb, vf);
     ld.rows(kbase + off, nb, kr);
@@ -254,10 +280,6 @@ attn_bwd_dq_kernel(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
   // S^T = K Q^T and dP^T = V dO^T of one tile (16 MFMAs), fragments from LDS.
   auto scores = [&](const char* kf, const char* vf, f32x16& s, f32x16& dpt) {
@@ -275,7 +297,7 @@ attn_bwd_dq_kernel(BwdParams p) {
   // 4*hi + r%4, and only the last tile can hold keys past Skv (P = 0 there).
   auto softmax = [&](auto last_tag, int t, const f32x16& s, const f32x16& dpt, bf16x8 (&dsb)[2]) {
     constexpr bool LAST = decltype(last_tag)::value;
-    const int lim = p.Skv - t * TR - 4 * hi;
+    const int lim = skv - t * TR - 4 * hi;
 #pragma unroll
     for (int kk2 = 0; kk2 < 2; ++kk2) {
 #pragma unroll
@@ -346,6 +368,9 @@ attn_bwd_dq_kernel(BwdParams p) {
   }
   if (t < n_tiles) iter(t, kr0, kf1, vf1, kr1, kf2, vf2, kr2);
   if (t + 1 < n_tiles) iter(t + 1, kr1, kf2, vf2, kr2, kf0, vf0, kr0);
+  if constexpr (MULTI) {
+    if (++sblk < p.n_blk) goto dq_next_block;
+  }
 
   if (valid) {
     float* out = p.dq + b * p.dq_sb + (int64_t)row * p.dq_ss + h * p.dq_sh;
@@ -367,7 +392,7 @@ attn_bwd_dq_kernel(BwdParams p) {
 
 // --------------------------------------------------------------- dKV kernel
 
-template <int D>
+template <int D, bool MULTI = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(CP_BWD_DKV_WPE)))
 attn_bwd_dkv_kernel(BwdParams p) {
   using T = TileCfg<D>;
@@ -385,17 +410,27 @@ attn_bwd_dkv_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  const int tile = xcd_remap(blockIdx.x, p.n_wg);
-  const int kt = tile % p.n_t, bh = tile / p.n_t;
+  // MULTI: one grid over every block's key tiles (block-major after the XCD
+  // remap, so a block's tiles of one head stay on one XCD); the workgroup's
+  // block is found in the wg0 table.
+  int tile = xcd_remap(blockIdx.x, p.n_wg);
+  int blk = 0;
+  if constexpr (MULTI) {
+    while (blk + 1 < p.n_blk && tile >= p.wg0[blk + 1]) ++blk;
+    tile -= p.wg0[blk];
+  }
+  const int skv = MULTI ? p.lblk[blk] : p.Skv;
+  const int n_t = MULTI ? (skv + NW * 32 - 1) / (NW * 32) : p.n_t;
+  const int kt = tile % n_t, bh = tile / n_t;
   const int h = bh % p.H, b = bh / p.H;
   const int key = kt * (NW * 32) + wave * 32 + l32;  // this lane's key
-  const bool valid = key < p.Skv;
+  const bool valid = key < skv;
 
   // K^T and V^T as B operands: lane holds key l32, dims 16kk + 8hi..+7
   bf16x8 kt_[T::KK], vt_[T::KK];
   {
-    const uint16_t* kp = p.k + b * p.kv_sb + (int64_t)key * p.kv_ss + h * p.kv_sh + hi * 8;
-    const uint16_t* vp = p.v + b * p.kv_sb + (int64_t)key * p.kv_ss + h * p.kv_sh + hi * 8;
+    const uint16_t* kp = (MULTI ? p.kblk[blk] : p.k) + b * p.kv_sb + (int64_t)key * p.kv_ss + h * p.kv_sh + hi * 8;
+    const uint16_t* vp = (MULTI ? p.vblk[blk] : p.v) + b * p.kv_sb + (int64_t)key * p.kv_ss + h * p.kv_sh + hi * 8;
 #pragma unroll
     for (int kk = 0; kk < T::KK; ++kk) {
       kt_[kk] = valid ? *reinterpret_cast<const bf16x8*>(kp + kk * 16) : bf16x8{};
@@ -487,8 +522,8 @@ attn_bwd_dkv_kernel(BwdParams p) {
   if (t < n_tiles) step(qf0, df0, qr0, dr0, st0);
 
   if (valid) {
-    float* kout = p.dk + b * p.dkv_sb + (int64_t)key * p.dkv_ss + h * p.dkv_sh;
-    float* vout = p.dv + b * p.dkv_sb + (int64_t)key * p.dkv_ss + h * p.dkv_sh;
+    float* kout = (MULTI ? p.dkblk[blk] : p.dk) + b * p.dkv_sb + (int64_t)key * p.dkv_ss + h * p.dkv_sh;
+    float* vout = (MULTI ? p.dvblk[blk] : p.dv) + b * p.dkv_sb + (int64_t)key * p.dkv_ss + h * p.dkv_sh;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -587,7 +622,67 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_bwd_ring_d(const BwdArgs& a, const BwdBlocks& bb, hipStream_t stream) {
+  if (bb.n < 1 || bb.n > kMaxBwdBlocks || a.accumulate_dq) return hipErrorInvalidValue;
+  BwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = nullptr;
+  p.v = nullptr;
+  p.dob = static_cast<const uint16_t*>(a.dout_b);
+  p.lse = a.lse;
+  p.delta = a.delta;
+  p.dq = a.dq;
+  p.dk = nullptr;
+  p.dv = nullptr;
+  p.q_sb = a.qs.b; p.q_ss = a.qs.s; p.q_sh = a.qs.h;
+  p.kv_sb = a.kvs.b; p.kv_ss = a.kvs.s; p.kv_sh = a.kvs.h;
+  p.dq_sb = a.dqs.b; p.dq_ss = a.dqs.s; p.dq_sh = a.dqs.h;
+  p.dkv_sb = a.dkvs.b; p.dkv_ss = a.dkvs.s; p.dkv_sh = a.dkvs.h;
+  p.B = a.B; p.H = a.H; p.Sq = a.Sq; p.Skv = 0;
+  p.c = a.scale * kLog2e;
+  p.scale = a.scale;
+  p.n_blk = bb.n;
+  int64_t tot = 0;
+  for (int i = 0; i < kMaxBwdBlocks; ++i) {
+    const bool in = i < bb.n;
+    if (in && bb.len[i] < 1) return hipErrorInvalidValue;
+    p.kblk[i] = in ? static_cast<const uint16_t*>(bb.k[i]) : nullptr;
+    p.vblk[i] = in ? static_cast<const uint16_t*>(bb.v[i]) : nullptr;
+    p.dkblk[i] = in ? bb.dk[i] : nullptr;
+    p.dvblk[i] = in ? bb.dv[i] : nullptr;
+    p.lblk[i] = in ? bb.len[i] : 0;
+    p.wg0[i] = (int)tot;
+    if (in) tot += (int64_t)((bb.len[i] + NW * 32 - 1) / (NW * 32)) * a.H * a.B;
+    if (tot > 0x7fffffff) return hipErrorInvalidConfiguration;
+  }
+  p.wg0[kMaxBwdBlocks] = (int)tot;
+  // dQ: one launch, the blocks in turn
+  p.n_t = (a.Sq + NW * 32 - 1) / (NW * 32);
+  const int64_t n = (int64_t)p.n_t * a.H * a.B;
+  if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
+  p.n_wg = (int)n;
+  if (p.n_wg > 0) {
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false, true>), dim3(p.n_wg), dim3(NW * 64), 0,
+                       a.dq_stream ? a.dq_stream : stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // dK, dV: one grid over every block's key tiles
+  p.n_t = 0;
+  p.n_wg = (int)tot;
+  if (p.n_wg == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, true>), dim3(p.n_wg), dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_attn_bwd_ring_bf16(const BwdArgs& a, const BwdBlocks& bb, hipStream_t stream) {
+  if (a.D == 128) return launch_bwd_ring_d<128>(a, bb, stream);
+  if (a.D == 64) return launch_bwd_ring_d<64>(a, bb, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_attn_bwd_prep(const float* out, Strides os, const float* dout, Strides ds, void* dout_b,
                                 float* delta, int B, int H, int Sq, int D, hipStream_t stream) {

@@ -81,6 +81,22 @@ struct BwdArgs {
   hipStream_t dq_stream;
 };
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+
+// The backward of 2..kMaxBwdBlocks non-empty blocks of a ring in two
+// launches: dQ with every workgroup taking its query tile through the blocks
+// in turn (accumulated in registers, written once: a.accumulate_dq must be
+// false), and dK, dV of every block in one grid. a.k, a.v, a.dk, a.dv and
+// a.Skv are not used; a.kvs / a.dkvs are the blocks' shared strides.
+constexpr int kMaxBwdBlocks = 16;
+struct BwdBlocks {
+  int n;
+  const void* const* k;
+  const void* const* v;
+  float* const* dk;
+  float* const* dv;
+  const int* len;  // each >= 1
+};
+hipError_t launch_attn_bwd_ring_bf16(const BwdArgs& a, const BwdBlocks& bb, hipStream_t stream);
 // delta = rowsum(dO * O) and dO rounded to bf16 (contiguous [B, Sq, H, D]).
 hipError_t launch_attn_bwd_prep(const float* out, Strides os, const float* dout, Strides ds, void* dout_b,
                                 float* delta, int B, int H, int Sq, int D, hipStream_t stream);

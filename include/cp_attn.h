@@ -396,6 +396,13 @@ cp_status_t cp_attn_block_bwd(const void* q, const int64_t* q_strides, const voi
  *              entries of empty blocks are not used
  *   workspace  cp_attn_bwd_workspace_size(B, H, Sq, D) bytes
  * If every block is empty, dq = 0.
+ * Launch plan: where neither kernel's grid would leave a quarter of its last
+ * round of workgroup slots idle (see "Streams" above), 2 to 16 non-empty
+ * blocks run as two launches: dQ with every workgroup taking its query tile
+ * through the blocks in turn (summed in registers, written once; equal to
+ * the per-block chain up to float32 rounding of the sum's order), and dK, dV
+ * of every block in one grid (the same bits as per block). Otherwise the
+ * blocks run one after the other, dQ added into in place.
  */
 cp_status_t cp_ring_attention_bwd(const void* q, const int64_t* q_strides, const void* const* k_blocks,
                                   const void* const* v_blocks, const int64_t* kv_strides, const int* block_len,
