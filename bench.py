@@ -451,7 +451,7 @@ def hbm_traffic(w: workloads.Workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py runs one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
     import torch

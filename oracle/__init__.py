@@ -20,7 +20,7 @@ Sources (diffusers v0.43.0 documentation pages):
   * "Inferencia distribuida" (distributed-inference guide, Spanish), sections
     "Ring Attention", "Ulysses Attention".
 
-Readings taken where the pages are silent (each is listed in the design doc too):
+Readings taken where the pages are silent:
   * the merge of per-block partials is the exact log-sum-exp recombination,
     the only merge under which a full ring equals full attention;
   * the softmax scale is 1/sqrt(D) and LSE is the natural log of
