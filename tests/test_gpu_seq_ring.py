@@ -9,8 +9,8 @@ oracle within the bf16 tolerances (out 1e-2, LSE 1e-3). Small shapes force the
 8-wave shape and pass no workspace (with a workspace and a forced 8-wave shape,
 the other one-launch form, partials in parallel, is taken); the FLUX ring-2
 share takes this path with the library's own shape choice. Cases: ragged query
-and key tails, one-key and empty blocks, 5 and 16 blocks, and 17 blocks, which
-run one launch per block.
+and key tails, one-key and empty blocks, 5 and 16 blocks, 17 blocks (which run
+one launch per block), and strided views of Q, K and the output.
 """
 import numpy as np
 import pytest
@@ -105,3 +105,37 @@ def test_seq_ring_flux_ring2_share(cp):
     o_ref, l_ref = oracle.attention(inp.q[:, rows], inp.k, inp.v, w.scale)
     assert_close("out rows", out.cpu().numpy()[:, rows], o_ref, TOL["bf16"]["o"])
     assert_close("lse rows", lse.cpu().numpy()[:, :, rows], l_ref, TOL["bf16"]["lse"])
+
+
+def test_seq_ring_strided_views(cp):
+    """Blocks in turn with a strided Q view, K blocks sliced from a NaN-padded all-gather
+    buffer [P, B, Lmax, H, D] and an output view inside a larger NaN-filled buffer: the same
+    bits as contiguous tensors, nothing written outside the output view, no NaN read."""
+    B, H, D, Sq, lens = 2, 3, 128, 300, (256, 130, 64)
+    say("seq ring strided views", lens)
+    inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=77)
+    scale = inp.workload.scale
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    offs = workloads.block_offsets(lens)
+    vp = [cp.pack_v(v[:, o:o + L].contiguous()) for o, L in zip(offs, lens)]
+    kb = [k[:, o:o + L] for o, L in zip(offs, lens)]
+    Lmax = max(lens)
+    kpad = torch.full((len(lens), B, Lmax, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for i, (o, L) in enumerate(zip(offs, lens)):
+        kpad[i, :, :L] = k[:, o:o + L]
+    kb_pad = [kpad[i, :, :L] for i, L in enumerate(lens)]
+    qbig = torch.zeros((B, Sq, H + 2, D), dtype=torch.bfloat16, device="cuda")
+    qbig[:, :, 1:H + 1] = q
+    q_view = qbig[:, :, 1:H + 1]
+    obig = torch.full((B, Sq, H + 1, D), float("nan"), dtype=torch.float32, device="cuda")
+    out_view = obig[:, :, :H]
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
+    with fwd_waves(cp, 8):
+        cp.cp_ring_attention(q_view, kb_pad, vp, out_view, lse, scale=scale, flags=cp.CP_RING_ANYTHING)
+        out_c = torch.empty((B, Sq, H, D), dtype=torch.float32, device="cuda")
+        lse_c = torch.empty_like(lse)
+        cp.cp_ring_attention(q, kb, vp, out_c, lse_c, scale=scale, flags=cp.CP_RING_ANYTHING)
+    torch.cuda.synchronize()
+    assert torch.isnan(obig[:, :, H]).all().item(), "wrote outside the output view"
+    assert torch.equal(out_view, out_c) and torch.equal(lse, lse_c)
+    assert not torch.isnan(out_c).any().item()
