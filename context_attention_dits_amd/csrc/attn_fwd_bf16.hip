@@ -265,9 +265,9 @@ attn_fwd_bf16_kernel(Params p) {
   const int qrow0 = qt * C::BM + wave * (QB * 32);
 
   // SEQ: the workgroup takes its query tile through every block in turn
-  // (block 0 written, later blocks merged by the epilogue); between blocks a
-  // workgroup barrier keeps the next block's first loads out of LDS stages the
-  // other wave group may still be reading. Each lane keeps its row's LSE (as
+  // (block 0 written, later blocks merged by the epilogue); the next block's
+  // first loads wait for the other wave group only where they would land in
+  // an LDS stage it may still be reading (see the prologue). Each lane keeps its row's LSE (as
   // stored) in a register; the output it merges is what the same lane wrote.
   // Q is loaded again for every block, as by one launch per block.
   float lse_keep[QB];
@@ -276,11 +276,9 @@ attn_fwd_bf16_kernel(Params p) {
   // (The block loop is a backward jump that only the SEQ instantiation has,
   // so the other shapes compile exactly as without it.)
   int sblk = 0;
+  int seq_prev_stage = -1;  // SEQ: LDS stage of the previous block's last tile
 seq_next_block:
-  if constexpr (SEQ) {
-    blk = sblk;
-    if (sblk > 0) __syncthreads();
-  }
+  if constexpr (SEQ) blk = sblk;
 
   // Kernel arguments used inside the tile loop, pinned in SGPRs: reloading
   // them from the argument segment there would make the next LDS wait also
@@ -727,9 +725,16 @@ seq_next_block:
     char* const vt3[3] = {vtb0, vtb1, vtb2};
     // prologue: K_0, K_1 and raw V_0..V_2 loaded, V_0^T built (packed: K_0,
     // K_1 and V_0^T loaded), scores of tile 0
+    // SEQ, later blocks: the other wave group may still be in the previous
+    // block's last MFMA half, which reads only that block's last V^T stage
+    // (no scores, so no K stage): the K loads go at once, V_0's only after a
+    // workgroup barrier when it lands in that stage.
     issue_k(0, kbuf0);
     issue_k(1, kbuf1);
     if constexpr (PACKED) {
+      if constexpr (SEQ) {
+        if (seq_prev_stage == 0) __syncthreads();
+      }
       issue_v(0, vtb0);
       sync(Pend0{});
       scores(kbuf0, sa);
@@ -912,6 +917,7 @@ seq_next_block:
     if (threadIdx.x == 0) __hip_atomic_store(p.flags + tile, blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if constexpr (SEQ) {
+    seq_prev_stage = (n_tiles - 1) % 3;
     if (++sblk < p.n_blk) goto seq_next_block;
   }
 }
