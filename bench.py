@@ -507,7 +507,7 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us/step)")
     tflops = w.flops / (ms_step * 1e-3) / 1e12
 
-    k_ms, k_flops = prob.time_block_kernels(max(5, min(args.steps, 50)), graph=args.graph)
+    k_ms, k_flops = prob.time_block_kernels(max(5, min(args.steps, 200)), graph=args.graph)
     achieved = k_flops / (k_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     log(f"[bench] block kernel: {k_ms * 1e3:.1f} us/launch, {achieved:.1f} TFLOP/s ({achieved / peak:.1%} of {peak})")
