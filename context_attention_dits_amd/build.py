@@ -4,7 +4,8 @@ Usage: ``python -m context_attention_dits_amd.build [--out PATH] [-DNAME=VALUE .
 Every call compiles from source (no up-to-date check). Objects go to
 ``context_attention_dits_amd/_build/``; the shared library lands next to this
 file unless ``--out`` says otherwise. ``-D`` definitions select kernel tile
-variants (e.g. ``-DCP_FWD_QB=2``) for a library built at another path.
+variants (e.g. ``-DCP_FWD_QB=2``: two 32-query blocks per wave, 4-wave shape only) for a
+library built at another path.
 """
 from __future__ import annotations
 

@@ -140,6 +140,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // offsets; checked by the caller through o_end.)
 bool one_launch_ring(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree) {
   if (dtype != CP_BF16 || D != 128 || B <= 0 || H <= 0 || Sq <= 0) return false;
+  if (cpattn::ring_max_blocks() < 2) return false;  // library built without the 8-wave shape
   const int waves = g_fwd_waves.load(std::memory_order_relaxed);
   if (waves == 4) return false;
   cpattn::FwdArgs a{};

@@ -75,7 +75,7 @@
 #include "kernels.h"
 
 #ifndef CP_FWD_QB
-#define CP_FWD_QB 1  // 32-query blocks per wave
+#define CP_FWD_QB 1  // 32-query blocks per wave (the 8-wave shape needs 1: other values run 4 waves only)
 #endif
 #ifndef CP_FWD_NW
 #define CP_FWD_NW 0  // default workgroup shape for D = 128: 4, 8 (ping-pong), or 0 to choose per launch
@@ -1143,7 +1143,7 @@ hipError_t launch_pack_v(const void* v, Strides vs, void* packed, int B, int H, 
 // four rounds of 256 workgroups and its last (or only) round is less than
 // half full.
 int pick_waves(const FwdArgs& a) {
-  if (a.D != 128) return 4;
+  if (a.D != 128 || CP_FWD_QB != 1) return 4;
   if (a.waves != 0) return a.waves;
   if (CP_FWD_NW != 0) return CP_FWD_NW;
   const int64_t n_wg8 = (int64_t)((a.Sq + 255) / 256) * a.H * a.B;
@@ -1153,7 +1153,7 @@ int pick_waves(const FwdArgs& a) {
 
 template <int D>
 hipError_t launch_dn(const FwdArgs& a, hipStream_t stream) {
-  if constexpr (D == 128) {
+  if constexpr (D == 128 && CP_FWD_QB == 1) {
     if (pick_waves(a) == 8) return launch_dw<D, 8>(a, stream);
   }
   return launch_dw<D, 4>(a, stream);
@@ -1164,21 +1164,27 @@ hipError_t launch_dn(const FwdArgs& a, hipStream_t stream) {
 // CU has read, and with at most 3 blocks a tile is merged at most twice, the
 // second time by a CU that has either not read the tile before or written it
 // itself since. More blocks run as one launch per block.
-int ring_max_blocks() { return CP_RING_SC1 ? kMaxRingBlocks : 3; }
+int ring_max_blocks() { return CP_FWD_QB != 1 ? 0 : CP_RING_SC1 ? kMaxRingBlocks : 3; }
 
-int seq_max_blocks() { return CP_FWD_SEQ ? kMaxRingBlocks : 0; }
+int seq_max_blocks() { return (CP_FWD_SEQ && CP_FWD_QB == 1) ? kMaxRingBlocks : 0; }
 
 hipError_t launch_ring_seq_bf16(const FwdArgs& a, const RingBlocks& rb, hipStream_t stream) {
-  if (a.D != 128 || !a.v_packed || !CP_FWD_SEQ) return hipErrorInvalidValue;
-  return launch_seq_128(a, rb, stream);
+  if constexpr (CP_FWD_SEQ && CP_FWD_QB == 1) {
+    if (a.D != 128 || !a.v_packed) return hipErrorInvalidValue;
+    return launch_seq_128(a, rb, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 int64_t ring_flag_count(int B, int H, int Sq) { return (int64_t)((Sq + 255) / 256) * H * B; }
 
 hipError_t launch_ring_bf16(const FwdArgs& a, const RingBlocks& rb, int* flags, hipStream_t stream) {
-  // packed V only: with V transposed in the kernel the ring variant spills heavily
-  if (a.D != 128 || !a.v_packed) return hipErrorInvalidValue;
-  return launch_ring_128<true>(a, rb, flags, stream);
+  if constexpr (CP_FWD_QB == 1) {
+    // packed V only: with V transposed in the kernel the ring variant spills heavily
+    if (a.D != 128 || !a.v_packed) return hipErrorInvalidValue;
+    return launch_ring_128<true>(a, rb, flags, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
