@@ -54,7 +54,10 @@ import workloads  # noqa: E402
 METRIC = "ring-block attention TFLOP/s (fwd+LSE merge) and % of MI355X bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA bf16; fp32 vector ALU
 PEAK_HBM_GBS = 8000.0
-DEFAULT_WORKLOAD = "flux1024_ring2_bf16"
+DEFAULT_WORKLOAD = "flux1024_ulysses2_bf16"
+# Block kernels timed in the same run besides the step's own workload (roofline only).
+EXTRA_ROOFLINES = ("video32k_ring4_bf16",)
+NOMINAL_CLOCK_MHZ = 2400.0  # the clock the dense peaks are quoted at
 
 
 def log(*a):
@@ -79,7 +82,47 @@ def parse():
                     help="pass V as [B, S, H, D] instead of packed (bf16 workloads)")
     ap.add_argument("--separate-merge", action="store_true",
                     help="merge partials with the standalone merge kernel instead of the fused epilogue")
+    ap.add_argument("--extra", default=",".join(EXTRA_ROOFLINES),
+                    help="comma-separated workloads whose block kernel is also timed (roofline_extra); '' for none")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward")
+    ap.add_argument("--no-hbm", action="store_true", help="skip the cold-cache HBM kernels")
     return ap.parse_args()
+
+
+def clock_beside(run_once, cycles: int = 40_000_000):
+    """Shader clock (MHz) while `run_once` keeps the GPU busy: a one-thread kernel that spins for
+    `cycles` of the shader clock (torch.cuda._sleep counts s_memtime, the shader-clock counter)
+    runs on a second stream (default priority) while the launches repeat on the current one; its
+    duration between two HIP events gives the clock. It needs a free compute unit to start on:
+    where every unit is busy it starts when one frees, which the long spin makes a few percent
+    at most. None if torch lacks the spin kernel."""
+    import torch
+    if not hasattr(torch.cuda, "_sleep"):
+        return None
+    side = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    run_once()
+    with torch.cuda.stream(side):
+        e0.record(side)
+        torch.cuda._sleep(cycles)
+        e1.record(side)
+    t0 = time.perf_counter()
+    while not e1.query() and time.perf_counter() - t0 < 10.0:
+        for _ in range(4):
+            run_once()
+    torch.cuda.synchronize()
+    return cycles / (e0.elapsed_time(e1) * 1e3)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 class Problem:
@@ -131,9 +174,9 @@ class Problem:
         # (where the block kernel runs its 8-wave shape, or the packed ring runs as one launch;
         # the 4-wave kernel on its own gains nothing from it)
         lens = [kb.shape[1] for kb in self.kb]
-        self.packed = packed_v and w.dtype == "bf16" and (
+        self.packed = bool(packed_v and w.dtype == "bf16" and (
             cp.cp_attn_fwd_waves(B, H, D, w.Sq) == 8
-            or cp.cp_ring_attention_one_launch(cp.CP_BF16, B, H, D, w.Sq, lens))
+            or cp.cp_ring_attention_one_launch(cp.CP_BF16, B, H, D, w.Sq, lens)))
         self.vb_att = list(self.vb)
         if self.packed:
             self.vb_att = [cp.pack_v(x) for x in self.vb]
@@ -197,10 +240,9 @@ class Problem:
             cp.cp_ulysses_pack_heads(self.recv2, self.back, self.heads, cp.CP_REGROUP_HEAD_TO_SEQ)
             return
         if w.ulysses_degree > 1:
-            P = w.ulysses_degree
-            cp.cp_ulysses_regroup(self.q, self.qr, P, cp.CP_REGROUP_SEQ_TO_HEAD)
-            cp.cp_ulysses_regroup(self.k_own, self.kb[0], P, cp.CP_REGROUP_SEQ_TO_HEAD)
-            cp.cp_ulysses_regroup(self.v_own, self.vb[0], P, cp.CP_REGROUP_SEQ_TO_HEAD)
+            # this rank's Q, K and V shards, regrouped by one launch
+            cp.cp_ulysses_regroup_multi([self.q, self.k_own, self.v_own], [self.qr, self.kb[0], self.vb[0]],
+                                        w.ulysses_degree, cp.CP_REGROUP_SEQ_TO_HEAD)
         if self.packed:
             cp.cp_attn_pack_v(self.vb[0], self.vb_att[0].data)
         cp.cp_ring_attention(self.q_att, self.kb, self.vb_att, self.out, self.lse, scale=w.scale,
@@ -266,6 +308,7 @@ class Problem:
 
             ms = self._timed_passes(one_pass, reps, graph)
             self.block_launch = "one launch for all blocks"
+            self.block_pass = one_pass
             return ms / reps, w.flops
         self.block_launch = "one launch per block"
 
@@ -275,6 +318,7 @@ class Problem:
                                      flags=cp.CP_BLOCK_ACCUMULATE if i > 0 else 0)
 
         ms = self._timed_passes(one_pass, reps, graph)
+        self.block_pass = one_pass
         flops = sum(4 * w.B * w.attn_H * w.Sq * kb.shape[1] * w.D for _, kb, _ in blocks) / len(blocks)
         return ms / (reps * len(blocks)), flops
 
@@ -315,15 +359,18 @@ class Problem:
 
 
 def time_hbm_kernels(reps: int = 5):
-    """HBM rate of the two bandwidth-bound kernels, cold caches.
+    """HBM rate of the bandwidth-bound kernels, cold caches.
 
     cp_lse_merge on the 32k-token ring-4 share (out [1, 8192, 24, 128] float32,
-    in place), cp_ulysses_regroup SEQ_TO_HEAD of a [1, 16384, 24, 128] bf16
-    tensor at degree 2, cp_ulysses_pack_heads of the same tensor into
-    uneven head groups (7, 6, 6, 5) and cp_attn_pack_v of it (as one V block
-    of 16384 keys). Before each timed launch a 512 MiB buffer is read so
-    that neither L2 nor the 256 MB Infinity Cache holds the operands; bytes are
-    the algorithmic ones (every element read once, written once).
+    in place); the Ulysses-2 share's regroup of its Q, K and V shards
+    ([1, 2304, 24, 128] bf16 each -> [1, 4608, 12, 128]) as the step runs it
+    (one cp_ulysses_regroup_multi launch) and as three cp_ulysses_regroup
+    launches; cp_ulysses_regroup SEQ_TO_HEAD of a [1, 16384, 24, 128] bf16
+    tensor at degree 2, cp_ulysses_pack_heads of the same tensor into uneven
+    head groups (7, 6, 6, 5) and cp_attn_pack_v of it (as one V block of 16384
+    keys). Before each timed launch a 512 MiB buffer is read so that neither L2
+    nor the 256 MB Infinity Cache holds the operands; bytes are the algorithmic
+    ones (every element read once, written once).
     """
     import torch
     import context_attention_dits_amd as cp
@@ -344,34 +391,49 @@ def time_hbm_kernels(reps: int = 5):
             ms.append(e0.elapsed_time(e1))
         return sum(ms[1:]) / reps
 
+    out = {}
+
+    def record(name, ms, nb, shape):
+        gbs = nb / (ms * 1e-3) / 1e9
+        out[name] = {"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "us": round(ms * 1e3, 2),
+                     "bytes": nb, "shape": shape}
+
     B, Sq, H, D = 1, 8192, 24, 128
     g = torch.Generator(device="cuda").manual_seed(5)
     oa = torch.randn(B, Sq, H, D, device="cuda", generator=g)
     ob = torch.randn(B, Sq, H, D, device="cuda", generator=g)
     la = torch.randn(B, H, Sq, device="cuda", generator=g)
     lb = torch.randn(B, H, Sq, device="cuda", generator=g)
-    merge_ms = timed(lambda: cp.cp_lse_merge(oa, la, ob, lb))
-    merge_bytes = 3 * 4 * B * Sq * H * D + 3 * 4 * B * H * Sq
-    S_l, P = 16384, 2
+    record("lse_merge", timed(lambda: cp.cp_lse_merge(oa, la, ob, lb)),
+           3 * 4 * B * Sq * H * D + 3 * 4 * B * H * Sq, "out [1,8192,24,128] f32 + lse, in place (32k ring-4 share)")
+    del oa, ob, la, lb
+    # the Ulysses-2 share's own regroup: Q, K, V shards [1, 2304, 24, 128] bf16
+    S3, P = 2304, 2
+    xs = [torch.randn(1, S3, H, D, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3)]
+    ys = [torch.empty(1, P * S3, H // P, D, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    qkv_bytes = 3 * 2 * 2 * S3 * H * D
+    record("ulysses_regroup_qkv", timed(lambda: cp.cp_ulysses_regroup_multi(xs, ys, P, cp.CP_REGROUP_SEQ_TO_HEAD)),
+           qkv_bytes, "Q, K, V [1,2304,24,128] bf16 -> [1,4608,12,128], one launch (Ulysses-2 share)")
+
+    def three():
+        for x, y in zip(xs, ys):
+            cp.cp_ulysses_regroup(x, y, P, cp.CP_REGROUP_SEQ_TO_HEAD)
+
+    record("ulysses_regroup_qkv_3launch", timed(three), qkv_bytes,
+           "Q, K, V [1,2304,24,128] bf16 -> [1,4608,12,128], one launch per tensor (Ulysses-2 share)")
+    del xs, ys
+    S_l = 16384
     x = torch.randn(B, S_l, H, D, device="cuda", generator=g).to(torch.bfloat16)
     y = torch.empty(B, P * S_l, H // P, D, dtype=torch.bfloat16, device="cuda")
-    regroup_ms = timed(lambda: cp.cp_ulysses_regroup(x, y, P, cp.CP_REGROUP_SEQ_TO_HEAD))
-    regroup_bytes = 2 * 2 * B * S_l * H * D
+    big = 2 * 2 * B * S_l * H * D
+    record("ulysses_regroup", timed(lambda: cp.cp_ulysses_regroup(x, y, P, cp.CP_REGROUP_SEQ_TO_HEAD)), big,
+           "[1,16384,24,128] bf16 -> [1,32768,12,128], degree 2")
     pieces = torch.empty(x.numel(), dtype=torch.bfloat16, device="cuda")
-    pack_ms = timed(lambda: cp.cp_ulysses_pack_heads(x, pieces, [7, 6, 6, 5], cp.CP_REGROUP_SEQ_TO_HEAD))
+    record("ulysses_pack_heads",
+           timed(lambda: cp.cp_ulysses_pack_heads(x, pieces, [7, 6, 6, 5], cp.CP_REGROUP_SEQ_TO_HEAD)), big,
+           "[1,16384,24,128] bf16 -> pieces of 7, 6, 6, 5 heads")
     pv = torch.empty(cp.cp_attn_packed_v_bytes(B, H, D, S_l), dtype=torch.uint8, device="cuda")
-    packv_ms = timed(lambda: cp.cp_attn_pack_v(x, pv))
-    out = {}
-    for name, ms, nb, shape in (("lse_merge", merge_ms, merge_bytes, "out [1,8192,24,128] f32 + lse, in place"),
-                                ("ulysses_regroup", regroup_ms, regroup_bytes,
-                                 "[1,16384,24,128] bf16 -> [1,32768,12,128], degree 2"),
-                                ("ulysses_pack_heads", pack_ms, regroup_bytes,
-                                 "[1,16384,24,128] bf16 -> pieces of 7, 6, 6, 5 heads"),
-                                ("pack_v", packv_ms, regroup_bytes,
-                                 "V [1,16384,24,128] bf16 -> packed tiles")):
-        gbs = nb / (ms * 1e-3) / 1e9
-        out[name] = {"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "us": round(ms * 1e3, 2),
-                     "bytes": nb, "shape": shape}
+    record("pack_v", timed(lambda: cp.cp_attn_pack_v(x, pv)), big, "V [1,16384,24,128] bf16 -> packed tiles")
     return out
 
 
@@ -422,6 +484,7 @@ def cpu_baseline(w: workloads.Workload, inp, target_s: float):
     flops = 4 * w.B * n_heads * w.Sq * w.Skv * w.D * passes
     what = f"{n_heads} of {H} heads" if n_heads < H else f"all {H} heads x {passes} passes"
     return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{what}, B={w.B} Sq={w.Sq} Skv={w.Skv} (every block, merged), numpy float64, "
                       f"{total:.1f} s"}
 
@@ -446,6 +509,25 @@ def hbm_traffic(w: workloads.Workload):
     if rec.get("kernel_source_sha256") != sha or not entry:
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+def block_roofline(prob, reps: int, graph: bool):
+    """The roofline entry of one workload's block kernel: HIP-event time per launch as the step
+    launches it, TFLOP/s against the dense peak at the nominal clock, and the shader clock
+    measured beside the same launches (clock_beside, a pass of its own after the timed one) with
+    the fraction of the peak at that clock."""
+    w = prob.w
+    k_ms, k_flops = prob.time_block_kernels(reps, graph=graph)
+    achieved = k_flops / (k_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    mhz = clock_beside(prob.block_pass)
+    return {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
+            "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": hbm_traffic(w),
+            "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel",
+            "us_per_launch": round(k_ms * 1e3, 2), "flops_per_launch": k_flops, "launches": prob.block_launch,
+            "clock_mhz": None if mhz is None else round(mhz, 1),
+            "clock_method": "one-thread s_memtime spin on a second stream beside the same launches",
+            "frac_at_clock": None if mhz is None else round(achieved / (peak * mhz / NOMINAL_CLOCK_MHZ), 4)}
 
 
 def main():
@@ -507,13 +589,28 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us/step)")
     tflops = w.flops / (ms_step * 1e-3) / 1e12
 
-    k_ms, k_flops = prob.time_block_kernels(max(5, min(args.steps, 200)), graph=args.graph)
-    achieved = k_flops / (k_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    log(f"[bench] block kernel: {k_ms * 1e3:.1f} us/launch, {achieved:.1f} TFLOP/s ({achieved / peak:.1%} of {peak})")
+    roofline = block_roofline(prob, max(5, min(args.steps, 200)), args.graph)
+    log(f"[bench] block kernel: {roofline['us_per_launch']:.1f} us/launch, {roofline['achieved']:.1f} TFLOP/s "
+        f"({roofline['frac']:.1%} of {peak}; clock {roofline['clock_mhz']} MHz, "
+        f"{roofline['frac_at_clock']} of the peak at that clock)")
+    extra = {}
+    for name in [x for x in args.extra.split(",") if x and x != w.name]:
+        wx = workloads.by_name(name)
+        px = Problem(wx, args.separate_merge, packed_v=not args.unpacked_v)
+        for _ in range(10):
+            px.step()
+        torch.cuda.synchronize()
+        rx = block_roofline(px, 30, args.graph)
+        rx["workload"] = name
+        extra[name] = rx
+        log(f"[bench] {name} block kernel: {rx['us_per_launch']:.1f} us/launch, {rx['achieved']:.1f} TFLOP/s "
+            f"({rx['frac']:.1%} of {PEAK_TFLOPS[wx.dtype]}; clock {rx['clock_mhz']} MHz)")
+        del px
+        torch.cuda.empty_cache()
 
     bwd = None
-    if w.dtype == "bf16":
+    if w.dtype == "bf16" and not args.no_backward:
         b_ms, b_flops = prob.time_backward(max(5, min(args.steps, 20)))
         b_tf = b_flops / (b_ms * 1e-3) / 1e12
         bwd = {"TFLOP/s": round(b_tf, 2), "frac": round(b_tf / PEAK_TFLOPS["bf16"], 4),
@@ -522,7 +619,7 @@ def main():
                "kernels": "attn_bwd_prep_kernel, attn_bwd_dq_kernel, attn_bwd_dkv_kernel"}
         log(f"[bench] backward: {b_ms * 1e3:.1f} us/pass, {b_tf:.1f} TFLOP/s ({b_tf / PEAK_TFLOPS['bf16']:.1%} of bf16 peak)")
 
-    hbm = time_hbm_kernels()
+    hbm = {} if args.no_hbm else time_hbm_kernels()
     for name, r in hbm.items():
         log(f"[bench] {name}: {r['us']:.1f} us, {r['GB/s']:.0f} GB/s ({r['frac']:.1%} of {PEAK_HBM_GBS:.0f}), {r['shape']}")
 
@@ -554,10 +651,8 @@ def main():
                    "merge": "separate" if args.separate_merge else "fused",
                    "v_layout": "packed" if prob.packed else "bshd",
                    "pct_of_bf16_peak": round(100 * tflops / PEAK_TFLOPS["bf16"], 2)},
-        "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": hbm_traffic(w),
-                     "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel",
-                     "us_per_launch": round(k_ms * 1e3, 2), "launches": prob.block_launch},
+        "roofline": roofline,
+        "roofline_extra": extra,
         "cpu_baseline": cpu,
         "hbm_kernels": hbm,
         "backward": bwd,

@@ -18,15 +18,16 @@ from typing import Optional, Sequence, Tuple
 
 from . import _lib
 from ._lib import (CP_BF16, CP_BLOCK_ACCUMULATE, CP_BLOCK_PACKED_V, CP_BWD_ACCUMULATE_DQ,  # noqa: F401
-                   CP_ERR_HIP, CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_F32, CP_OK,
+                   CP_ERR_HIP, CP_ERR_INVALID_ARG, CP_ERR_ORDER, CP_ERR_UNSUPPORTED, CP_ERR_WORKSPACE, CP_F32,
+                   CP_FWD_EIGHT_WAVES, CP_FWD_FOUR_WAVES, CP_OK, CP_ONE_LAUNCH_IN_TURN, CP_ONE_LAUNCH_PARALLEL,
                    CP_REGROUP_HEAD_TO_SEQ, CP_REGROUP_SEQ_TO_HEAD, CP_RING_ANYTHING, CP_RING_PACKED_V,
                    CP_RING_SEPARATE_MERGE, STATUS_NAMES)
 
 __all__ = [
-    "CpAttnError", "load", "cp_abi_version", "cp_last_error", "cp_attn_set_fwd_waves", "cp_attn_fwd_waves",
-    "cp_ring_attention_one_launch", "cp_attn_block_fwd",
+    "CpAttnError", "load", "cp_abi_version", "cp_last_error", "wave_flags", "cp_attn_fwd_waves",
+    "cp_ring_attention_one_launch", "cp_ring_attention_check", "cp_attn_block_fwd",
     "cp_lse_merge", "PackedV", "cp_attn_packed_v_bytes", "cp_attn_pack_v", "pack_v", "cp_ulysses_regroup_pack_v",
-    "cp_ring_attention", "cp_ring_attention_workspace_size", "cp_ulysses_regroup",
+    "cp_ring_attention", "cp_ring_attention_workspace_size", "cp_ulysses_regroup", "cp_ulysses_regroup_multi",
     "cp_ulysses_pack_heads", "cp_ulysses_concat_seq", "split_counts",
     "cp_attn_bwd_workspace_size", "cp_attn_bwd_prep", "cp_attn_block_bwd", "cp_ring_attention_bwd",
     "ring_attention", "ring_attention_bwd",
@@ -109,12 +110,11 @@ def cp_last_error() -> str:
     return _lib.load().cp_last_error().decode()
 
 
-def cp_attn_set_fwd_waves(waves: int) -> int:
-    """Workgroup shape of the bfloat16 block kernel (0 auto, 4 or 8); returns the previous one."""
-    prev = _lib.load().cp_attn_set_fwd_waves(int(waves))
-    if prev < 0:
-        raise ValueError(f"cp_attn_set_fwd_waves: waves must be 0, 4 or 8, got {waves}")
-    return prev
+def wave_flags(waves: int) -> int:
+    """CP_FWD_FOUR_WAVES / CP_FWD_EIGHT_WAVES for a forced workgroup shape (4 or 8); 0 chooses per launch."""
+    if waves not in (0, 4, 8):
+        raise ValueError(f"waves must be 0, 4 or 8, got {waves}")
+    return {0: 0, 4: CP_FWD_FOUR_WAVES, 8: CP_FWD_EIGHT_WAVES}[waves]
 
 
 class PackedV:
@@ -186,22 +186,38 @@ def _v_operand(name, v, dev):
     return False, _gpu(name, _bshd(name, v), dev)
 
 
-def cp_attn_fwd_waves(B: int, H: int, D: int, Sq: int) -> int:
-    """Workgroup shape (4, or 8 for the ping-pong kernel) of the bfloat16 block kernel at these sizes;
-    0 for sizes it does not run. Packed V (cp_attn_pack_v) pays off in the 8-wave shape."""
-    return int(_lib.load().cp_attn_fwd_waves(B, H, D, Sq))
+def cp_attn_fwd_waves(B: int, H: int, D: int, Sq: int, waves: int = 0) -> int:
+    """Workgroup shape (4, or 8 for the ping-pong kernel) of the bfloat16 block kernel at these sizes
+    (``waves`` forces one, as the call's flags would); 0 for sizes it does not run. Packed V
+    (cp_attn_pack_v) pays off in the 8-wave shape."""
+    return int(_lib.load().cp_attn_fwd_waves(B, H, D, Sq, wave_flags(waves)))
 
 
-def cp_ring_attention_one_launch(dtype: int, B: int, H: int, D: int, Sq: int, block_lens) -> bool:
-    """Whether cp_ring_attention with packed V and a workspace runs these blocks as one launch."""
+def cp_ring_attention_one_launch(dtype: int, B: int, H: int, D: int, Sq: int, block_lens, waves: int = 0) -> int:
+    """How cp_ring_attention with packed V and a workspace runs these blocks: 0 one launch per block,
+    or one launch: CP_ONE_LAUNCH_IN_TURN or CP_ONE_LAUNCH_PARALLEL."""
     lens = (ctypes.c_int * len(block_lens))(*[int(x) for x in block_lens])
-    return bool(_lib.load().cp_ring_attention_one_launch(dtype, B, H, D, Sq, lens, len(block_lens)))
+    return int(_lib.load().cp_ring_attention_one_launch(dtype, B, H, D, Sq, lens, len(block_lens),
+                                                        wave_flags(waves)))
 
 
-def cp_attn_block_fwd(q, k, v, out, lse, scale: Optional[float] = None, flags: int = 0, stream=None):
-    """Partial attention of q against one K/V block into (out, lse); see cp_attn_block_fwd in the header.
-    ``v`` may be a PackedV (from cp_attn_pack_v), which sets CP_BLOCK_PACKED_V."""
+def cp_ring_attention_check(workspace, stream=None):
+    """Raise CpAttnError (CP_ERR_ORDER) if a merge wait of the last parallel-partials ring launch on
+    this workspace gave up; waits for the stream."""
     lib = _lib.load()
+    _gpu("workspace", workspace)
+    st = lib.cp_ring_attention_check(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                     _stream(stream))
+    _check(st, "cp_ring_attention_check")
+
+
+def cp_attn_block_fwd(q, k, v, out, lse, scale: Optional[float] = None, flags: int = 0, stream=None,
+                      waves: int = 0):
+    """Partial attention of q against one K/V block into (out, lse); see cp_attn_block_fwd in the header.
+    ``v`` may be a PackedV (from cp_attn_pack_v), which sets CP_BLOCK_PACKED_V; ``waves`` (4 or 8)
+    forces the workgroup shape (CP_FWD_FOUR_WAVES / CP_FWD_EIGHT_WAVES)."""
+    lib = _lib.load()
+    flags |= wave_flags(waves)
     dev = _gpu("q", _bshd("q", q)).device
     _gpu("k", _bshd("k", k), dev)
     packed, v = _v_operand("v", v, dev)
@@ -286,14 +302,16 @@ def cp_ring_attention_workspace_size(B: int, H: int, Sq: int, D: int, flags: int
 
 
 def cp_ring_attention(q, k_blocks: Sequence, v_blocks: Sequence, out, lse, scale: Optional[float] = None,
-                      flags: int = 0, workspace=None, stream=None):
+                      flags: int = 0, workspace=None, stream=None, waves: int = 0):
     """One rank's ring share over resident K/V blocks into (out, lse); see cp_ring_attention.
 
     ``k_blocks[i]``/``v_blocks[i]`` are ``[B, L_i, H, D]`` views sharing one stride triple
     (e.g. slices of one buffer, or of a padded ``[P, B, Lmax, H, D]`` gather). The V blocks may
-    instead all be PackedV (cp_attn_pack_v), which sets CP_RING_PACKED_V.
+    instead all be PackedV (cp_attn_pack_v), which sets CP_RING_PACKED_V. ``waves`` (4 or 8)
+    forces the workgroup shape.
     """
     lib = _lib.load()
+    flags |= wave_flags(waves)
     dev = _gpu("q", _bshd("q", q)).device
     _gpu("out", _bshd("out", out), dev); _gpu("lse", lse, dev)
     B, Sq, H, D = q.shape
@@ -317,14 +335,8 @@ def cp_ring_attention(q, k_blocks: Sequence, v_blocks: Sequence, out, lse, scale
     _check(st, "cp_ring_attention")
 
 
-def cp_ulysses_regroup(inp, out, degree: int, direction: int = CP_REGROUP_SEQ_TO_HEAD, stream=None):
-    """Ulysses head/token regroup (loopback all-to-all permutation); see cp_ulysses_regroup.
-
-    SEQ_TO_HEAD: inp [B, S_local, H, D] -> out [B, P*S_local, H/P, D];
-    HEAD_TO_SEQ: inp [B, P*S_local, H/P, D] -> out [B, S_local, H, D]. Both contiguous.
-    """
-    lib = _lib.load()
-    dev = _gpu("inp", inp).device
+def _regroup_shapes(inp, out, degree: int, direction: int, dev):
+    _gpu("inp", inp, dev)
     _gpu("out", out, dev)
     if inp.dtype != out.dtype:
         raise TypeError("inp and out must share a dtype")
@@ -337,9 +349,40 @@ def cp_ulysses_regroup(inp, out, degree: int, direction: int = CP_REGROUP_SEQ_TO
         raise ValueError(f"H={H} must be divisible by degree={degree}")
     if tuple(head.shape) != (B, degree * S_l, H // degree, D):
         raise ValueError(f"head-sharded side must be {(B, degree * S_l, H // degree, D)}, got {tuple(head.shape)}")
+    return B, S_l, H, D
+
+
+def cp_ulysses_regroup(inp, out, degree: int, direction: int = CP_REGROUP_SEQ_TO_HEAD, stream=None):
+    """Ulysses head/token regroup (loopback all-to-all permutation); see cp_ulysses_regroup.
+
+    SEQ_TO_HEAD: inp [B, S_local, H, D] -> out [B, P*S_local, H/P, D];
+    HEAD_TO_SEQ: inp [B, P*S_local, H/P, D] -> out [B, S_local, H, D]. Both contiguous.
+    """
+    lib = _lib.load()
+    dev = _gpu("inp", inp).device
+    B, S_l, H, D = _regroup_shapes(inp, out, degree, direction, dev)
     st = lib.cp_ulysses_regroup(inp.data_ptr(), out.data_ptr(), inp.element_size(), B, S_l, H, D, degree,
                                 direction, _stream(stream))
     _check(st, "cp_ulysses_regroup")
+
+
+def cp_ulysses_regroup_multi(inputs: Sequence, outputs: Sequence, degree: int,
+                             direction: int = CP_REGROUP_SEQ_TO_HEAD, stream=None):
+    """cp_ulysses_regroup of several tensors of one shape and dtype (Q, K and V) in one launch."""
+    lib = _lib.load()
+    if len(inputs) != len(outputs) or not 1 <= len(inputs) <= 8:
+        raise ValueError("inputs and outputs must be equally long lists of 1..8 tensors")
+    dev = _gpu("inputs[0]", inputs[0]).device
+    shapes = {_regroup_shapes(i, o, degree, direction, dev) for i, o in zip(inputs, outputs)}
+    if len(shapes) != 1 or len({t.dtype for t in inputs}) != 1:
+        raise ValueError("every tensor must have the same shape and dtype")
+    B, S_l, H, D = shapes.pop()
+    n = len(inputs)
+    ip = (ctypes.c_void_p * n)(*[t.data_ptr() for t in inputs])
+    op = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outputs])
+    st = lib.cp_ulysses_regroup_multi(ip, op, n, inputs[0].element_size(), B, S_l, H, D, degree, direction,
+                                      _stream(stream))
+    _check(st, "cp_ulysses_regroup_multi")
 
 
 def split_counts(n: int, parts: int):
@@ -488,8 +531,9 @@ def pack_v(v, stream=None) -> PackedV:
 
 
 def ring_attention(q, k_blocks, v_blocks, scale: Optional[float] = None, ring_anything: Optional[bool] = None,
-                   separate_merge: bool = False, stream=None) -> Tuple:
-    """Allocate (out, lse) and run cp_ring_attention; returns (out, lse)."""
+                   separate_merge: bool = False, stream=None, waves: int = 0) -> Tuple:
+    """Allocate (out, lse) and run cp_ring_attention; returns (out, lse). ``waves`` (4 or 8) forces the
+    bf16 block kernel's workgroup shape."""
     torch = _torch()
     B, Sq, H, D = q.shape
     out = torch.empty((B, Sq, H, D), dtype=torch.float32, device=q.device)
@@ -504,7 +548,8 @@ def ring_attention(q, k_blocks, v_blocks, scale: Optional[float] = None, ring_an
     nbytes = cp_ring_attention_workspace_size(B, H, Sq, D, flags)
     if nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    cp_ring_attention(q, k_blocks, v_blocks, out, lse, scale=scale, flags=flags, workspace=ws, stream=stream)
+    cp_ring_attention(q, k_blocks, v_blocks, out, lse, scale=scale, flags=flags, workspace=ws, stream=stream,
+                      waves=waves)
     return out, lse
 
 

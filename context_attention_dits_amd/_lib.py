@@ -20,8 +20,10 @@ CP_ERR_INVALID_ARG = 1
 CP_ERR_UNSUPPORTED = 2
 CP_ERR_WORKSPACE = 3
 CP_ERR_HIP = 4
+CP_ERR_ORDER = 5
 STATUS_NAMES = {0: "CP_OK", 1: "CP_ERR_INVALID_ARG", 2: "CP_ERR_UNSUPPORTED", 3: "CP_ERR_WORKSPACE",
-                4: "CP_ERR_HIP"}
+                4: "CP_ERR_HIP", 5: "CP_ERR_ORDER"}
+ABI_VERSION = 2
 
 CP_F32 = 0
 CP_BF16 = 1
@@ -31,6 +33,10 @@ CP_BLOCK_PACKED_V = 0x2
 CP_RING_ANYTHING = 0x2
 CP_RING_SEPARATE_MERGE = 0x4
 CP_RING_PACKED_V = 0x8
+CP_FWD_FOUR_WAVES = 0x100
+CP_FWD_EIGHT_WAVES = 0x200
+CP_ONE_LAUNCH_IN_TURN = 1
+CP_ONE_LAUNCH_PARALLEL = 2
 
 CP_BWD_ACCUMULATE_DQ = 0x1
 
@@ -44,9 +50,9 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 _SIGNATURES = {
     "cp_abi_version": (_i, []),
     "cp_last_error": (ctypes.c_char_p, []),
-    "cp_attn_set_fwd_waves": (_i, [_i]),
-    "cp_attn_fwd_waves": (_i, [_i, _i, _i, _i]),
-    "cp_ring_attention_one_launch": (_i, [_i, _i, _i, _i, _i, ctypes.POINTER(_i), _i]),
+    "cp_attn_fwd_waves": (_i, [_i, _i, _i, _i, ctypes.c_uint]),
+    "cp_ring_attention_one_launch": (_i, [_i, _i, _i, _i, _i, ctypes.POINTER(_i), _i, ctypes.c_uint]),
+    "cp_ring_attention_check": (_i, [_vp, ctypes.c_size_t, _vp]),
     "cp_attn_block_fwd": (_i, [_vp, _i64p, _vp, _vp, _i64p, _i, _i, _i, _i, _i, _i, ctypes.c_float,
                                ctypes.c_uint, _vp, _i64p, _vp, _vp]),
     "cp_lse_merge": (_i, [_vp, _vp, _vp, _vp, _i64p, _i64p, _i, _i, _i, _i, _vp]),
@@ -58,6 +64,8 @@ _SIGNATURES = {
                                ctypes.POINTER(_i), _i, _i, _i, _i, _i, _i, ctypes.c_float, ctypes.c_uint,
                                _vp, _i64p, _vp, _vp, ctypes.c_size_t, _vp]),
     "cp_ulysses_regroup": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "cp_ulysses_regroup_multi": (_i, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _i, _i, _i, _i, _i, _i, _i,
+                                      _vp]),
     "cp_ulysses_pack_heads": (_i, [_vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(_i), _i, _vp]),
     "cp_ulysses_concat_seq": (_i, [_vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(_i), _i, _vp]),
     "cp_attn_bwd_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
@@ -96,8 +104,8 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.cp_abi_version() != 1:
-        raise RuntimeError(f"{path}: ABI version {lib.cp_abi_version()}, expected 1")
+    if lib.cp_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path}: ABI version {lib.cp_abi_version()}, expected {ABI_VERSION}")
     _lib = lib
     return lib
 

@@ -41,8 +41,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (expected /opt/rocm/bin/hipcc)")
 
 
+# A second library for the GPU test of the one-launch ring's bounded merge wait: the same
+# sources with every merge, after its real wait, waiting 16 polls for a flag no workgroup sets,
+# so every wait gives up, is counted and poisons its tile, while every kernel still ends normally.
+RING_WAIT_TEST_LIB = "libcpattn_ringwait_test.so"
+RING_WAIT_TEST_DEFINES = {"CP_RING_TEST_NEVER_READY": "1"}
+
+
 def build(out: Optional[str] = None, defines: Optional[Dict[str, str]] = None,
-          build_dir: Optional[str] = None, verbose: bool = False) -> str:
+          build_dir: Optional[str] = None, verbose: bool = False, test_libs: bool = True) -> str:
     out = out or os.path.join(PKG, LIB_NAME)
     tag = "_".join(f"{k}{v}" for k, v in sorted((defines or {}).items())) or "default"
     build_dir = build_dir or os.path.join(PKG, "_build", tag)
@@ -60,20 +67,44 @@ def build(out: Optional[str] = None, defines: Optional[Dict[str, str]] = None,
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = out + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    # Resolve every symbol now (RTLD_NOW), so a missing kernel stub fails the build, not the first call.
-    try:
-        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
-    except OSError as e:
-        os.remove(tmp)
-        raise RuntimeError(f"built library does not load: {e}") from e
-    os.replace(tmp, out)
+    def link(objs: List[str], dst: str) -> None:
+        tmp = dst + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        # Resolve every symbol now (RTLD_NOW), so a missing kernel stub fails the build, not the first call.
+        try:
+            ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+        except OSError as e:
+            os.remove(tmp)
+            raise RuntimeError(f"built library does not load: {e}") from e
+        os.replace(tmp, dst)
+
+    # the ring-wait test library needs only the forward kernel recompiled with its define
+    wait_dir = os.path.join(PKG, "_build", "ringwait_test")
+    wait_obj = os.path.join(wait_dir, "attn_fwd_bf16.o")
+    with_test = test_libs and not defines
+
+    def compile_wait() -> str:
+        os.makedirs(wait_dir, exist_ok=True)
+        df = [f"-D{k}={v}" for k, v in sorted(RING_WAIT_TEST_DEFINES.items())]
+        cmd = [cc, *HIPCC_FLAGS, *df, "-c", os.path.join(CSRC, "attn_fwd_bf16.hip"), "-o", wait_obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for attn_fwd_bf16.hip (ring-wait test build):\n{r.stderr}")
+        return wait_obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+        futs = [ex.submit(compile_one, src) for src in SOURCES]
+        wait_fut = ex.submit(compile_wait) if with_test else None
+        objs = [f.result() for f in futs]
+        if wait_fut is not None:
+            wait_fut.result()
+    link(objs, out)
+    if with_test:
+        link([wait_obj if os.path.basename(o) == "attn_fwd_bf16.o" else o for o in objs],
+             os.path.join(os.path.dirname(out), RING_WAIT_TEST_LIB))
     return out
 
 

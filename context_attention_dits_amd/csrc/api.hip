@@ -25,7 +25,6 @@ namespace {
 using cpattn::Strides;
 
 thread_local std::string g_err;
-std::atomic<int> g_fwd_waves{0};  // cp_attn_set_fwd_waves
 
 cp_status_t fail(cp_status_t st, const char* fmt, ...) {
   char buf[512];
@@ -109,7 +108,7 @@ cp_status_t check_kv(const void* k, const void* v, int Skv) {
 // One validated block: launches the attention (overwrite or accumulate) or the empty fill.
 cp_status_t run_block(const void* q, Strides qs, const void* k, const void* v, Strides kvs, int dtype,
                       int B, int H, int D, int Sq, int Skv, float scale, bool accumulate, bool v_packed,
-                      float* out, Strides os, float* lse, hipStream_t stream) {
+                      int waves, float* out, Strides os, float* lse, hipStream_t stream, int* err = nullptr) {
   if (Skv == 0) {
     if (accumulate) return CP_OK;
     return hip_status(cpattn::launch_fill_empty(out, os, lse, B, H, Sq, D, stream), "fill_empty");
@@ -120,13 +119,21 @@ cp_status_t run_block(const void* q, Strides qs, const void* k, const void* v, S
   a.B = B; a.H = H; a.D = D; a.Sq = Sq; a.Skv = Skv;
   a.scale = scale;
   a.accumulate = accumulate;
-  a.waves = g_fwd_waves.load(std::memory_order_relaxed);
+  a.waves = waves;
   a.v_packed = v_packed;
+  a.err = err;
   if (dtype == CP_BF16) return hip_status(cpattn::launch_attn_fwd_bf16(a, stream), "attn_fwd_bf16");
   return hip_status(cpattn::launch_attn_fwd_f32(a, stream), "attn_fwd_f32");
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr unsigned kWaveFlags = CP_FWD_FOUR_WAVES | CP_FWD_EIGHT_WAVES;
+
+// The workgroup shape a call's flags force (4 or 8), or 0 to choose per launch.
+int forced_waves(unsigned flags) {
+  return (flags & CP_FWD_FOUR_WAVES) ? 4 : (flags & CP_FWD_EIGHT_WAVES) ? 8 : 0;
+}
 
 // Does a packed-V ring with a workspace run as one launch? When the blocks'
 // own launches would use the 4-wave kernel (a grid too small, or with a
@@ -138,10 +145,9 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // LSE). Bigger grids keep one launch per block, which measured as fast or
 // faster. (The output's byte offsets must also fit the kernel's 32-bit buffer
 // offsets; checked by the caller through o_end.)
-bool one_launch_ring(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree) {
+bool one_launch_ring(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree, int waves) {
   if (dtype != CP_BF16 || D != 128 || B <= 0 || H <= 0 || Sq <= 0) return false;
   if (cpattn::ring_max_blocks() < 2) return false;  // library built without the 8-wave shape
-  const int waves = g_fwd_waves.load(std::memory_order_relaxed);
   if (waves == 4) return false;
   cpattn::FwdArgs a{};
   a.B = B; a.H = H; a.D = D; a.Sq = Sq;
@@ -162,9 +168,8 @@ bool one_launch_ring(int dtype, int B, int H, int D, int Sq, const int* block_le
 // the 8-wave shape, 2 .. seq_max_blocks() non-empty blocks): saves the fixed
 // cost of every launch after the first (on the FLUX ring-2 share ~12-17 us of
 // a ~66 us launch).
-bool seq_ring(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree) {
+bool seq_ring(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree, int waves) {
   if (dtype != CP_BF16 || D != 128 || B <= 0 || H <= 0 || Sq <= 0) return false;
-  const int waves = g_fwd_waves.load(std::memory_order_relaxed);
   if (waves == 4) return false;
   cpattn::FwdArgs a{};
   a.B = B; a.H = H; a.D = D; a.Sq = Sq;
@@ -187,35 +192,35 @@ int cp_abi_version(void) { return CP_ATTN_ABI_VERSION; }
 
 const char* cp_last_error(void) { return g_err.c_str(); }
 
-int cp_attn_fwd_waves(int B, int H, int D, int Sq) {
+int cp_attn_fwd_waves(int B, int H, int D, int Sq, unsigned flags) {
   if (B <= 0 || H <= 0 || Sq <= 0 || (D != 64 && D != 128)) return 0;
+  if ((flags & kWaveFlags) == kWaveFlags) return 0;
   cpattn::FwdArgs a{};
   a.B = B; a.H = H; a.D = D; a.Sq = Sq;
-  a.waves = g_fwd_waves.load(std::memory_order_relaxed);
+  a.waves = forced_waves(flags);
   return cpattn::pick_waves(a);
 }
 
-int cp_ring_attention_one_launch(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree) {
+int cp_ring_attention_one_launch(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree,
+                                 unsigned flags) {
   if (block_len == nullptr || ring_degree < 1) return 0;
+  if ((flags & kWaveFlags) == kWaveFlags || (flags & CP_RING_SEPARATE_MERGE)) return 0;
   for (int i = 0; i < ring_degree; ++i)
     if (block_len[i] < 0) return 0;
-  return (one_launch_ring(dtype, B, H, D, Sq, block_len, ring_degree) ||
-          seq_ring(dtype, B, H, D, Sq, block_len, ring_degree))
-             ? 1
-             : 0;
-}
-
-int cp_attn_set_fwd_waves(int waves) {
-  if (waves != 0 && waves != 4 && waves != 8) return -1;
-  return g_fwd_waves.exchange(waves);
+  const int waves = forced_waves(flags);
+  if (one_launch_ring(dtype, B, H, D, Sq, block_len, ring_degree, waves)) return CP_ONE_LAUNCH_PARALLEL;
+  if (seq_ring(dtype, B, H, D, Sq, block_len, ring_degree, waves)) return CP_ONE_LAUNCH_IN_TURN;
+  return 0;
 }
 
 cp_status_t cp_attn_block_fwd(const void* q, const int64_t* q_strides, const void* k, const void* v,
                               const int64_t* kv_strides, int dtype, int B, int H, int D, int Sq,
                               int Skv, float scale, unsigned flags, float* out,
                               const int64_t* out_strides, float* lse, void* stream) {
-  if (flags & ~(CP_BLOCK_ACCUMULATE | CP_BLOCK_PACKED_V))
+  if (flags & ~(CP_BLOCK_ACCUMULATE | CP_BLOCK_PACKED_V | kWaveFlags))
     return fail(CP_ERR_INVALID_ARG, "cp_attn_block_fwd: unknown flags 0x%x", flags);
+  if ((flags & kWaveFlags) == kWaveFlags)
+    return fail(CP_ERR_INVALID_ARG, "cp_attn_block_fwd: CP_FWD_FOUR_WAVES and CP_FWD_EIGHT_WAVES together");
   const bool packed = (flags & CP_BLOCK_PACKED_V) != 0;
   if (packed && dtype != CP_BF16)
     return fail(CP_ERR_UNSUPPORTED, "cp_attn_block_fwd: packed V is for CP_BF16 only");
@@ -227,7 +232,7 @@ cp_status_t cp_attn_block_fwd(const void* q, const int64_t* q_strides, const voi
   if (B == 0 || H == 0 || Sq == 0) return CP_OK;
   if ((st = check_kv(k, v, Skv)) != CP_OK) return st;
   return run_block(q, qs, k, v, kvs, dtype, B, H, D, Sq, Skv, scale, (flags & CP_BLOCK_ACCUMULATE) != 0,
-                   packed, out, os, lse, static_cast<hipStream_t>(stream));
+                   packed, forced_waves(flags), out, os, lse, static_cast<hipStream_t>(stream));
 }
 
 cp_status_t cp_lse_merge(float* out_acc, float* lse_acc, const float* out_blk, const float* lse_blk,
@@ -324,7 +329,7 @@ size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned fl
   if (B <= 0 || H <= 0 || Sq <= 0 || D <= 0) return 0;
   if (flags & CP_RING_SEPARATE_MERGE) return partial_bytes(B, H, Sq, D);
   if (D == 128 && (flags & CP_RING_PACKED_V))
-    return align_up((size_t)cpattn::ring_flag_count(B, H, Sq) * sizeof(int), 256);
+    return align_up((size_t)(cpattn::kRingFlagOffset + cpattn::ring_flag_count(B, H, Sq)) * sizeof(int), 256);
   return 0;
 }
 
@@ -334,8 +339,11 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
                               int Sq, float scale, unsigned flags, float* out,
                               const int64_t* out_strides, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  if (flags & ~(CP_RING_ANYTHING | CP_RING_SEPARATE_MERGE | CP_RING_PACKED_V))
+  if (flags & ~(CP_RING_ANYTHING | CP_RING_SEPARATE_MERGE | CP_RING_PACKED_V | kWaveFlags))
     return fail(CP_ERR_INVALID_ARG, "cp_ring_attention: unknown flags 0x%x", flags);
+  if ((flags & kWaveFlags) == kWaveFlags)
+    return fail(CP_ERR_INVALID_ARG, "cp_ring_attention: CP_FWD_FOUR_WAVES and CP_FWD_EIGHT_WAVES together");
+  const int waves = forced_waves(flags);
   const bool packed = (flags & CP_RING_PACKED_V) != 0;
   if (packed && dtype != CP_BF16)
     return fail(CP_ERR_UNSUPPORTED, "cp_ring_attention: packed V is for CP_BF16 only");
@@ -370,14 +378,14 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
   float* ws_out = nullptr;
   float* ws_lse = nullptr;
   int* ws_flags = nullptr;  // one launch for all blocks (see cp_ring_attention_workspace_size)
-  if (!separate && workspace != nullptr && B > 0 && H > 0 && Sq > 0) {
+  if (!separate && workspace != nullptr && B > 0 && H > 0 && Sq > 0 && D == 128 && packed) {
     const size_t need = cp_ring_attention_workspace_size(B, H, Sq, D, flags);
     if (workspace_bytes < need)
       return fail(CP_ERR_WORKSPACE, "cp_ring_attention: workspace of %zu bytes needed, %zu given", need,
                   workspace_bytes);
     if (!aligned(workspace, 256))
       return fail(CP_ERR_UNSUPPORTED, "cp_ring_attention: workspace must be 256-byte aligned");
-    if (need > 0) ws_flags = static_cast<int*>(workspace);
+    ws_flags = static_cast<int*>(workspace);
   }
   if (separate && B > 0 && H > 0 && Sq > 0) {
     const size_t need = partial_bytes(B, H, Sq, D);
@@ -393,7 +401,7 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
   if (B == 0 || H == 0 || Sq == 0) return CP_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (ws_flags != nullptr && packed && one_launch_ring(dtype, B, H, D, Sq, block_len, ring_degree)) {
+  if (ws_flags != nullptr && packed && one_launch_ring(dtype, B, H, D, Sq, block_len, ring_degree, waves)) {
     const void* kb[16];
     const void* vb[16];
     int len[16], vt0[16], vnt[16];
@@ -431,7 +439,7 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
       return hip_status(cpattn::launch_ring_bf16(a, rb, ws_flags, s), "attn_fwd_bf16 (ring)");
     }
   }
-  if (packed && !separate && seq_ring(dtype, B, H, D, Sq, block_len, ring_degree)) {
+  if (packed && !separate && seq_ring(dtype, B, H, D, Sq, block_len, ring_degree, waves)) {
     const void* kb[16];
     const void* vb[16];
     int len[16], vt0[16], vnt[16];
@@ -453,6 +461,7 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
     a.accumulate = false;
     a.waves = 8;
     a.v_packed = true;
+    a.err = ws_flags;
     const cpattn::RingBlocks rb{n, kb, vb, len, vt0, vnt};
     return hip_status(cpattn::launch_ring_seq_bf16(a, rb, s), "attn_fwd_bf16 (blocks in turn)");
   }
@@ -490,21 +499,40 @@ cp_status_t cp_ring_attention(const void* q, const int64_t* q_strides, const voi
     if (block_len[i] == 0) continue;  // a block over no keys has weight 0 in the merge
     if (!have) {
       st = run_block(q, qs, k_blocks[i], v_blocks[i], kvs, dtype, B, H, D, Sq, block_len[i], scale, false,
-                     packed, out, os, lse, s);
+                     packed, waves, out, os, lse, s, ws_flags);
       have = true;
     } else if (separate) {
       st = run_block(q, qs, k_blocks[i], v_blocks[i], kvs, dtype, B, H, D, Sq, block_len[i], scale, false,
-                     packed, ws_out, ws_s, ws_lse, s);
+                     packed, waves, ws_out, ws_s, ws_lse, s);
       if (st == CP_OK)
         st = hip_status(cpattn::launch_lse_merge(out, lse, ws_out, ws_lse, os, ws_s, B, H, Sq, D, s),
                         "lse_merge");
     } else {
       st = run_block(q, qs, k_blocks[i], v_blocks[i], kvs, dtype, B, H, D, Sq, block_len[i], scale, true,
-                     packed, out, os, lse, s);
+                     packed, waves, out, os, lse, s);
     }
     if (st != CP_OK) return st;
   }
   if (!have) return hip_status(cpattn::launch_fill_empty(out, os, lse, B, H, Sq, D, s), "fill_empty");
+  return CP_OK;
+}
+
+cp_status_t cp_ring_attention_check(const void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "cp_ring_attention_check";
+  if (workspace == nullptr || workspace_bytes < (size_t)cpattn::kRingFlagOffset * sizeof(int))
+    return fail(CP_ERR_WORKSPACE, "%s: a ring workspace of at least %zu bytes is needed", fn,
+                (size_t)cpattn::kRingFlagOffset * sizeof(int));
+  if (!aligned(workspace, 256)) return fail(CP_ERR_UNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int gave_up = 0;
+  cp_status_t st = hip_status(hipMemcpyAsync(&gave_up, workspace, sizeof(int), hipMemcpyDeviceToHost, s), fn);
+  if (st != CP_OK) return st;
+  if ((st = hip_status(hipStreamSynchronize(s), fn)) != CP_OK) return st;
+  if (gave_up != 0)
+    return fail(CP_ERR_ORDER,
+                "%s: %d merge wait(s) of the last parallel-partials ring launch gave up; the query tiles "
+                "concerned hold NaN",
+                fn, gave_up);
   return CP_OK;
 }
 
@@ -859,30 +887,59 @@ cp_status_t cp_ring_attention_bwd(const void* q, const int64_t* q_strides, const
   return CP_OK;
 }
 
-cp_status_t cp_ulysses_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
-                               int D, int degree, int direction, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launch shared by cp_ulysses_regroup (one tensor) and cp_ulysses_regroup_multi.
+cp_status_t regroup_impl(const char* fn, const void* const* in, void* const* out, int n_tensors, int elem_bytes,
+                         int B, int S_local, int H, int D, int degree, int direction, void* stream) {
   if (elem_bytes != 2 && elem_bytes != 4)
-    return fail(CP_ERR_UNSUPPORTED, "cp_ulysses_regroup: elem_bytes must be 2 or 4 (got %d)", elem_bytes);
-  if (B < 0 || S_local < 0 || H < 0 || D < 0)
-    return fail(CP_ERR_INVALID_ARG, "cp_ulysses_regroup: sizes must be non-negative");
-  if (degree < 1) return fail(CP_ERR_INVALID_ARG, "cp_ulysses_regroup: degree must be >= 1 (got %d)", degree);
+    return fail(CP_ERR_UNSUPPORTED, "%s: elem_bytes must be 2 or 4 (got %d)", fn, elem_bytes);
+  if (B < 0 || S_local < 0 || H < 0 || D < 0) return fail(CP_ERR_INVALID_ARG, "%s: sizes must be non-negative", fn);
+  if (degree < 1) return fail(CP_ERR_INVALID_ARG, "%s: degree must be >= 1 (got %d)", fn, degree);
   if (H % degree != 0)
-    return fail(CP_ERR_INVALID_ARG,
-                "cp_ulysses_regroup: the number of heads H=%d must be divisible by the Ulysses degree %d",
+    return fail(CP_ERR_INVALID_ARG, "%s: the number of heads H=%d must be divisible by the Ulysses degree %d", fn,
                 H, degree);
   if (direction != CP_REGROUP_SEQ_TO_HEAD && direction != CP_REGROUP_HEAD_TO_SEQ)
-    return fail(CP_ERR_INVALID_ARG, "cp_ulysses_regroup: unknown direction %d", direction);
+    return fail(CP_ERR_INVALID_ARG, "%s: unknown direction %d", fn, direction);
   const int64_t bytes = (int64_t)B * S_local * H * D * elem_bytes;
   if (bytes == 0) return CP_OK;
-  if (!in || !out) return fail(CP_ERR_INVALID_ARG, "cp_ulysses_regroup: pointers must be non-null");
-  const uintptr_t a = reinterpret_cast<uintptr_t>(in), b = reinterpret_cast<uintptr_t>(out);
-  if (a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes)
-    return fail(CP_ERR_INVALID_ARG, "cp_ulysses_regroup: in and out overlap");
-  if (!aligned(in, elem_bytes) || !aligned(out, elem_bytes))
-    return fail(CP_ERR_UNSUPPORTED, "cp_ulysses_regroup: pointers must be aligned to elem_bytes");
-  return hip_status(cpattn::launch_regroup(in, out, elem_bytes, B, S_local, H, D, degree, direction,
+  auto overlap = [bytes](const void* x, const void* y) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+    return a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes;
+  };
+  for (int i = 0; i < n_tensors; ++i) {
+    if (!in[i] || !out[i]) return fail(CP_ERR_INVALID_ARG, "%s: pointers must be non-null", fn);
+    if (!aligned(in[i], elem_bytes) || !aligned(out[i], elem_bytes))
+      return fail(CP_ERR_UNSUPPORTED, "%s: pointers must be aligned to elem_bytes", fn);
+    for (int j = 0; j < n_tensors; ++j) {
+      if (overlap(in[j], out[i])) return fail(CP_ERR_INVALID_ARG, "%s: in and out overlap", fn);
+      if (j != i && overlap(out[j], out[i])) return fail(CP_ERR_INVALID_ARG, "%s: outputs %d and %d overlap", fn, j, i);
+    }
+  }
+  return hip_status(cpattn::launch_regroup(in, out, n_tensors, elem_bytes, B, S_local, H, D, degree, direction,
                                            static_cast<hipStream_t>(stream)),
                     "ulysses_regroup");
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status_t cp_ulysses_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
+                               int D, int degree, int direction, void* stream) {
+  return regroup_impl("cp_ulysses_regroup", &in, &out, 1, elem_bytes, B, S_local, H, D, degree, direction, stream);
+}
+
+cp_status_t cp_ulysses_regroup_multi(const void* const* in, void* const* out, int n_tensors, int elem_bytes, int B,
+                                     int S_local, int H, int D, int degree, int direction, void* stream) {
+  const char* fn = "cp_ulysses_regroup_multi";
+  if (n_tensors < 1 || n_tensors > cpattn::kMaxRegroupTensors)
+    return fail(CP_ERR_INVALID_ARG, "%s: n_tensors must be in 1..%d (got %d)", fn, cpattn::kMaxRegroupTensors,
+                n_tensors);
+  if (!in || !out) return fail(CP_ERR_INVALID_ARG, "%s: pointer arrays must be non-null", fn);
+  return regroup_impl(fn, in, out, n_tensors, elem_bytes, B, S_local, H, D, degree, direction, stream);
 }
 
 }  // extern "C"
@@ -949,3 +1006,4 @@ cp_status_t cp_ulysses_concat_seq(const void* in, void* out, int elem_bytes, int
 }
 
 }  // extern "C"
+

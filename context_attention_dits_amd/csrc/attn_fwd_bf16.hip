@@ -89,8 +89,14 @@
 #ifndef CP_FWD_SCHED_PV
 #define CP_FWD_SCHED_PV 1  // pipeline the transposing V reads ahead of the PV MFMAs
 #endif
-#ifndef CP_RING_SC1
-#define CP_RING_SC1 0  // one-launch ring: device-scope (1) or L2-coherent (0) out/lse accesses
+#ifndef CP_RING_ACQREL
+#define CP_RING_ACQREL 0  // 1: order the one-launch ring's merges with agent-scope acquire/release (measured slower)
+#endif
+#ifndef CP_RING_SPIN_LIMIT
+#define CP_RING_SPIN_LIMIT (1 << 22)  // one-launch ring: polls before a merge wait gives up
+#endif
+#ifndef CP_RING_TEST_NEVER_READY
+#define CP_RING_TEST_NEVER_READY 0  // test builds only: after its real wait, every merge waits for a flag no workgroup sets
 #endif
 #ifndef CP_FWD_SEQ
 #define CP_FWD_SEQ 1  // rings of 2+ blocks on the 8-wave shape: one launch, blocks in turn per workgroup
@@ -116,9 +122,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Word 3 of a raw (unswizzled, untyped) buffer descriptor on gfx9-family GPUs.
 constexpr int kBufferFlags = 0x00020000;
-// Cache-policy operand of buffer loads/stores for device scope (sc1): the
-// access bypasses the caches that are not coherent across XCDs.
-constexpr int kDeviceScope = 16;
+
+// Cache-policy operand of buffer loads: sc0 makes a load miss the CU's L1
+// (it is served by the XCD's L2).
+constexpr int kMissL1 = 1;
 
 // One launch over several ring blocks: at most this many (more run as one launch each).
 constexpr int kMaxRingBlocks = 16;
@@ -138,9 +145,11 @@ struct Params {
   float c;   // scale * log2(e)
   // Ring launch only: workgroup i works on block i / u8 (u8 = n_wg rounded up
   // to a multiple of 8, so that a query tile has the same XCD in every block);
-  // flags[tile] = index of the last block merged into (out, lse) for that tile.
+  // flags[tile] = index of the last block merged into (out, lse) for that tile;
+  // *err counts the merge waits that gave up (their query tiles are set to NaN).
   int n_blk, u8, spin_limit;
   int* flags;
+  int* err;  // also for the other forms: zeroed by workgroup 0 when not null
   const uint16_t* kblk[kMaxRingBlocks];
   const uint16_t* vblk[kMaxRingBlocks];
   int lblk[kMaxRingBlocks];
@@ -161,6 +170,9 @@ __device__ __forceinline__ float half_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Index of the XCD this wave runs on (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15; }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // 16 bytes per lane from global memory at base + voff into LDS at
@@ -259,10 +271,14 @@ attn_fwd_bf16_kernel(Params p) {
   } else {
     tile = xcd_remap(blockIdx.x, p.n_wg);
   }
-  const int qt = tile % p.n_qt;
-  const int bh = tile / p.n_qt;
-  const int h = bh % p.H, b = bh / p.H;
-  const int qrow0 = qt * C::BM + wave * (QB * 32);
+  int qt = tile % p.n_qt;
+  int bh = tile / p.n_qt;
+  int h = bh % p.H, b = bh / p.H;
+  int qrow0 = qt * C::BM + wave * (QB * 32);
+  if constexpr (!RING) {
+    // a ring call's workspace error count: this form has no merge waits
+    if (p.err != nullptr && blockIdx.x == 0 && tid == 0) *p.err = 0;
+  }
 
   // SEQ: the workgroup takes its query tile through every block in turn
   // (block 0 written, later blocks merged by the epilogue); the next block's
@@ -812,61 +828,78 @@ seq_next_block:
 
   // ---- epilogue: normalise, LSE, optional merge into the accumulator
   // RING: block 0 writes, later blocks merge, each after the previous block's
-  // workgroup for the same query tile has published its (out, lse): it waits
-  // for flags[tile] == blk - 1. (out, lse) and the flags go through
-  // device-scope accesses, which bypass the caches that are not coherent
-  // across XCDs, so a reader sees what the writer's completed stores left in
-  // memory. The wait is bounded; it cannot deadlock: the awaited workgroup
-  // has the same index modulo u8, so it runs on the same XCD, which starts
-  // workgroups in index order, and it waits only on earlier ones itself.
+  // workgroup for the same query tile has published its (out, lse): that
+  // workgroup's stores have completed (reached its XCD's L2) before it sets
+  // flags[tile] = 16 * blk + (its XCD), and this workgroup waits for
+  // 16 * (blk - 1) + x. The merge reads out and lse past its CU's L1, from the
+  // L2, which holds what the publisher wrote only if x is this workgroup's
+  // own XCD: workgroups whose index differs by a multiple of 8 run on one
+  // XCD, which the launch arranges, and the flag checks it (a flag from
+  // another XCD counts as a failed wait). No cache is written back or
+  // invalidated. (CP_RING_ACQREL=1 builds order the merges with agent-scope
+  // acquire/release instead, which is slower.) The wait cannot deadlock: the
+  // awaited workgroup has the same index modulo u8 and a lower index, and it
+  // waits only on lower ones itself. It is bounded all the same: a wait that
+  // gives up counts itself in *err and sets the tile's out and lse to NaN
+  // instead of merging, then publishes as usual, so no later block waits on
+  // it in vain and the result cannot pass for a correct one.
   bool acc = ACC || (SEQ && sblk > 0);
+  bool gave_up = false;
   if constexpr (RING) {
     acc = blk > 0;
     if (acc) {
+      __shared__ int s_gave_up;
       if (threadIdx.x == 0) {
-        int n = 0;
-        while (__hip_atomic_load(p.flags + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != blk - 1 &&
-               ++n < p.spin_limit)
-          __builtin_amdgcn_s_sleep(1);
+        auto poll = [&] {
+          return CP_RING_ACQREL ? __hip_atomic_load(p.flags + tile, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
+                                : __hip_atomic_load(p.flags + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        int n = 0, f = -1;
+        bool ready;
+        while (!(ready = (f = poll()) >= 0 && (f >> 4) == blk - 1) && ++n < p.spin_limit) __builtin_amdgcn_s_sleep(1);
+        if (!CP_RING_ACQREL && ready && (f & 15) != xcc_id()) ready = false;  // not this XCD's L2
+        if (CP_RING_TEST_NEVER_READY && ready) {
+          // test builds: then a second, short wait for a value no workgroup publishes
+          n = 0;
+          while (!(ready = poll() == 16 * (blk + 1000)) && ++n < 16) __builtin_amdgcn_s_sleep(1);
+        }
+        s_gave_up = !ready;
+        if (!ready) __hip_atomic_fetch_add(p.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
+      gave_up = s_gave_up != 0;
     }
   }
   // accesses to out and lse. RING: through a buffer descriptor with 32-bit
-  // offsets (fewer address registers than 64-bit pointers), with device
-  // scope (CP_RING_SC1: bypassing the caches) or plain (coherent through the
-  // XCD's L2 that all workgroups of a query tile share).
+  // offsets (fewer address registers than 64-bit pointers).
   const __amdgpu_buffer_rsrc_t orsrc =
       __builtin_amdgcn_make_buffer_rsrc(p.out, (short)0, 0x7fffffff, kBufferFlags);
-  constexpr int kRingPolicy = CP_RING_SC1 ? kDeviceScope : 0;
+  const __amdgpu_buffer_rsrc_t lrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(p.lse, (short)0, 0x7fffffff, kBufferFlags);
+  constexpr int kMergeLoad = CP_RING_ACQREL ? 0 : kMissL1;  // RING: past any stale L1 copy
   auto o_load = [&](const float* ptr) -> f32x4 {
     if constexpr (RING) {
-      return __builtin_amdgcn_raw_buffer_load_b128(orsrc, (int)((ptr - p.out) * 4), 0, kRingPolicy);
+      return __builtin_amdgcn_raw_buffer_load_b128(orsrc, (int)((ptr - p.out) * 4), 0, kMergeLoad);
     } else {
       return *reinterpret_cast<const f32x4*>(ptr);
     }
   };
   auto o_store = [&](float* ptr, f32x4 v) {
     if constexpr (RING) {
-      __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (int)((ptr - p.out) * 4), 0, kRingPolicy);
+      __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (int)((ptr - p.out) * 4), 0, 0);
     } else {
       *reinterpret_cast<f32x4*>(ptr) = v;
     }
   };
   auto l_load = [&](const float* ptr) -> float {
-    if constexpr (RING && CP_RING_SC1) {
-      return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (RING) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrsrc, (int)((ptr - p.lse) * 4), 0,
+                                                                            kMergeLoad));
     } else {
       return *ptr;
     }
   };
-  auto l_store = [&](float* ptr, float v) {
-    if constexpr (RING && CP_RING_SC1) {
-      __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      *ptr = v;
-    }
-  };
+  auto l_store = [&](float* ptr, float v) { *ptr = v; };
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qrow0 + qb * 32 + l32;
@@ -876,7 +909,15 @@ seq_next_block:
     if (row < p.Sq) {
       float* orow = p.out + b * p.o_sb + (int64_t)row * p.o_ss + h * p.o_sh;
       float* lrow = p.lse + ((int64_t)b * p.H + h) * p.Sq + row;
-      if (acc) {
+      if (RING && gave_up) {
+        // the previous block's partial for this tile was not seen: no merge
+        const f32x4 nan4 = {NAN, NAN, NAN, NAN};
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) o_store(orow + db * 32 + 8 * g + 4 * hi, nan4);
+        if (hi == 0) l_store(lrow, NAN);
+      } else if (acc) {
         const float la2 = (SEQ ? lse_keep[qb] : l_load(lrow)) * kLog2e;
         const float M = fmaxf(la2, lse2);
         const float wa = fast_exp2(la2 - M);  // 0 when the accumulator is empty (-inf)
@@ -911,10 +952,17 @@ seq_next_block:
     }
   }
   if constexpr (RING) {
-    // publish: every wave's stores have completed, then the flag
+    // publish: every wave's stores have completed, then the flag (release:
+    // those stores become visible to an acquiring reader first)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt: no wait
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(p.flags + tile, blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      const int f = 16 * blk + xcc_id();
+      if (CP_RING_ACQREL)
+        __hip_atomic_store(p.flags + tile, f, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        __hip_atomic_store(p.flags + tile, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   if constexpr (SEQ) {
     seq_prev_stage = (n_tiles - 1) % 3;
@@ -926,7 +974,7 @@ template <int D, int NW, bool ACC, bool PACKED>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   constexpr int QB = CP_FWD_QB;
   using C = Cfg<D, QB, NW>;
-  Params p;
+  Params p{};
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
   p.v = static_cast<const uint16_t*>(a.v);
@@ -941,25 +989,30 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
   p.n_wg = (int)n_wg;
   p.c = a.scale * kLog2e;
+  p.err = a.err;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, NW, ACC, PACKED, false>), dim3(p.n_wg), dim3(C::NT), 0, stream,
                      p);
   return hipGetLastError();
 }
 
-__global__ void __launch_bounds__(256) fill_flags_kernel(int* flags, int n) {
+// Reset of the ring launch's workspace: the error count to 0, every flag to -1.
+__global__ void __launch_bounds__(256) fill_flags_kernel(int* err, int* flags, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) flags[i] = -1;
+  if (i == 0) *err = 0;
 }
 
 // One launch for a ring of blocks (ping-pong shape, D = 128): n_blk * u8
 // workgroups, block-major; see the kernel's epilogue for the ordering of the
-// merges. flags: n_wg ints, reset here by a fill kernel (no memset, so the
-// pair can be captured in a graph).
+// merges. ws: the error count, then (at int 64) n_wg flags, reset here by a
+// fill kernel (no memset, so the pair can be captured in a graph).
 template <bool PACKED>
-hipError_t launch_ring_128(const FwdArgs& a, const RingBlocks& rb, int* flags, hipStream_t stream) {
+hipError_t launch_ring_128(const FwdArgs& a, const RingBlocks& rb, int* ws, hipStream_t stream) {
+  int* const err = ws;
+  int* const flags = ws + kRingFlagOffset;
   constexpr int QB = CP_FWD_QB;
   using C = Cfg<128, QB, 8>;
-  Params p;
+  Params p{};
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = nullptr;
   p.v = nullptr;
@@ -976,8 +1029,9 @@ hipError_t launch_ring_128(const FwdArgs& a, const RingBlocks& rb, int* flags, h
   p.n_wg = (int)n_wg;
   p.u8 = (int)u8;
   p.n_blk = rb.n;
-  p.spin_limit = 1 << 22;
+  p.spin_limit = CP_RING_SPIN_LIMIT;
   p.flags = flags;
+  p.err = err;
   p.c = a.scale * kLog2e;
   for (int i = 0; i < kMaxRingBlocks; ++i) {
     p.kblk[i] = i < rb.n ? static_cast<const uint16_t*>(rb.k[i]) : nullptr;
@@ -986,7 +1040,7 @@ hipError_t launch_ring_128(const FwdArgs& a, const RingBlocks& rb, int* flags, h
     p.vnt[i] = i < rb.n ? rb.vnt[i] : 0;
   }
   if (a.accumulate) return hipErrorInvalidValue;  // the ring launch writes block 0
-  hipLaunchKernelGGL(fill_flags_kernel, dim3((unsigned)((n_wg + 255) / 256)), dim3(256), 0, stream, flags,
+  hipLaunchKernelGGL(fill_flags_kernel, dim3((unsigned)((n_wg + 255) / 256)), dim3(256), 0, stream, err, flags,
                      (int)n_wg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1002,7 +1056,7 @@ hipError_t launch_ring_128(const FwdArgs& a, const RingBlocks& rb, int* flags, h
 hipError_t launch_seq_128(const FwdArgs& a, const RingBlocks& rb, hipStream_t stream) {
   constexpr int QB = CP_FWD_QB;
   using C = Cfg<128, QB, 8>;
-  Params p;
+  Params p{};
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = nullptr;
   p.v = nullptr;
@@ -1021,6 +1075,7 @@ hipError_t launch_seq_128(const FwdArgs& a, const RingBlocks& rb, hipStream_t st
   p.n_blk = rb.n;
   p.spin_limit = 0;
   p.flags = nullptr;
+  p.err = a.err;
   p.c = a.scale * kLog2e;
   for (int i = 0; i < kMaxRingBlocks; ++i) {
     const bool in = i < rb.n;
@@ -1159,12 +1214,9 @@ hipError_t launch_dn(const FwdArgs& a, hipStream_t stream) {
   return launch_dw<D, 4>(a, stream);
 }
 
-// With L2-coherent out/lse accesses a merging workgroup must not find a
-// stale copy of its tile's output in its CU's L1: the L1 only holds lines the
-// CU has read, and with at most 3 blocks a tile is merged at most twice, the
-// second time by a CU that has either not read the tile before or written it
-// itself since. More blocks run as one launch per block.
-int ring_max_blocks() { return CP_FWD_QB != 1 ? 0 : CP_RING_SC1 ? kMaxRingBlocks : 3; }
+// The merges of the ring launch read past the L1, so no stale copy of a tile
+// can be hit however many blocks merge into it.
+int ring_max_blocks() { return CP_FWD_QB != 1 ? 0 : kMaxRingBlocks; }
 
 int seq_max_blocks() { return (CP_FWD_SEQ && CP_FWD_QB == 1) ? kMaxRingBlocks : 0; }
 
@@ -1178,11 +1230,12 @@ hipError_t launch_ring_seq_bf16(const FwdArgs& a, const RingBlocks& rb, hipStrea
 
 int64_t ring_flag_count(int B, int H, int Sq) { return (int64_t)((Sq + 255) / 256) * H * B; }
 
-hipError_t launch_ring_bf16(const FwdArgs& a, const RingBlocks& rb, int* flags, hipStream_t stream) {
+
+hipError_t launch_ring_bf16(const FwdArgs& a, const RingBlocks& rb, int* ws, hipStream_t stream) {
   if constexpr (CP_FWD_QB == 1) {
     // packed V only: with V transposed in the kernel the ring variant spills heavily
     if (a.D != 128 || !a.v_packed) return hipErrorInvalidValue;
-    return launch_ring_128<true>(a, rb, flags, stream);
+    return launch_ring_128<true>(a, rb, ws, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -46,6 +46,11 @@ struct FwdArgs {
   bool accumulate;  // merge into (out, lse) instead of overwriting
   int waves;        // bf16 workgroup shape: 4, 8, or 0 to choose per launch
   bool v_packed;    // bf16: v is the output of launch_pack_v for this block (kvs is K's)
+  // bf16 ring calls given a workspace: its count of merge waits that gave up. The
+  // parallel-partials launch resets it with its own reset kernel; the other
+  // launches set it to 0 from their first workgroup, so that it always
+  // describes the last call that used the workspace.
+  int* err = nullptr;
 };
 
 // V of one bf16 block rewritten in the tile / fragment order that the
@@ -108,10 +113,12 @@ int pick_waves(const FwdArgs& a);
 
 // One launch for all the (non-empty) blocks of a ring, bf16, D = 128, packed V: the
 // blocks' partials are computed in parallel and merged into (out, lse) in
-// block order, each query tile's merges ordered through flags[tile]
-// (ring_flag_count ints of caller memory, 4-byte aligned; reset by the
-// launch). a.k, a.v, a.Skv and a.accumulate are not used; a.kvs is the blocks'
-// shared stride triple and a.v_packed says whether every v[i] is packed.
+// block order, each query tile's merges ordered through a flag. ws is caller
+// memory, 4-byte aligned: ws[0] counts the merge waits that gave up (their
+// tiles are set to NaN), ws[kRingFlagOffset ..] holds ring_flag_count flags;
+// both are reset by the launch. a.k, a.v, a.Skv and a.accumulate are not
+// used; a.kvs is the blocks' shared stride triple and a.v_packed says whether
+// every v[i] is packed.
 struct RingBlocks {
   int n;
   const void* const* k;  // K of block i at its first key (kvs strides)
@@ -122,7 +129,8 @@ struct RingBlocks {
 };
 int ring_max_blocks();
 int64_t ring_flag_count(int B, int H, int Sq);
-hipError_t launch_ring_bf16(const FwdArgs& a, const RingBlocks& rb, int* flags, hipStream_t stream);
+constexpr int kRingFlagOffset = 64;  // ints before the first flag (256 bytes: the error count, padding)
+hipError_t launch_ring_bf16(const FwdArgs& a, const RingBlocks& rb, int* ws, hipStream_t stream);
 // One launch for 2..seq_max_blocks() non-empty blocks (bf16, D = 128, packed V,
 // 8-wave shape): each workgroup takes its query tile through the blocks in
 // turn, block 0 written and later blocks merged in its epilogue (the
@@ -159,8 +167,10 @@ constexpr int kMaxUlyssesDegree = 64;
 hipError_t launch_pieces(const void* in, void* out, int axis, int64_t B, int64_t M, int64_t unit_bytes,
                          int64_t units_per_row, const int* seg_units, int P, int to_pieces, hipStream_t stream);
 
-// Ulysses regroup bit copy; see cp_ulysses_regroup.
-hipError_t launch_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
-                          int D, int degree, int direction, hipStream_t stream);
+// Ulysses regroup bit copy of n (1..kMaxRegroupTensors) tensors of one shape in
+// one launch; see cp_ulysses_regroup and cp_ulysses_regroup_multi.
+constexpr int kMaxRegroupTensors = 8;
+hipError_t launch_regroup(const void* const* in, void* const* out, int n, int elem_bytes, int B, int S_local,
+                          int H, int D, int degree, int direction, hipStream_t stream);
 
 }  // namespace cpattn

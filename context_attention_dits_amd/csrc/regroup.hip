@@ -62,13 +62,19 @@ struct RegroupDiv<W, int64_t> {  // plain 64-bit division for tensors of 2^31 wo
   __device__ __forceinline__ int64_t by_s(int64_t n) const { return n / s_local; }
 };
 
+// Up to kMaxRegroupTensors tensors of one shape regrouped by one launch (the
+// Ulysses exchange moves Q, K and V together): blockIdx.y picks the tensor.
+struct RegroupPtrs {
+  const char* in[kMaxRegroupTensors];
+  char* out[kMaxRegroupTensors];
+};
+
 template <int W, typename I>
 __global__ void __launch_bounds__(kThreads)
-regroup_kernel(const char* __restrict__ in, char* __restrict__ out, RegroupDiv<W, I> dv, I S_local,
-               I P, I chunk_words, I n_words, int direction) {
+regroup_kernel(RegroupPtrs ptrs, RegroupDiv<W, I> dv, I S_local, I P, I chunk_words, I n_words, int direction) {
   using T = typename Word<W>::type;
-  const T* src = reinterpret_cast<const T*>(in);
-  T* dst = reinterpret_cast<T*>(out);
+  const T* src = reinterpret_cast<const T*>(ptrs.in[blockIdx.y]);
+  T* dst = reinterpret_cast<T*>(ptrs.out[blockIdx.y]);
   const I id = (I)blockIdx.x * kThreads + (I)threadIdx.x;
   if (id >= n_words) return;
   const I cid = dv.by_chunk(id);  // (b, s, g), g fastest: the sequence-sharded order
@@ -86,23 +92,22 @@ regroup_kernel(const char* __restrict__ in, char* __restrict__ out, RegroupDiv<W
 }
 
 template <int W>
-hipError_t launch_w(const void* in, void* out, int64_t chunk_bytes, int B, int S_local, int P,
+hipError_t launch_w(const RegroupPtrs& ptrs, int n, int64_t chunk_bytes, int B, int S_local, int P,
                     int direction, hipStream_t stream) {
   const int64_t chunk_words = chunk_bytes / W;
   const int64_t n_words = chunk_words * P * S_local * B;
-  if (n_words == 0) return hipSuccess;
+  if (n_words == 0 || n == 0) return hipSuccess;
   const int64_t g = (n_words + kThreads - 1) / kThreads;
   if (g > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const char* src = static_cast<const char*>(in);
-  char* dst = static_cast<char*>(out);
   if (n_words <= 0x7fffffff) {
     RegroupDiv<W, uint32_t> dv{FastDiv((uint32_t)chunk_words), FastDiv((uint32_t)P), FastDiv((uint32_t)S_local)};
-    hipLaunchKernelGGL((regroup_kernel<W, uint32_t>), dim3((unsigned)g), dim3(kThreads), 0, stream, src, dst,
-                       dv, (uint32_t)S_local, (uint32_t)P, (uint32_t)chunk_words, (uint32_t)n_words, direction);
+    hipLaunchKernelGGL((regroup_kernel<W, uint32_t>), dim3((unsigned)g, (unsigned)n), dim3(kThreads), 0, stream,
+                       ptrs, dv, (uint32_t)S_local, (uint32_t)P, (uint32_t)chunk_words, (uint32_t)n_words,
+                       direction);
   } else {
     RegroupDiv<W, int64_t> dv{chunk_words, (int64_t)P, (int64_t)S_local};
-    hipLaunchKernelGGL((regroup_kernel<W, int64_t>), dim3((unsigned)g), dim3(kThreads), 0, stream, src, dst,
-                       dv, (int64_t)S_local, (int64_t)P, chunk_words, n_words, direction);
+    hipLaunchKernelGGL((regroup_kernel<W, int64_t>), dim3((unsigned)g, (unsigned)n), dim3(kThreads), 0, stream,
+                       ptrs, dv, (int64_t)S_local, (int64_t)P, chunk_words, n_words, direction);
   }
   return hipGetLastError();
 }
@@ -202,15 +207,21 @@ hipError_t launch_pieces(const void* in, void* out, int axis, int64_t B, int64_t
   }
 }
 
-hipError_t launch_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
-                          int D, int degree, int direction, hipStream_t stream) {
+hipError_t launch_regroup(const void* const* in, void* const* out, int n, int elem_bytes, int B, int S_local,
+                          int H, int D, int degree, int direction, hipStream_t stream) {
+  if (n < 1 || n > kMaxRegroupTensors) return hipErrorInvalidValue;
   const int64_t chunk_bytes = (int64_t)(H / degree) * D * elem_bytes;
-  const uintptr_t align = reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out) |
-                          static_cast<uintptr_t>(chunk_bytes);
-  if ((align & 15) == 0) return launch_w<16>(in, out, chunk_bytes, B, S_local, degree, direction, stream);
-  if ((align & 7) == 0) return launch_w<8>(in, out, chunk_bytes, B, S_local, degree, direction, stream);
-  if ((align & 3) == 0) return launch_w<4>(in, out, chunk_bytes, B, S_local, degree, direction, stream);
-  return launch_w<2>(in, out, chunk_bytes, B, S_local, degree, direction, stream);
+  RegroupPtrs ptrs{};
+  uintptr_t align = static_cast<uintptr_t>(chunk_bytes);
+  for (int i = 0; i < n; ++i) {
+    ptrs.in[i] = static_cast<const char*>(in[i]);
+    ptrs.out[i] = static_cast<char*>(out[i]);
+    align |= reinterpret_cast<uintptr_t>(in[i]) | reinterpret_cast<uintptr_t>(out[i]);
+  }
+  if ((align & 15) == 0) return launch_w<16>(ptrs, n, chunk_bytes, B, S_local, degree, direction, stream);
+  if ((align & 7) == 0) return launch_w<8>(ptrs, n, chunk_bytes, B, S_local, degree, direction, stream);
+  if ((align & 3) == 0) return launch_w<4>(ptrs, n, chunk_bytes, B, S_local, degree, direction, stream);
+  return launch_w<2>(ptrs, n, chunk_bytes, B, S_local, degree, direction, stream);
 }
 
 }  // namespace cpattn

@@ -22,11 +22,17 @@
  *     element size must be a multiple of 16 bytes. The K/V sequence stride
  *     must not exceed 2^24 elements.
  *   - The caller allocates and owns every buffer (inputs, outputs and any
- *     workspace). The library keeps no pointer after a call returns and
- *     allocates no device memory.
+ *     workspace). The library keeps no pointer to them after a call returns
+ *     and allocates no device memory. What it does own, created on first use
+ *     and kept until the process ends: per device, one extra stream and two
+ *     events used by the backward (see "Streams" at the backward entry
+ *     points), and one process-wide mutex that serialises the backward's
+ *     enqueueing of work on them. It holds no other state between calls:
+ *     every choice of launch form is made from the call's own arguments.
  *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
- *     work on that stream and never synchronise the host; results are ready
- *     once the stream has reached that point.
+ *     work on that stream and never synchronise the host (the one exception
+ *     is cp_ring_attention_check, which says so); results are ready once the
+ *     stream has reached that point.
  *   - Arguments are validated on the host before anything is enqueued. On
  *     error nothing is launched, a non-zero status is returned and
  *     cp_last_error() describes the problem. CP_ERR_HIP reports a failed
@@ -47,14 +53,15 @@
 extern "C" {
 #endif
 
-#define CP_ATTN_ABI_VERSION 1
+#define CP_ATTN_ABI_VERSION 2
 
 typedef enum cp_status {
   CP_OK = 0,
   CP_ERR_INVALID_ARG = 1, /* bad pointer, size, stride or combination */
   CP_ERR_UNSUPPORTED = 2, /* valid request outside the supported set (dtype, D, alignment) */
   CP_ERR_WORKSPACE = 3,   /* workspace missing or too small */
-  CP_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+  CP_ERR_HIP = 4,         /* the HIP runtime reported an error at launch */
+  CP_ERR_ORDER = 5        /* cp_ring_attention_check: a merge of a one-launch ring ran out of order */
 } cp_status_t;
 
 typedef enum cp_dtype { CP_F32 = 0, CP_BF16 = 1 } cp_dtype_t;
@@ -71,6 +78,14 @@ typedef enum cp_dtype { CP_F32 = 0, CP_BF16 = 1 } cp_dtype_t;
 /* cp_ring_attention flag: every v_blocks[i] is block i's V as written by cp_attn_pack_v
  * (CP_BF16 only). */
 #define CP_RING_PACKED_V 0x8u
+
+/* cp_attn_block_fwd and cp_ring_attention flags: force the bf16 block kernel's workgroup shape
+ * for this call (a property of this implementation, not of the pages): four waves and 128 query
+ * rows per workgroup, or eight waves and 256 rows in two ping-pong groups. Without either the
+ * shape is chosen per launch from the grid size (cp_attn_fwd_waves); head dim 64 always uses
+ * four waves. Results agree to rounding either way. Setting both is CP_ERR_INVALID_ARG. */
+#define CP_FWD_FOUR_WAVES 0x100u
+#define CP_FWD_EIGHT_WAVES 0x200u
 
 /* cp_attn_block_bwd flag: add this block's dQ to dq instead of overwriting it. */
 #define CP_BWD_ACCUMULATE_DQ 0x1u
@@ -143,9 +158,12 @@ cp_status_t cp_lse_merge(float* out_acc, float* lse_acc, const float* out_blk, c
  * cp_ring_attention_workspace_size -- bytes of workspace cp_ring_attention
  * uses for these sizes and flags. With CP_RING_SEPARATE_MERGE: one float32
  * partial output [B, Sq, H, D] and its LSE (required). Otherwise, with
- * CP_RING_PACKED_V and D = 128: one int per 256-row query tile of each (b, h),
- * rounded up to 256 bytes (optional: with it, bf16 rings of 2..16 non-empty
- * blocks run as one launch; without it, as one launch per block). Else 0.
+ * CP_RING_PACKED_V and D = 128: 256 bytes (a count of merge waits that gave
+ * up, see cp_ring_attention_check) plus one int per 256-row query tile of
+ * each (b, h), rounded up to 256 bytes (optional: with it, bf16 rings of
+ * 2..16 non-empty blocks, or one block of two or more key tiles, on grids
+ * the per-block launches would run on four waves run as one launch; without
+ * it, as one launch per block or with the blocks in turn). Else 0.
  */
 size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned flags);
 
@@ -176,16 +194,19 @@ size_t cp_ring_attention_workspace_size(int B, int H, int Sq, int D, unsigned fl
  *   workspace           device buffer of workspace_bytes, 256-byte aligned,
  *                       at least cp_ring_attention_workspace_size(); may be
  *                       NULL unless CP_RING_SEPARATE_MERGE is set.
+ *   flags also takes CP_FWD_FOUR_WAVES or CP_FWD_EIGHT_WAVES.
  * One launch for the whole ring (packed V with a workspace, bf16, D = 128,
- * 2 or 3 non-empty blocks, and a grid the per-block launches would run on the
- * 4-wave kernel; cp_ring_attention_one_launch says whether a call qualifies):
- * the partials of all blocks are computed in parallel, and each query tile's
- * merges still run in block order through the same epilogue arithmetic, so
- * the result is the same, bit for bit, as one launch per block. A single
- * non-empty block of at least 128 keys on such a grid is split at a 64-key
- * tile boundary into two halves run the same way (two partials merged by
- * their LSE: equal to one pass up to rounding). Calls that share a workspace
- * must not overlap.
+ * 2 to 16 non-empty blocks, and a grid the per-block launches would run on
+ * the 4-wave kernel; cp_ring_attention_one_launch says whether a call
+ * qualifies, CP_ONE_LAUNCH_PARALLEL): the partials of all blocks are
+ * computed in parallel, and each query tile's merges still run in block
+ * order through the same epilogue arithmetic (ordered by per-tile flags in
+ * the workspace with agent-scope acquire/release; cp_ring_attention_check
+ * reports a wait that gave up), so the result is the same, bit for bit, as
+ * one launch per block. A single non-empty block of at least 128 keys on such
+ * a grid is split at a 64-key tile boundary into two halves run the same way
+ * (two partials merged by their LSE: equal to one pass up to rounding). Calls
+ * that share a workspace must not overlap.
  * Otherwise, with packed V on the 8-wave shape (cp_attn_fwd_waves), 2 to 16
  * non-empty blocks run as one launch without workspace in which each
  * workgroup takes its query tile through the blocks in order, writing block
@@ -251,11 +272,30 @@ cp_status_t cp_attn_pack_v(const void* v, const int64_t* v_strides, int B, int H
 cp_status_t cp_ulysses_regroup_pack_v(const void* in, int B, int S_local, int H, int D, int degree,
                                       void* packed, size_t packed_bytes, void* stream);
 
-/* 1 if cp_ring_attention, given these sizes and block lengths with packed V
- * (CP_RING_PACKED_V) and a workspace, runs the whole ring as one launch
- * (either form; see cp_ring_attention), else 0. A caller that packs V only for speed can use
- * this and cp_attn_fwd_waves to decide whether to. */
-int cp_ring_attention_one_launch(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree);
+/* How cp_ring_attention, given these sizes, block lengths and flags with packed V
+ * (CP_RING_PACKED_V) and a workspace of cp_ring_attention_workspace_size bytes, runs the ring:
+ * 0 one launch per block, CP_ONE_LAUNCH_IN_TURN one launch with the blocks in turn per
+ * workgroup, CP_ONE_LAUNCH_PARALLEL one launch with the blocks' partials in parallel (the form
+ * whose merges wait on other workgroups; see cp_ring_attention_check). A caller that packs V
+ * only for speed can use this and cp_attn_fwd_waves to decide whether to. */
+#define CP_ONE_LAUNCH_IN_TURN 1
+#define CP_ONE_LAUNCH_PARALLEL 2
+int cp_ring_attention_one_launch(int dtype, int B, int H, int D, int Sq, const int* block_len, int ring_degree,
+                                 unsigned flags);
+
+/*
+ * cp_ring_attention_check -- whether every merge of the last cp_ring_attention call that used
+ * this workspace (packed V, bf16, D = 128) ran in order.
+ *
+ * In the parallel-partials form (CP_ONE_LAUNCH_PARALLEL) a merge waits, with a bounded number
+ * of polls, for the previous block's workgroup to publish its partial. A wait
+ * that gives up is counted in the workspace, and the query tile's out and lse are set to NaN
+ * instead of merged, so a wrong result is never silent. This call waits for `stream` (it
+ * synchronises the host with it), reads the count and returns CP_OK when it is 0, CP_ERR_ORDER
+ * otherwise. Every cp_ring_attention call that is given such a workspace and runs a bf16 kernel
+ * resets the count (the other forms have no waits and leave it 0).
+ */
+cp_status_t cp_ring_attention_check(const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * cp_ulysses_regroup -- the Ulysses all-to-all's local permutation, loopback.
@@ -273,6 +313,21 @@ int cp_ring_attention_one_launch(int dtype, int B, int H, int D, int Sq, const i
  */
 cp_status_t cp_ulysses_regroup(const void* in, void* out, int elem_bytes, int B, int S_local, int H,
                                int D, int degree, int direction, void* stream);
+
+/*
+ * cp_ulysses_regroup_multi -- cp_ulysses_regroup of n_tensors tensors of the
+ * same shape in one launch.
+ *
+ * [CP] "Atencao Ulysses": the first all-to-all moves the query, key and value
+ * projections together, so a rank regroups three tensors of one shape at a
+ * time; one launch pays the start-up and drain of a bandwidth-bound pass once
+ * instead of per tensor. in and out are host arrays of n_tensors (1..8)
+ * device pointers; tensor i is regrouped from in[i] into out[i] exactly as
+ * cp_ulysses_regroup would (same arguments and layouts). No output may
+ * overlap any input or another output; inputs may coincide.
+ */
+cp_status_t cp_ulysses_regroup_multi(const void* const* in, void* const* out, int n_tensors, int elem_bytes, int B,
+                                     int S_local, int H, int D, int degree, int direction, void* stream);
 
 /*
  * Ulysses Anything: the packs around an all-to-all whose splits are uneven.
@@ -413,21 +468,12 @@ cp_status_t cp_ring_attention_bwd(const void* q, const int64_t* q_strides, const
                                   const int64_t* dkv_strides, void* workspace, size_t workspace_bytes,
                                   void* stream);
 
-/* Workgroup shape of the bfloat16 block kernel, a process-wide tuning knob
- * (no source passage; a property of this implementation). 0 = chosen per
- * launch from the grid size (the default), 4 = four waves and 128 query rows
- * per workgroup, 8 = eight waves and 256 rows in two ping-pong groups. Head
- * dim 64 always uses 4. Results agree to rounding either way. Returns the
- * previous setting; any other value is rejected with -1 and the setting is
- * left unchanged. Launches already enqueued are not affected. */
-int cp_attn_set_fwd_waves(int waves);
-
-/* The workgroup shape (4 or 8, as above) the bfloat16 block kernel will use
- * for these sizes under the current setting; 0 if B, H or Sq is not positive
- * or D is not 64 or 128. V packed by cp_attn_pack_v speeds up the 8-wave
- * shape only (the 4-wave kernel reads V at the same speed either way), so a
- * caller that has to pack V itself can skip it when this returns 4. */
-int cp_attn_fwd_waves(int B, int H, int D, int Sq);
+/* The workgroup shape (4 or 8 waves, see CP_FWD_FOUR_WAVES) the bfloat16 block kernel will use
+ * for these sizes and flags (only the two shape flags matter); 0 if B, H or Sq is not positive,
+ * D is not 64 or 128, or both shape flags are set. V packed by cp_attn_pack_v speeds up the
+ * 8-wave shape only (the 4-wave kernel reads V at the same speed either way), so a caller that
+ * has to pack V itself can skip it when this returns 4. */
+int cp_attn_fwd_waves(int B, int H, int D, int Sq, unsigned flags);
 
 /* Message for the last non-CP_OK status returned on the calling thread ("" if none). */
 const char* cp_last_error(void);

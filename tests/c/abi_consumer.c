@@ -33,8 +33,9 @@ int main(void) {
   CHECK(cp_attn_packed_v_bytes(1, 24, 128, 2304) == (size_t)24 * 36 * 64 * 128 * 2);
   CHECK(cp_attn_packed_v_bytes(1, 24, 80, 2304) == 0);
   CHECK(cp_attn_bwd_workspace_size(1, 2, 8, 128) > 0);
-  CHECK(cp_attn_fwd_waves(1, 24, 128, 2304) == 8);
-  CHECK(cp_attn_fwd_waves(1, 24, 64, 2304) == 4);
+  CHECK(cp_attn_fwd_waves(1, 24, 128, 2304, 0) == 8);
+  CHECK(cp_attn_fwd_waves(1, 24, 64, 2304, 0) == 4);
+  CHECK(cp_attn_fwd_waves(1, 24, 128, 2304, CP_FWD_FOUR_WAVES) == 4);
 
   /* block attention: unsupported head dim, bad scale, unknown flag, packed f32 */
   const int64_t* contiguous = NULL;

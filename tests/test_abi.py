@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
             "cp_ulysses_concat_seq"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.cp_abi_version() == 1
+    assert lib.cp_abi_version() == _lib.ABI_VERSION
 
 
 def _block(lib, dtype=1, B=1, H=2, D=128, Sq=8, Skv=8, scale=0.1, flags=0, q=FAKE, k=FAKE, v=FAKE,
@@ -98,7 +98,7 @@ def test_ring_rejects_uneven_without_ring_anything(lib):
 def test_ring_rejects_degree_flags_and_null_blocks(lib):
     assert _ring(lib, []) == _lib.CP_ERR_INVALID_ARG
     assert "ring_degree" in _err(lib)
-    assert _ring(lib, [8, 8], flags=0x100) == _lib.CP_ERR_INVALID_ARG
+    assert _ring(lib, [8, 8], flags=0x1000) == _lib.CP_ERR_INVALID_ARG
     assert _ring(lib, [8, 8], kptrs=[FAKE, 0]) == _lib.CP_ERR_INVALID_ARG
     assert "block 1" in _err(lib)
 
@@ -134,6 +134,28 @@ def test_regroup_rejects(lib):
     assert f(FAKE, FAKE + 64, 2, 1, 16, 24, 128, 2, 0, None) == _lib.CP_ERR_INVALID_ARG  # overlap
     assert "overlap" in _err(lib)
     assert f(0, 0, 2, 0, 16, 24, 128, 2, 0, None) == _lib.CP_OK
+
+
+def test_regroup_multi_rejects(lib):
+    import ctypes
+    f = lib.cp_ulysses_regroup_multi
+    V = ctypes.c_void_p * 3
+    ins, outs = V(FAKE, FAKE + (1 << 28), FAKE + (2 << 28)), V(FAKE + (3 << 28), FAKE + (4 << 28), FAKE + (5 << 28))
+    assert f(ins, outs, 0, 2, 1, 16, 24, 128, 2, 0, None) == _lib.CP_ERR_INVALID_ARG
+    assert "n_tensors" in _err(lib)
+    assert f(ins, outs, 9, 2, 1, 16, 24, 128, 2, 0, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(None, outs, 3, 2, 1, 16, 24, 128, 2, 0, None) == _lib.CP_ERR_INVALID_ARG
+    assert f(ins, outs, 3, 2, 1, 16, 24, 128, 5, 0, None) == _lib.CP_ERR_INVALID_ARG
+    assert "divisible" in _err(lib)
+    # an output overlapping another tensor's input, or two outputs overlapping, is refused
+    assert f(ins, V(FAKE + (3 << 28), FAKE + 64, FAKE + (5 << 28)), 3, 2, 1, 16, 24, 128, 2, 0,
+             None) == _lib.CP_ERR_INVALID_ARG
+    assert "overlap" in _err(lib)
+    assert f(ins, V(FAKE + (3 << 28), FAKE + (3 << 28) + 64, FAKE + (5 << 28)), 3, 2, 1, 16, 24, 128, 2, 0,
+             None) == _lib.CP_ERR_INVALID_ARG
+    assert "overlap" in _err(lib)
+    # shared inputs are fine; an empty problem enqueues nothing
+    assert f(V(0, 0, 0), V(0, 0, 0), 3, 2, 0, 16, 24, 128, 2, 0, None) == _lib.CP_OK
 
 
 BWD_NEED = 4096 + 256  # bf16 dO [1, 8, 2, 128] and D [1, 2, 8] float32, each padded to 256 bytes
@@ -237,16 +259,22 @@ def test_split_counts():
     assert cp.split_counts(2, 3) == [1, 1, 0]
 
 
-def test_set_fwd_waves(lib):
-    """The bf16 workgroup-shape knob accepts 0, 4 and 8 only and returns the previous value."""
-    prev = lib.cp_attn_set_fwd_waves(4)
-    try:
-        assert prev in (0, 4, 8)
-        assert lib.cp_attn_set_fwd_waves(8) == 4
-        assert lib.cp_attn_set_fwd_waves(5) == -1
-        assert lib.cp_attn_set_fwd_waves(0) == 8
-    finally:
-        lib.cp_attn_set_fwd_waves(prev)
+def test_shape_flags(lib):
+    """The bf16 workgroup shape is forced per call by a flag; both flags together are refused, and
+    the library exports no process-wide setting for it."""
+    four, eight = _lib.CP_FWD_FOUR_WAVES, _lib.CP_FWD_EIGHT_WAVES
+    assert not hasattr(lib, "cp_attn_set_fwd_waves")
+    assert _block(lib, flags=four | eight) == _lib.CP_ERR_INVALID_ARG
+    assert "together" in _err(lib)
+    assert _ring(lib, [8, 8], flags=four | eight) == _lib.CP_ERR_INVALID_ARG
+    # each flag alone passes validation (the call then fails later on the fake pointers' contents
+    # only on a GPU; here a zero-sized problem stops it first)
+    assert _block(lib, flags=four, B=0) == _lib.CP_OK
+    assert _block(lib, flags=eight, B=0) == _lib.CP_OK
+    import context_attention_dits_amd as cp
+    assert cp.wave_flags(0) == 0 and cp.wave_flags(4) == four and cp.wave_flags(8) == eight
+    with pytest.raises(ValueError):
+        cp.wave_flags(5)
 
 
 def test_binding_refuses_host_tensors():
@@ -306,8 +334,8 @@ def test_regroup_pack_v_rejects(lib):
 
 def test_fwd_waves_query(lib):
     """The bf16 kernel's workgroup shape for the benchmark shapes, and its knob."""
-    q = lib.cp_attn_fwd_waves
-    assert lib.cp_attn_set_fwd_waves(0) in (0, 4, 8)
+    def q(B, H, D, Sq, flags=0):
+        return lib.cp_attn_fwd_waves(B, H, D, Sq, flags)
     assert q(1, 24, 128, 2304) == 8   # 216 ping-pong workgroups: one round, mostly full
     assert q(1, 12, 128, 4608) == 8
     assert q(1, 24, 128, 8192) == 8
@@ -315,11 +343,10 @@ def test_fwd_waves_query(lib):
     assert q(1, 12, 128, 2304) == 4   # 108: under half a round
     assert q(1, 24, 64, 8192) == 4    # D = 64 has the 4-wave kernel only
     assert q(0, 24, 128, 2304) == 0 and q(1, 24, 96, 2304) == 0
-    prev = lib.cp_attn_set_fwd_waves(8)
-    try:
-        assert q(1, 12, 128, 2304) == 8 and q(1, 24, 64, 8192) == 4
-    finally:
-        lib.cp_attn_set_fwd_waves(prev)
+    eight, four = _lib.CP_FWD_EIGHT_WAVES, _lib.CP_FWD_FOUR_WAVES
+    assert q(1, 12, 128, 2304, eight) == 8 and q(1, 24, 64, 8192, eight) == 4
+    assert q(1, 24, 128, 2304, four) == 4
+    assert q(1, 24, 128, 2304, four | eight) == 0
 
 
 def test_plain_c_consumer(tmp_path):
@@ -344,47 +371,50 @@ def test_plain_c_consumer(tmp_path):
 
 
 def test_ring_one_launch_workspace_rules(lib):
-    """With packed V (bf16, D = 128) the ring can run as one launch, whose per-query-tile flags
-    live in the workspace: one int per 256-row tile of each (b, h), in 256-byte units. Without
-    a workspace the ring still runs, one launch per block; a workspace that is too small or
-    misaligned is rejected."""
+    """With packed V (bf16, D = 128) the ring can run as one launch, whose error count and
+    per-query-tile flags live in the workspace: 256 bytes, then one int per 256-row tile of each
+    (b, h), in 256-byte units. Without a workspace the ring still runs, one launch per block; a
+    workspace that is too small or misaligned is rejected, and so is one too small or misaligned
+    for cp_ring_attention_check."""
     pk = _lib.CP_RING_PACKED_V
-    assert lib.cp_ring_attention_workspace_size(1, 24, 2304, 128, pk) == 1024   # 9 * 24 ints -> 256-byte units
-    assert lib.cp_ring_attention_workspace_size(2, 24, 1536, 128, pk | _lib.CP_RING_ANYTHING) == 1280
+    assert lib.cp_ring_attention_workspace_size(1, 24, 2304, 128, pk) == 256 + 1024  # 9 * 24 ints
+    assert lib.cp_ring_attention_workspace_size(2, 24, 1536, 128, pk | _lib.CP_RING_ANYTHING) == 256 + 1280
     assert lib.cp_ring_attention_workspace_size(1, 24, 2304, 64, pk) == 0
     assert lib.cp_ring_attention_workspace_size(1, 24, 2304, 128, 0) == 0
     need = lib.cp_ring_attention_workspace_size(1, 2, 8, 128, pk)
-    assert need == 256
+    assert need == 512
+    assert lib.cp_ring_attention_check(None, need, None) == _lib.CP_ERR_WORKSPACE
+    assert lib.cp_ring_attention_check(FAKE, 64, None) == _lib.CP_ERR_WORKSPACE
+    assert lib.cp_ring_attention_check(FAKE + 16, need, None) == _lib.CP_ERR_UNSUPPORTED
     assert _ring(lib, [8, 8], flags=pk, ws=FAKE, ws_bytes=need - 4) == _lib.CP_ERR_WORKSPACE
     assert _ring(lib, [8, 8], flags=pk, ws=FAKE + 16, ws_bytes=need) == _lib.CP_ERR_UNSUPPORTED
 
 
 def test_ring_one_launch_query(lib):
-    """Which packed rings run as one launch (bf16, D = 128): 2 or 3 non-empty blocks in parallel
+    """Which packed rings run as one launch (bf16, D = 128): 2 to 16 non-empty blocks in parallel
     on grids the per-block launches would run on the 4-wave kernel (one block: split in two), and
     2 to 16 non-empty blocks in turn per workgroup on the 8-wave shape."""
-    def q(dtype, B, H, D, Sq, lens):
+    par, turn = _lib.CP_ONE_LAUNCH_PARALLEL, _lib.CP_ONE_LAUNCH_IN_TURN
+
+    def q(dtype, B, H, D, Sq, lens, flags=0):
         arr = (ctypes.c_int * len(lens))(*lens)
-        return lib.cp_ring_attention_one_launch(dtype, B, H, D, Sq, arr, len(lens))
-    prev = lib.cp_attn_set_fwd_waves(0)
-    try:
-        assert q(1, 2, 24, 128, 1536, [1536, 1536, 1535]) == 1   # ring-anything share
-        assert q(1, 1, 12, 128, 2304, [2304, 2304]) == 1         # USP share
-        assert q(1, 1, 24, 128, 2304, [2304, 2304]) == 1         # FLUX ring-2: 8-wave, blocks in turn
-        assert q(1, 1, 24, 128, 2304, [2304] * 4) == 1           # 8-wave: up to 16 blocks in turn
-        assert q(1, 1, 24, 128, 2304, [2304] * 16 + [0]) == 1
-        assert q(1, 1, 24, 128, 2304, [2304] * 17) == 0          # more: one launch per block
-        assert q(1, 2, 24, 128, 1536, [1536, 0, 1535]) == 1      # empty blocks do not count
-        assert q(1, 2, 24, 128, 1536, [1536] * 4) == 0           # 4-wave grid: more than 3 blocks
-        assert q(1, 2, 24, 128, 1536, [1536, 0, 0]) == 1         # one block: split in two halves
-        assert q(1, 1, 6, 128, 4481, [4481]) == 1                # the Ulysses Anything share, split
-        assert q(1, 1, 12, 128, 4608, [4608]) == 0               # Ulysses-2: 8-wave per block
-        assert q(1, 1, 6, 128, 4481, [127]) == 0                 # under two tiles: not split
-        assert q(0, 2, 24, 128, 1536, [1536, 1536]) == 0         # float32
-        assert q(1, 2, 24, 64, 1536, [1536, 1536]) == 0          # D = 64
-        lib.cp_attn_set_fwd_waves(8)
-        assert q(1, 1, 24, 128, 2304, [2304, 2304]) == 1
-        lib.cp_attn_set_fwd_waves(4)
-        assert q(1, 1, 12, 128, 2304, [2304, 2304]) == 0
-    finally:
-        lib.cp_attn_set_fwd_waves(prev)
+        return lib.cp_ring_attention_one_launch(dtype, B, H, D, Sq, arr, len(lens), flags)
+    assert q(1, 2, 24, 128, 1536, [1536, 1536, 1535]) == par   # ring-anything share
+    assert q(1, 1, 12, 128, 2304, [2304, 2304]) == par         # USP share
+    assert q(1, 1, 24, 128, 2304, [2304, 2304]) == turn        # FLUX ring-2: 8-wave, blocks in turn
+    assert q(1, 1, 24, 128, 2304, [2304] * 4) == turn          # 8-wave: up to 16 blocks in turn
+    assert q(1, 1, 24, 128, 2304, [2304] * 16 + [0]) == turn
+    assert q(1, 1, 24, 128, 2304, [2304] * 17) == 0            # more: one launch per block
+    assert q(1, 2, 24, 128, 1536, [1536, 0, 1535]) == par      # empty blocks do not count
+    assert q(1, 2, 24, 128, 1536, [1536] * 4) == par           # 4-wave grid: up to 16 blocks in parallel
+    assert q(1, 2, 24, 128, 1536, [1536] * 17) == 0
+    assert q(1, 2, 24, 128, 1536, [1536, 0, 0]) == par         # one block: two halves in parallel
+    assert q(1, 1, 6, 128, 4481, [4481]) == par                # the Ulysses Anything share, split in two
+    assert q(1, 1, 12, 128, 4608, [4608]) == 0                 # Ulysses-2: 8-wave per block
+    assert q(1, 1, 12, 128, 4608, [4608], _lib.CP_FWD_FOUR_WAVES) == 0
+    assert q(1, 1, 6, 128, 4481, [127]) == 0                   # under two tiles: not split
+    assert q(0, 2, 24, 128, 1536, [1536, 1536]) == 0           # float32
+    assert q(1, 2, 24, 64, 1536, [1536, 1536]) == 0            # D = 64
+    assert q(1, 1, 24, 128, 2304, [2304, 2304], _lib.CP_FWD_EIGHT_WAVES) == par
+    assert q(1, 1, 12, 128, 2304, [2304, 2304], _lib.CP_FWD_FOUR_WAVES) == 0
+    assert q(1, 1, 12, 128, 2304, [2304, 2304], _lib.CP_RING_SEPARATE_MERGE) == 0

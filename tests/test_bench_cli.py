@@ -25,10 +25,20 @@ def test_cpu_baseline_fields():
     w = workloads.by_name("tiny_ring4_f32")
     inp = workloads.make_inputs(w)
     rec = bench.cpu_baseline(w, inp, target_s=0.2)
-    assert set(rec) == {"value", "unit", "cores", "kind", "sample"}
+    assert set(rec) == {"value", "unit", "cores", "kind", "sample", "cpu_model"}
     assert rec["unit"] == "TFLOP/s" and rec["kind"] == "oracle"
+    assert isinstance(rec["cpu_model"], str) and rec["cpu_model"]
     assert rec["value"] > 0 and rec["cores"] >= 1
     assert "passes" in rec["sample"] or "heads" in rec["sample"]
+
+
+def test_default_workload_is_the_ulysses2_share():
+    """The headline line is the Ulysses-2 share (the workload the >=50%-of-peak target names), with the
+    32k ring-4 share's block kernel timed beside it."""
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.DEFAULT_WORKLOAD == "flux1024_ulysses2_bf16"
+    assert "video32k_ring4_bf16" in bench.EXTRA_ROOFLINES
 
 
 @pytest.mark.parametrize("name", ["flux1024_ring2_bf16", "video32k_ring4_bf16"])

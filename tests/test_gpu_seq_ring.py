@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_util import TOL, assert_close, dev, fwd_waves, say
+from tests.gpu_util import TOL, assert_close, dev, full_ref, say
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ def cp():
     return m
 
 
-def _per_block(cp, q, kb, vp, scale):
+def _per_block(cp, q, kb, vp, scale, waves=0):
     B, Sq, H, D = q.shape
     out = torch.empty((B, Sq, H, D), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
@@ -41,7 +41,8 @@ def _per_block(cp, q, kb, vp, scale):
     for k, v in zip(kb, vp):
         if k.shape[1] == 0:
             continue
-        cp.cp_attn_block_fwd(q, k, v, out, lse, scale=scale, flags=0 if first else cp.CP_BLOCK_ACCUMULATE)
+        cp.cp_attn_block_fwd(q, k, v, out, lse, scale=scale, flags=0 if first else cp.CP_BLOCK_ACCUMULATE,
+                             waves=waves)
         first = False
     return out, lse
 
@@ -68,13 +69,14 @@ def test_seq_ring_equals_per_block(cp, B, H, D, Sq, lens):
     vp = [cp.pack_v(v[:, o:o + L].contiguous()) for o, L in zip(offs, lens)]
     anything = len(set(lens)) > 1 or 0 in lens
     flags = cp.CP_RING_ANYTHING if anything else 0
-    with fwd_waves(cp, 8):
-        one = cp.cp_ring_attention_one_launch(cp.CP_BF16, B, H, D, Sq, lens)
-        assert one == (2 <= sum(1 for L in lens if L) <= 16), one
-        out = torch.empty((B, Sq, H, D), dtype=torch.float32, device="cuda")
-        lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
-        cp.cp_ring_attention(q, kb, vp, out, lse, scale=scale, flags=flags)  # no workspace
-        out_b, lse_b = _per_block(cp, q, kb, vp, scale)
+    # with a workspace these rings would run their partials in parallel (8 waves forced); without
+    # one, as here, the blocks run in turn
+    one = cp.cp_ring_attention_one_launch(cp.CP_BF16, B, H, D, Sq, lens, waves=8)
+    assert one == (cp.CP_ONE_LAUNCH_PARALLEL if 2 <= sum(1 for L in lens if L) <= 16 else 0), one
+    out = torch.empty((B, Sq, H, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
+    cp.cp_ring_attention(q, kb, vp, out, lse, scale=scale, flags=flags, waves=8)  # no workspace
+    out_b, lse_b = _per_block(cp, q, kb, vp, scale, waves=8)
     torch.cuda.synchronize()
     assert torch.equal(out, out_b) and torch.equal(lse, lse_b), \
         (float((out - out_b).abs().max()), float((lse - lse_b).abs().max()))
@@ -86,7 +88,7 @@ def test_seq_ring_equals_per_block(cp, B, H, D, Sq, lens):
 
 def test_seq_ring_flux_ring2_share(cp):
     """The FLUX 1024px ring-2 share (216 workgroups) takes this path on the library's own shape
-    choice; bit-equal to the per-block launches, and sampled rows against the oracle."""
+    choice; bit-equal to the per-block launches, and every element against the oracle."""
     w = workloads.by_name("flux1024_ring2_bf16")
     say("seq ring flux ring-2 share")
     inp = workloads.make_inputs(w)
@@ -95,16 +97,15 @@ def test_seq_ring_flux_ring2_share(cp):
     kb = [k[:, o:o + L] for o, L in zip(offs, w.block_lens)]
     vp = [cp.pack_v(v[:, o:o + L].contiguous()) for o, L in zip(offs, w.block_lens)]
     assert cp.cp_attn_fwd_waves(w.B, w.H, w.D, w.Sq) == 8
-    assert cp.cp_ring_attention_one_launch(cp.CP_BF16, w.B, w.H, w.D, w.Sq, w.block_lens)
+    assert cp.cp_ring_attention_one_launch(cp.CP_BF16, w.B, w.H, w.D, w.Sq, w.block_lens) == \
+        cp.CP_ONE_LAUNCH_IN_TURN
     out, lse = cp.ring_attention(q, kb, vp, scale=w.scale)
     out_b, lse_b = _per_block(cp, q, kb, vp, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(out, out_b) and torch.equal(lse, lse_b)
-    rows = np.random.default_rng(3).choice(w.Sq, 24, replace=False)
-    rows = np.concatenate([rows, [0, w.Sq - 1]])
-    o_ref, l_ref = oracle.attention(inp.q[:, rows], inp.k, inp.v, w.scale)
-    assert_close("out rows", out.cpu().numpy()[:, rows], o_ref, TOL["bf16"]["o"])
-    assert_close("lse rows", lse.cpu().numpy()[:, :, rows], l_ref, TOL["bf16"]["lse"])
+    o_ref, l_ref = full_ref(w.name, inp.q, inp.k, inp.v, w.scale)
+    assert_close("out", out.cpu().numpy(), o_ref, TOL["bf16"]["o"])
+    assert_close("lse", lse.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
 
 
 def test_seq_ring_strided_views(cp):
@@ -130,12 +131,37 @@ def test_seq_ring_strided_views(cp):
     obig = torch.full((B, Sq, H + 1, D), float("nan"), dtype=torch.float32, device="cuda")
     out_view = obig[:, :, :H]
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
-    with fwd_waves(cp, 8):
-        cp.cp_ring_attention(q_view, kb_pad, vp, out_view, lse, scale=scale, flags=cp.CP_RING_ANYTHING)
-        out_c = torch.empty((B, Sq, H, D), dtype=torch.float32, device="cuda")
-        lse_c = torch.empty_like(lse)
-        cp.cp_ring_attention(q, kb, vp, out_c, lse_c, scale=scale, flags=cp.CP_RING_ANYTHING)
+    cp.cp_ring_attention(q_view, kb_pad, vp, out_view, lse, scale=scale, flags=cp.CP_RING_ANYTHING, waves=8)
+    out_c = torch.empty((B, Sq, H, D), dtype=torch.float32, device="cuda")
+    lse_c = torch.empty_like(lse)
+    cp.cp_ring_attention(q, kb, vp, out_c, lse_c, scale=scale, flags=cp.CP_RING_ANYTHING, waves=8)
     torch.cuda.synchronize()
     assert torch.isnan(obig[:, :, H]).all().item(), "wrote outside the output view"
     assert torch.equal(out_view, out_c) and torch.equal(lse, lse_c)
     assert not torch.isnan(out_c).any().item()
+
+
+@pytest.mark.parametrize("lens", [(128, 128), (129, 128), (128, 129, 128), (128, 64, 129, 1)])
+def test_seq_ring_two_tile_blocks_many_seeds(cp, lens):
+    """Blocks of two 64-key tiles (128 keys) and of two tiles and one key (129), where the
+    pipeline's prologue of one block meets the tail steps of the previous one: 8 heads, six
+    seeds, every element against the oracle and bit-equal to one launch per block."""
+    B, H, D, Sq = 1, 8, 128, 300
+    scale = 1.0 / np.sqrt(D)
+    for seed in range(6):
+        say("seq ring two-tile blocks", lens, "seed", seed)
+        inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=6100 + 37 * seed + sum(lens))
+        q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+        offs = workloads.block_offsets(lens)
+        kb = [k[:, o:o + L] for o, L in zip(offs, lens)]
+        vp = [cp.pack_v(v[:, o:o + L].contiguous()) for o, L in zip(offs, lens)]
+        flags = cp.CP_RING_ANYTHING if len(set(lens)) > 1 else 0
+        out = torch.empty((B, Sq, H, D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
+        cp.cp_ring_attention(q, kb, vp, out, lse, scale=scale, flags=flags, waves=8)
+        out_b, lse_b = _per_block(cp, q, kb, vp, scale, waves=8)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_b) and torch.equal(lse, lse_b), (seed, lens)
+        o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, scale)
+        assert_close("out", out.cpu().numpy(), o_ref, TOL["bf16"]["o"])
+        assert_close("lse", lse.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
