@@ -53,6 +53,9 @@ _SIGNATURES = {
     "cp_attn_fwd_waves": (_i, [_i, _i, _i, _i, ctypes.c_uint]),
     "cp_ring_attention_one_launch": (_i, [_i, _i, _i, _i, _i, ctypes.POINTER(_i), _i, ctypes.c_uint]),
     "cp_ring_attention_check": (_i, [_vp, ctypes.c_size_t, _vp]),
+    "cp_ring_attention_noalloc": (_i, [_vp, _i64p, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64p,
+                                       ctypes.POINTER(_i), _i, _i, _i, _i, _i, _i, ctypes.c_float, ctypes.c_uint,
+                                       _vp, _i64p, _vp, _vp]),
     "cp_attn_block_fwd": (_i, [_vp, _i64p, _vp, _vp, _i64p, _i, _i, _i, _i, _i, _i, ctypes.c_float,
                                ctypes.c_uint, _vp, _i64p, _vp, _vp]),
     "cp_lse_merge": (_i, [_vp, _vp, _vp, _vp, _i64p, _i64p, _i, _i, _i, _i, _vp]),

@@ -1007,3 +1007,63 @@ cp_status_t cp_ulysses_concat_seq(const void* in, void* out, int elem_bytes, int
 
 }  // extern "C"
 
+// ---- cp_ring_attention_noalloc: the ring with a library-owned static workspace
+namespace {
+
+// Device memory the no-allocation ring uses in place of a caller's workspace: the
+// parallel-partials form's error count and per-tile flags. One copy per GPU, for the life of
+// the process; every call on a GPU shares it.
+constexpr size_t kScratchBytes = 64 * 1024;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device (with that device
+// current). In host code the array's own name is not a device address.
+cp_status_t scratch_address(const char* fn, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(CP_ERR_UNSUPPORTED, "%s: device %d is beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return CP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status_t cp_ring_attention_noalloc(const void* q, const int64_t* q_strides, const void* const* k_blocks,
+                                      const void* const* v_blocks, const int64_t* kv_strides, const int* block_len,
+                                      int ring_degree, int dtype, int B, int H, int D, int Sq, float scale,
+                                      unsigned flags, float* out, const int64_t* out_strides, float* lse,
+                                      void* stream) {
+  const char* fn = "cp_ring_attention_noalloc";
+  if (flags & CP_RING_SEPARATE_MERGE)
+    return fail(CP_ERR_INVALID_ARG, "%s: CP_RING_SEPARATE_MERGE needs a caller workspace (use cp_ring_attention)", fn);
+  const size_t need = cp_ring_attention_workspace_size(B, H, Sq, D, flags);
+  if (need > kScratchBytes)
+    return fail(CP_ERR_WORKSPACE,
+                "%s: these sizes need %zu bytes of workspace, more than the %zu-byte static scratch "
+                "(B*H*ceil(Sq/256) must stay at most %zu); use cp_ring_attention with a workspace",
+                fn, need, kScratchBytes, (kScratchBytes - 256) / sizeof(int));
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (need > 0) {
+    cp_status_t st = scratch_address(fn, &ws);
+    if (st != CP_OK) return st;
+    ws_bytes = kScratchBytes;
+  }
+  return cp_ring_attention(q, q_strides, k_blocks, v_blocks, kv_strides, block_len, ring_degree, dtype, B, H, D,
+                           Sq, scale, flags, out, out_strides, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

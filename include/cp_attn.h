@@ -475,6 +475,26 @@ cp_status_t cp_ring_attention_bwd(const void* q, const int64_t* q_strides, const
  * has to pack V itself can skip it when this returns 4. */
 int cp_attn_fwd_waves(int B, int H, int D, int Sq, unsigned flags);
 
+/*
+ * cp_ring_attention_noalloc -- cp_ring_attention without a workspace argument and without
+ * allocating anything, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, layouts and results as cp_ring_attention, except that the workspace of the
+ * parallel-partials form (256 bytes plus one int per 256-row query tile of each (b, h)) lives
+ * in a static device array of 64 KB that the library holds on every GPU it runs on until the
+ * process ends: packed-V calls with B * H * ceil(Sq / 256) above 16320 are CP_ERR_WORKSPACE, and
+ * CP_RING_SEPARATE_MERGE (whose partial buffer is as large as out) is CP_ERR_INVALID_ARG. The call allocates and frees nothing; its first call on a device looks up
+ * that device's copy of the array. Every call on one GPU shares that array and each parallel-
+ * partials launch resets it first, so calls that overlap in time on one GPU (on different
+ * streams) race and must not be issued; calls in one stream are fine.
+ */
+cp_status_t cp_ring_attention_noalloc(const void* q, const int64_t* q_strides, const void* const* k_blocks,
+                                      const void* const* v_blocks, const int64_t* kv_strides, const int* block_len,
+                                      int ring_degree, int dtype, int B, int H, int D, int Sq, float scale,
+                                      unsigned flags, float* out, const int64_t* out_strides, float* lse,
+                                      void* stream);
+
 /* Message for the last non-CP_OK status returned on the calling thread ("" if none). */
 const char* cp_last_error(void);
 
