@@ -458,12 +458,16 @@ seq_next_block:
     bool rescale = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = s_cur[qb][0][0];
+      // two independent chains of maxima (half the dependent latency)
+      float mx0 = s_cur[qb][0][0], mx1 = s_cur[qb][0][1];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[qb][kb][r]);
-      const float mt = half_max(mx) * csc;
+        for (int r = 0; r < 16; r += 2) {
+          mx0 = fmaxf(mx0, s_cur[qb][kb][r]);
+          mx1 = fmaxf(mx1, s_cur[qb][kb][r + 1]);
+        }
+      const float mt = half_max(fmaxf(mx0, mx1)) * csc;
       const bool need = __builtin_amdgcn_ballot_w64(mt > m_run[qb] + CP_FWD_LAZY) != 0;
       const float m_new = need ? fmaxf(m_run[qb], mt) : m_run[qb];
       alpha[qb] = fast_exp2(m_run[qb] - m_new);  // 1 when the maximum is kept
@@ -483,7 +487,9 @@ seq_next_block:
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float mneg = -m_run[qb];
-      float ls = 0.f;
+      // float32 sums of the unrounded probabilities (LSE needs them), in four
+      // independent partial sums so that the adds do not form one dependent chain
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -493,12 +499,12 @@ seq_next_block:
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
             const float e = fast_exp2(fmaf(s_cur[qb][kb][kk2 * 8 + jj], csc, mneg));
-            ls += e;  // float32 sum of the unrounded probabilities: LSE needs it
+            ls[jj & 3] += e;
             t[jj] = (__bf16)e;
           }
           pf[qb][kb][kk2] = t;
         }
-      l_run[qb] += ls;
+      l_run[qb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
     if constexpr (!decltype(fuse_tag)::value) {
       // Split form: pin the probabilities and row sums here, so the compiler
