@@ -906,54 +906,96 @@ seq_next_block:
     }
   };
   auto l_store = [&](float* ptr, float v) { *ptr = v; };
+  // In the accumulator layout a lane holds one row and 16 of the 32 columns
+  // of each 32-column block, so its stores cover a 128-byte line of out in
+  // 32-byte pieces. STAGE (the parallel-partials ring): the values (merged,
+  // where merging, in that layout) go through a per-wave LDS area instead,
+  // from which lane L takes row L/8 (+8, +16, +24) and columns 4(L%8)..+3 of
+  // the block, so that eight lanes store one whole line. Chunk c of staged
+  // row r sits at c ^ (r % 8), spreading the banks. SR rows are staged per
+  // pass, as the LDS left by the tile stages allows. The area is the wave's
+  // own, and a wave's LDS accesses complete in order: no barrier. There the
+  // merges' pieces reached memory separately (more bytes written than out
+  // holds) and whole lines run faster; the one-block launches run slightly
+  // slower staged, and in the blocks-in-turn form the staging inside the
+  // block loop makes the compiler schedule the tile loop for fewer registers
+  // (its LDS reads no longer run ahead). Same values either way.
+  constexpr bool STAGE = RING;
+  constexpr int SR = (C::PINGPONG && PACKED) ? 32 : 16;
+  __shared__ __attribute__((aligned(1024))) char ostage[STAGE ? NW * SR * 128 : 16];
+  f32x4* const stg = reinterpret_cast<f32x4*>(ostage) + (STAGE ? wave * SR * 8 : 0);
+  const int sr = lane >> 3, sc = lane & 7;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qrow0 + qb * 32 + l32;
     const float lt = half_sum(l_run[qb]);
     const float lse2 = m_run[qb] + fast_log2(lt);  // log2 units
-    const float inv = 1.0f / lt;
+    // this lane's row: out = fa * out_old + fb * o, with no old part when fa < 0
+    float fa = -1.f, fb = 1.0f / lt, lse_out = lse2 * kLn2;
+    float* const lrow = p.lse + ((int64_t)b * p.H + h) * p.Sq + row;
+    float* const orow = p.out + b * p.o_sb + (int64_t)row * p.o_ss + h * p.o_sh + 4 * hi;
+    if (RING && gave_up) {
+      // the previous block's partial for this tile was not seen: no merge
+      fb = NAN;
+      lse_out = NAN;
+    } else if (acc && row < p.Sq) {
+      const float la2 = (SEQ ? lse_keep[qb] : l_load(lrow)) * kLog2e;
+      const float M = fmaxf(la2, lse2);
+      const float wa = fast_exp2(la2 - M);  // 0 when the accumulator is empty (-inf)
+      const float wb = fast_exp2(lse2 - M);
+      const float tot = wa + wb;
+      if (wa > 0.f) fa = wa / tot;
+      fb *= wb / tot;
+      lse_out = (M + fast_log2(tot)) * kLn2;
+    }
     if (row < p.Sq) {
-      float* orow = p.out + b * p.o_sb + (int64_t)row * p.o_ss + h * p.o_sh;
-      float* lrow = p.lse + ((int64_t)b * p.H + h) * p.Sq + row;
-      if (RING && gave_up) {
-        // the previous block's partial for this tile was not seen: no merge
-        const f32x4 nan4 = {NAN, NAN, NAN, NAN};
+      if constexpr (SEQ) lse_keep[qb] = lse_out;
+      if (hi == 0) l_store(lrow, lse_out);
+    }
+    // the lane's value for columns db*32 + 8g + 4hi .. +3 of its row
+    auto value = [&](int db, int g) -> f32x4 {
+      const f32x4 ob = {o[qb][db][4 * g], o[qb][db][4 * g + 1], o[qb][db][4 * g + 2], o[qb][db][4 * g + 3]};
+      f32x4 v = fb * ob;
+      if (fa >= 0.f) {
+        const f32x4 a = o_load(orow + db * 32 + 8 * g);
+        v = f32x4{__builtin_fmaf(fa, a[0], v[0]), __builtin_fmaf(fa, a[1], v[1]), __builtin_fmaf(fa, a[2], v[2]),
+                  __builtin_fmaf(fa, a[3], v[3])};
+      }
+      return v;
+    };
+    if constexpr (!STAGE) {
+      if (row < p.Sq) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) o_store(orow + db * 32 + 8 * g + 4 * hi, nan4);
-        if (hi == 0) l_store(lrow, NAN);
-      } else if (acc) {
-        const float la2 = (SEQ ? lse_keep[qb] : l_load(lrow)) * kLog2e;
-        const float M = fmaxf(la2, lse2);
-        const float wa = fast_exp2(la2 - M);  // 0 when the accumulator is empty (-inf)
-        const float wb = fast_exp2(lse2 - M);
-        const float tot = wa + wb;
-        const float fa = wa / tot, fb = (wb / tot) * inv;
+          for (int g = 0; g < 4; ++g) o_store(orow + db * 32 + 8 * g, value(db, g));
+      }
+    } else {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+      for (int pp = 0; pp < 32 / SR; ++pp) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float* dst = orow + db * 32 + 8 * g + 4 * hi;
-            const f32x4 ob = {o[qb][db][4 * g], o[qb][db][4 * g + 1], o[qb][db][4 * g + 2],
-                              o[qb][db][4 * g + 3]};
-            const f32x4 oa = o_load(dst);
-            o_store(dst, (wa > 0.f) ? (fa * oa + fb * ob) : (fb * ob));
+        for (int db = 0; db < D / 32; ++db) {
+          if (SR == 32 || l32 / SR == pp) {
+            const int rl = l32 % SR;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) stg[rl * 8 + ((2 * g + hi) ^ (rl & 7))] = value(db, g);
           }
-        const float lse_new = (M + fast_log2(tot)) * kLn2;
-        if constexpr (SEQ) lse_keep[qb] = lse_new;
-        if (hi == 0) l_store(lrow, lse_new);
-      } else {
+          f32x4 v[SR / 8];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 ob = {o[qb][db][4 * g], o[qb][db][4 * g + 1], o[qb][db][4 * g + 2],
-                              o[qb][db][4 * g + 3]};
-            o_store(orow + db * 32 + 8 * g + 4 * hi, ob * inv);
+          for (int i = 0; i < SR / 8; ++i) v[i] = stg[(sr + 8 * i) * 8 + (sc ^ sr)];
+          // read here, all at once, not inside the row checks below
+          if constexpr (SR == 32) {
+            asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+          } else {
+            asm volatile("" : "+v"(v[0]), "+v"(v[1]));
           }
-        if constexpr (SEQ) lse_keep[qb] = lse2 * kLn2;
-        if (hi == 0) l_store(lrow, lse2 * kLn2);
+#pragma unroll
+          for (int i = 0; i < SR / 8; ++i) {
+            const int grow = qrow0 + qb * 32 + pp * SR + sr + 8 * i;
+            if (grow < p.Sq)
+              o_store(p.out + b * p.o_sb + (int64_t)grow * p.o_ss + h * p.o_sh + db * 32 + 4 * sc, v[i]);
+          }
+        }
       }
     }
   }
