@@ -108,6 +108,58 @@ def build(out: Optional[str] = None, defines: Optional[Dict[str, str]] = None,
     return out
 
 
+# Host-side sanitizers for the C ABI's argument checking (api.hip), host pass only: the GPU code
+# is built as usual. The link puts the shared sanitizer runtime on the library's run path; a process
+# that is not itself instrumented (python) must preload that runtime (sanitizer_runtime()).
+SANITIZE_HOST_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g",
+]
+SANITIZED_LIB = "libcpattn_sanitized.so"
+
+
+def _clangxx() -> str:
+    return os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang++")
+
+
+def sanitizer_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of the ROCm LLVM toolchain (it carries UBSan too)."""
+    r = subprocess.run([_clangxx(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("ROCm LLVM's shared ASan runtime not found")
+    return path
+
+
+def build_sanitized(out_dir: str) -> str:
+    """Build ``out_dir/libcpattn_sanitized.so``: api.hip's host code under AddressSanitizer and
+    UndefinedBehaviorSanitizer, every other source as in build(). For CPU tests of the host-side
+    validation (no kernel is launched by them)."""
+    os.makedirs(out_dir, exist_ok=True)
+    cc = hipcc()
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        extra = SANITIZE_HOST_FLAGS if src == "api.hip" else []
+        r = subprocess.run([cc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src} (sanitized build):\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    out = os.path.join(out_dir, SANITIZED_LIB)
+    rt_dir = os.path.dirname(sanitizer_runtime())
+    rocm_lib = os.path.join(os.path.dirname(os.path.realpath(cc)), "..", "lib")
+    link_flags = ["-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan"]
+    r = subprocess.run([_clangxx(), *link_flags, "-o", out, *objs, f"-L{rocm_lib}", "-lamdhip64",
+                        f"-Wl,-rpath,{rocm_lib}", f"-Wl,-rpath,{rt_dir}"], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stderr}")
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--out", default=None)

@@ -619,7 +619,8 @@ bool bwd_concurrent(int64_t n_dq, int64_t n_dkv) {
 
 // Under g_side_mu: the device's side stream forked from s, or nullptr to run
 // everything on s (no device id, s belongs to another device than the
-// current one, creation failed, or first use while s is being captured).
+// current one, creation failed, first use while s is being captured, or the
+// side stream is part of a graph capture that s is not).
 hipStream_t side_fork(hipStream_t s) {
   if (!CP_BWD_SIDE_STREAM) return nullptr;
   int dev = -1;
@@ -640,6 +641,23 @@ hipStream_t side_fork(hipStream_t s) {
         hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
       ss.failed = true;
+      (void)hipGetLastError();
+      return nullptr;
+    }
+  }
+  // The side stream joins a graph capture through the fork event and stays
+  // in it until that capture ends. While it is part of a capture that s does
+  // not belong to (another thread's), this call runs on s alone.
+  hipStreamCaptureStatus side_cs = hipStreamCaptureStatusNone;
+  unsigned long long side_id = 0;
+  if (hipStreamGetCaptureInfo(ss.s, &side_cs, &side_id) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (side_cs != hipStreamCaptureStatusNone) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    unsigned long long id = 0;
+    if (hipStreamGetCaptureInfo(s, &cs, &id) != hipSuccess || cs != hipStreamCaptureStatusActive || id != side_id) {
       (void)hipGetLastError();
       return nullptr;
     }

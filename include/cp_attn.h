@@ -400,7 +400,9 @@ cp_status_t cp_ulysses_concat_seq(const void* in, void* out, int elem_bytes, int
  * forked from the caller's stream by an event and joined back before the
  * call returns. The caller sees one stream-ordered operation on its stream,
  * also under graph capture; calls on one device from several host threads
- * are serialised while they enqueue.
+ * are serialised while they enqueue. Under capture the second stream joins
+ * the capturing graph until that capture ends; meanwhile a call whose stream
+ * is not part of that same capture runs all its kernels on its own stream.
  */
 
 /* Bytes of backward workspace for these sizes (0 if any size is <= 0). */

@@ -583,3 +583,64 @@ def test_ring_and_backward_replay_in_a_graph(cp):
         for name, got, w in zip(("out", "lse", "dq", "dk", "dv"), (out, lse, dq, dk_all, dv_all), want):
             assert torch.equal(got, w), f"replay {rep}: {name} differs from the eager run"
     say("graph replays match the eager run bit for bit")
+
+
+def test_backward_on_another_stream_during_a_capture(cp):
+    """While one stream captures a backward whose dQ kernels use the library's second stream, that
+    stream belongs to the capture until it ends. An eager backward on another stream meanwhile must
+    not join it: it runs on its own stream, completes with the eager results, and the capture still
+    replays them."""
+    B, H, D, Sq, lens = 1, 4, 128, 300, (256, 200)
+    say("eager backward beside a capture")
+    inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=83)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    offs = workloads.block_offsets(lens)
+    kb = [k[:, a:a + L] for a, L in zip(offs, lens)]
+    vb = [v[:, a:a + L] for a, L in zip(offs, lens)]
+    do = torch.from_numpy(workloads.grad_out((B, Sq, H, D), 83)).cuda()
+    scale, flags = inp.workload.scale, cp.CP_RING_ANYTHING
+    out = torch.empty((B, Sq, H, D), device="cuda")
+    lse = torch.empty((B, H, Sq), device="cuda")
+    cp.cp_ring_attention(q, kb, vb, out, lse, scale=scale, flags=flags)
+
+    def grads():
+        dq = torch.empty_like(out)
+        dk_all = torch.empty((B, sum(lens), H, D), device="cuda")
+        dv_all = torch.empty_like(dk_all)
+        ws = torch.empty(cp.cp_attn_bwd_workspace_size(B, H, Sq, D), dtype=torch.uint8, device="cuda")
+        return dq, dk_all, dv_all, ws
+
+    def bwd(g, stream=None):
+        dq, dk_all, dv_all, ws = g
+        cp.cp_ring_attention_bwd(q, kb, vb, out, lse, do, dq, [dk_all[:, a:a + L] for a, L in zip(offs, lens)],
+                                 [dv_all[:, a:a + L] for a, L in zip(offs, lens)], scale=scale, flags=flags,
+                                 workspace=ws, stream=stream)
+
+    ref = grads()
+    bwd(ref)
+    torch.cuda.synchronize()
+    cap, eager = grads(), grads()
+    cap_stream, other = torch.cuda.Stream(), torch.cuda.Stream()
+    cap_stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap_stream):  # warm-up on the capture stream
+        bwd(cap)
+    torch.cuda.current_stream().wait_stream(cap_stream)
+    torch.cuda.synchronize()
+    for t in eager[:3]:
+        t.fill_(float("nan"))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap_stream, capture_error_mode="relaxed"):
+        bwd(cap)  # the second stream joins this capture
+        bwd(eager, stream=other.cuda_stream)  # not part of it: runs now, on `other` only
+    other.synchronize()
+    for name, got, want in zip(("dq", "dk", "dv"), eager[:3], ref[:3]):
+        assert torch.equal(got, want), f"eager backward beside the capture: {name} differs"
+    for t in cap[:3]:
+        t.fill_(float("nan"))
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    for name, got, want in zip(("dq", "dk", "dv"), cap[:3], ref[:3]):
+        assert torch.equal(got, want), f"captured backward: {name} differs"
+    say("eager backward beside the capture and the replay match the eager run")
