@@ -365,7 +365,8 @@ def time_hbm_kernels(reps: int = 5):
     in place); the Ulysses-2 share's regroup of its Q, K and V shards
     ([1, 2304, 24, 128] bf16 each -> [1, 4608, 12, 128]) as the step runs it
     (one cp_ulysses_regroup_multi launch) and as three cp_ulysses_regroup
-    launches; cp_ulysses_regroup SEQ_TO_HEAD of a [1, 16384, 24, 128] bf16
+    launches, and back to back over six sets of operands (the rate in a
+    pipeline, launch latency hidden); cp_ulysses_regroup SEQ_TO_HEAD of a [1, 16384, 24, 128] bf16
     tensor at degree 2, cp_ulysses_pack_heads of the same tensor into uneven
     head groups (7, 6, 6, 5) and cp_attn_pack_v of it (as one V block of 16384
     keys). Before each timed launch a 512 MiB buffer is read so that neither L2
@@ -421,7 +422,21 @@ def time_hbm_kernels(reps: int = 5):
 
     record("ulysses_regroup_qkv_3launch", timed(three), qkv_bytes,
            "Q, K, V [1,2304,24,128] bf16 -> [1,4608,12,128], one launch per tensor (Ulysses-2 share)")
-    del xs, ys
+    # back to back, as in a pipeline (the launch overlaps the previous kernel), over 6 sets of
+    # operands (510 MB, twice the Infinity Cache) so that each launch reads uncached data
+    sets = [([torch.randn(1, S3, H, D, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3)],
+             [torch.empty(1, P * S3, H // P, D, dtype=torch.bfloat16, device="cuda") for _ in range(3)])
+            for _ in range(6)]
+    n_b2b = 60
+
+    def b2b():
+        for i in range(n_b2b):
+            cp.cp_ulysses_regroup_multi(*sets[i % len(sets)], P, cp.CP_REGROUP_SEQ_TO_HEAD)
+
+    record("ulysses_regroup_qkv_back_to_back", timed(b2b) / n_b2b, qkv_bytes,
+           "Q, K, V [1,2304,24,128] bf16 -> [1,4608,12,128], one launch, 60 launches back to back over 6 "
+           "operand sets (Ulysses-2 share)")
+    del xs, ys, sets
     S_l = 16384
     x = torch.randn(B, S_l, H, D, device="cuda", generator=g).to(torch.bfloat16)
     y = torch.empty(B, P * S_l, H // P, D, dtype=torch.bfloat16, device="cuda")
