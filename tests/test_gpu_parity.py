@@ -2,10 +2,10 @@
 
 Every case draws seeded inputs from ``workloads``, runs the library on the GPU
 and compares element by element with the oracle on the same values. Small
-shapes are compared in full (they span several tiles and a ragged tail); the
-full-size workloads are compared on sampled query rows, which the oracle
-computes one by one against every key, in the same launch configuration the
-benchmark times. Tolerances: float32 inputs 1e-5 (out and LSE), bfloat16
+shapes are compared in full (they span several tiles and a ragged tail), and
+so are the full-size workloads, in the same launch configuration the benchmark
+times: every element of out and LSE against the oracle's full attention
+(computed once per workload and head, cached for the session). Tolerances: float32 inputs 1e-5 (out and LSE), bfloat16
 inputs 1e-2 (out) and 1e-3 (LSE); the regroup is bit-exact.
 """
 import math
@@ -367,7 +367,7 @@ def test_usp_small_full_compare(cp, B, S_l, H, D, P, R):
 
 def test_workload_usp_u2r2(cp):
     w = workloads.by_name("flux1024_usp_u2r2_bf16")
-    say(w.name, "regroups + ring over 2 blocks + inverse regroup, sampled rows")
+    say(w.name, "regroups + ring over 2 blocks + inverse regroup, every element")
     inp = workloads.make_inputs(w)
     P, R = w.ulysses_degree, w.ring_degree
     ks = [inp.k_shard(r) for r in range(R)]
@@ -490,7 +490,7 @@ def test_ulysses_anything_all_ranks(cp, B, seq, heads, D):
 
 def test_workload_ulysses_anything4(cp):
     """Rank 0's share as bench.py runs it: pack of its shards, attention of head group 0 over all
-    4481 tokens, unpack of the second exchange's pieces; sampled rows against the oracle."""
+    4481 tokens, unpack of the second exchange's pieces; every element against the oracle."""
     w = workloads.by_name("flux1008_ulysses_anything4_bf16")
     say(w.name)
     import bench
