@@ -4,7 +4,7 @@ The packed layout is checked element by element against the definition in the
 header, rebuilt here with numpy index arithmetic. Attention over packed V feeds
 the matrix cores the same operands in the same order as attention over the
 unpacked V, so the two must agree bit for bit; at the benchmark's full sizes the
-packed ring is also compared with the float64 oracle on sampled rows.
+packed ring is also compared with the float64 oracle on every element.
 """
 import numpy as np
 import pytest
