@@ -159,10 +159,14 @@ struct Params {
   int vnt[kMaxRingBlocks];
 };
 
+// Maximum that propagates NaN (IEEE maximum): unlike fmaxf it needs no
+// quieting of its operands first, so a row maximum costs only v_maximum3 ops.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Both 32-lane halves of a wave64 end up with max/sum over the pair (l, l^32).
 __device__ __forceinline__ float half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -463,11 +467,11 @@ seq_next_block:
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          mx0 = fmaxf(mx0, s_cur[qb][kb][r]);
-          mx1 = fmaxf(mx1, s_cur[qb][kb][r + 1]);
+        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) {
+          mx0 = vmax(mx0, s_cur[qb][kb][r]);
+          mx1 = vmax(mx1, s_cur[qb][kb][r + 1]);
         }
-      const float mt = half_max(fmaxf(mx0, mx1)) * csc;
+      const float mt = half_max(vmax(mx0, mx1)) * csc;
       const bool need = __builtin_amdgcn_ballot_w64(mt > m_run[qb] + CP_FWD_LAZY) != 0;
       const float m_new = need ? fmaxf(m_run[qb], mt) : m_run[qb];
       alpha[qb] = fast_exp2(m_run[qb] - m_new);  // 1 when the maximum is kept
@@ -489,7 +493,7 @@ seq_next_block:
       const float mneg = -m_run[qb];
       // float32 sums of the unrounded probabilities (LSE needs them), in four
       // independent partial sums so that the adds do not form one dependent chain
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      float ls[4];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -499,7 +503,11 @@ seq_next_block:
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
             const float e = fast_exp2(fmaf(s_cur[qb][kb][kk2 * 8 + jj], csc, mneg));
-            ls[jj & 3] += e;
+            if (kb == 0 && kk2 == 0 && jj < 4) {
+              ls[jj] = e;
+            } else {
+              ls[jj & 3] += e;
+            }
             t[jj] = (__bf16)e;
           }
           pf[qb][kb][kk2] = t;
