@@ -338,3 +338,36 @@ def test_ring_one_launch_splits_a_single_block(cp, B, H, Sq, L):
     o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.workload.scale)
     assert_close("out", o1.cpu().numpy(), o_ref, TOL["bf16"]["o"])
     assert_close("lse", l1.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
+
+
+def test_ring_output_beyond_2gib_offsets(cp):
+    """The parallel-partials ring addresses out and lse with 32-bit buffer offsets, so a call whose
+    output view spans 2 GiB or more must take another launch form. Here batch entry 1 of out lies
+    2.25 GiB past batch entry 0 (a view into a 4.5 GiB buffer): the result equals, bit for bit, the
+    same call on a compact out (which runs as one parallel-partials launch), and the oracle."""
+    B, H, D, Sq, lens = 2, 3, 128, 300, (256, 200)
+    assert cp.cp_ring_attention_one_launch(cp.CP_BF16, B, H, D, Sq, lens) == cp.CP_ONE_LAUNCH_PARALLEL
+    say("ring with out spanning more than 2 GiB")
+    inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=77)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    offs = workloads.block_offsets(lens)
+    kb = [k[:, a:a + L] for a, L in zip(offs, lens)]
+    pv = [cp.pack_v(v[:, a:a + L].contiguous()) for a, L in zip(offs, lens)]
+    flags = cp.CP_RING_ANYTHING
+    n = cp.cp_ring_attention_workspace_size(B, H, Sq, D, cp.CP_RING_PACKED_V | flags)
+    ws = torch.zeros((n,), dtype=torch.uint8, device="cuda")
+    out_c = torch.full((B, Sq, H, D), float("nan"), device="cuda")
+    lse_c = torch.full((B, H, Sq), float("nan"), device="cuda")
+    cp.cp_ring_attention(q, kb, pv, out_c, lse_c, scale=inp.workload.scale, flags=flags, workspace=ws)
+    rows = (9 << 30) // (4 * H * D * 4)  # rows per batch entry: 2.25 GiB
+    big = torch.empty((B, rows, H, D), device="cuda")
+    out_b = big[:, :Sq]
+    out_b.fill_(float("nan"))
+    lse_b = torch.full((B, H, Sq), float("nan"), device="cuda")
+    cp.cp_ring_attention(q, kb, pv, out_b, lse_b, scale=inp.workload.scale, flags=flags, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_b, out_c) and torch.equal(lse_b, lse_c)
+    o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.workload.scale)
+    assert_close("out", out_b.cpu().numpy(), o_ref, TOL["bf16"]["o"])
+    assert_close("lse", lse_b.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
+    del big, out_b
