@@ -86,6 +86,10 @@ def parse():
                     help="comma-separated workloads whose block kernel is also timed (roofline_extra); '' for none")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward")
     ap.add_argument("--no-hbm", action="store_true", help="skip the cold-cache HBM kernels")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="instead of the benchmark: load the diagnostic library (libcpattn_phase.so) and "
+                         "print the core-clock cycles of the block kernel's tile-loop intervals for the "
+                         "workload's one-block launch (8-wave shape)")
     return ap.parse_args()
 
 
@@ -545,12 +549,83 @@ def block_roofline(prob, reps: int, graph: bool):
             "frac_at_clock": None if mhz is None else round(achieved / (peak * mhz / NOMINAL_CLOCK_MHZ), 4)}
 
 
+PHASE_VALUES = 8  # per wave: [interval parity][work, wait at the barrier], interval count, unused
+
+
+def phase_trace(prob, warm_seconds: float = 0.5) -> dict:
+    """Cycle accounting of the block kernel's ping-pong tile loop (diagnostic library only).
+
+    Every wave of the 8-wave one-block launch reads the core clock (s_memtime) before and after
+    each workgroup barrier of its tile loop (the loop's first three barriers left out) and sums,
+    per interval parity, the work up to the barrier's waits and the time in them (tile loads, LDS
+    accesses, the other waves). Each reading is a scalar memory round trip the wave waits for, so
+    the traced launch runs slower than the plain one and both sums include those trips. Group A
+    (waves 0-3) runs its softmax in the odd intervals and its matrix-core half in the even ones,
+    group B (waves 4-7) the other way round. Medians over the workgroups' waves, in cycles per
+    interval, after `warm_seconds` of launches; one traced launch timed with HIP events."""
+    import ctypes
+    import numpy as np
+    import torch
+    cp, w = prob.cp, prob.w
+    lib = ctypes.CDLL(cp._lib.library_path())
+    if not hasattr(lib, "cp_debug_phase_trace"):
+        raise SystemExit(f"{cp._lib.library_path()} is not the diagnostic build (no cp_debug_phase_trace)")
+    lib.cp_debug_phase_trace.argtypes = [ctypes.c_void_p, ctypes.c_long]
+    lib.cp_debug_phase_trace.restype = ctypes.c_int
+    if w.dtype != "bf16" or len(prob.kb) != 1 or cp.cp_attn_fwd_waves(w.B, w.attn_H, w.D, w.Sq) != 8:
+        raise SystemExit("the phase trace covers the bfloat16 one-block launch on the 8-wave shape")
+    n_wg = -(-w.Sq // 256) * w.attn_H * w.B
+    if n_wg > 1024:
+        raise SystemExit(f"the diagnostic build records 1024 workgroups; this launch has {n_wg}")
+
+    def once():
+        cp.cp_attn_block_fwd(prob.q_att, prob.kb[0], prob.vb_att[0], prob.out, prob.lse, scale=w.scale)
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_seconds:
+        for _ in range(10):
+            once()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    once()
+    e1.record()
+    torch.cuda.synchronize()
+    n = n_wg * 8 * PHASE_VALUES
+    buf = (ctypes.c_ulonglong * n)()
+    st = lib.cp_debug_phase_trace(ctypes.addressof(buf), n)
+    if st != 0:
+        raise SystemExit(f"cp_debug_phase_trace failed ({st})")
+    a = np.frombuffer(buf, dtype=np.uint64).reshape(n_wg, 8, PHASE_VALUES).astype(np.float64)
+    count = a[:, :, 4]
+    if not (count > 1).all():
+        raise SystemExit("some waves recorded no intervals")
+    per = a[:, :, :4].reshape(n_wg, 8, 2, 2) / (count[:, :, None, None] / 2)
+    kinds = []
+    for par, name, a_half, b_half in ((1, "A softmax / B matrix half", "softmax", "matrix half"),
+                                      (0, "A matrix half / B softmax", "matrix half", "softmax")):
+        x = per[:, :, par, :]
+        grp = {}
+        for g, ws, half in (("A", slice(0, 4), a_half), ("B", slice(4, 8), b_half)):
+            med = np.median(x[:, ws, :].reshape(-1, 2), axis=0)
+            grp[g] = {"half": half, "work": round(float(med[0])), "wait": round(float(med[1]))}
+        kinds.append({"interval": name, "cycles": round(float(np.median(x.sum(axis=2)))), **grp})
+    step = sum(k["cycles"] for k in kinds)
+    return {"workload": w.name, "traced_launch_us": round(e0.elapsed_time(e1) * 1e3, 2), "workgroups": n_wg,
+            "intervals_per_wave": int(np.median(count)), "cycles_per_step": step,
+            "mfma_cycles_per_simd_step": 64 * 32, "intervals": kinds}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
+    if args.phase_trace:
+        # the diagnostic build, loaded before anything else loads the library
+        from context_attention_dits_amd.build import PHASE_TRACE_LIB
+        os.environ["CP_ATTN_LIBRARY"] = os.path.join(ROOT, "context_attention_dits_amd", PHASE_TRACE_LIB)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -558,6 +633,9 @@ def main():
     w = workloads.by_name(args.workload)
     log(f"[bench] workload {w.name}: B={w.B} H={w.attn_H} D={w.D} Sq={w.Sq} blocks={list(w.block_lens)}")
     prob = Problem(w, args.separate_merge, packed_v=not args.unpacked_v)
+    if args.phase_trace:
+        print(json.dumps({"phase_trace": phase_trace(prob)}), flush=True)
+        return 0
 
     # A burst of a few milliseconds runs on a GPU that is still changing its clock: the first
     # ~30 ms of steps of the FLUX ring-2 share take ~15% longer than later ones. Untimed steps

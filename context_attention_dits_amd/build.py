@@ -46,6 +46,13 @@ def hipcc() -> str:
 # so every wait gives up, is counted and poisons its tile, while every kernel still ends normally.
 RING_WAIT_TEST_LIB = "libcpattn_ringwait_test.so"
 RING_WAIT_TEST_DEFINES = {"CP_RING_TEST_NEVER_READY": "1"}
+# A diagnostic library: the block kernel's one-block launch also records the core-clock cycles of
+# its tile-loop intervals (work, wait for tile loads, barrier wait; cp_debug_phase_trace, which the
+# C ABI header does not declare). bench.py --phase-trace loads it.
+PHASE_TRACE_LIB = "libcpattn_phase.so"
+PHASE_TRACE_DEFINES = {"CP_FWD_PHASE_TRACE": "1"}
+# Libraries built next to the main one with only the forward kernel recompiled: name -> defines.
+VARIANT_LIBS = {RING_WAIT_TEST_LIB: RING_WAIT_TEST_DEFINES, PHASE_TRACE_LIB: PHASE_TRACE_DEFINES}
 
 
 def build(out: Optional[str] = None, defines: Optional[Dict[str, str]] = None,
@@ -81,30 +88,29 @@ def build(out: Optional[str] = None, defines: Optional[Dict[str, str]] = None,
             raise RuntimeError(f"built library does not load: {e}") from e
         os.replace(tmp, dst)
 
-    # the ring-wait test library needs only the forward kernel recompiled with its define
-    wait_dir = os.path.join(PKG, "_build", "ringwait_test")
-    wait_obj = os.path.join(wait_dir, "attn_fwd_bf16.o")
-    with_test = test_libs and not defines
+    # the variant libraries need only the forward kernel recompiled with their defines
+    with_variants = test_libs and not defines
 
-    def compile_wait() -> str:
-        os.makedirs(wait_dir, exist_ok=True)
-        df = [f"-D{k}={v}" for k, v in sorted(RING_WAIT_TEST_DEFINES.items())]
-        cmd = [cc, *HIPCC_FLAGS, *df, "-c", os.path.join(CSRC, "attn_fwd_bf16.hip"), "-o", wait_obj]
+    def compile_variant(name: str) -> str:
+        vdir = os.path.join(PKG, "_build", name.replace(".so", ""))
+        os.makedirs(vdir, exist_ok=True)
+        obj = os.path.join(vdir, "attn_fwd_bf16.o")
+        df = [f"-D{k}={v}" for k, v in sorted(VARIANT_LIBS[name].items())]
+        cmd = [cc, *HIPCC_FLAGS, *df, "-c", os.path.join(CSRC, "attn_fwd_bf16.hip"), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed for attn_fwd_bf16.hip (ring-wait test build):\n{r.stderr}")
-        return wait_obj
+            raise RuntimeError(f"hipcc failed for attn_fwd_bf16.hip ({name} build):\n{r.stderr}")
+        return obj
 
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + len(VARIANT_LIBS), os.cpu_count() or 4)) as ex:
         futs = [ex.submit(compile_one, src) for src in SOURCES]
-        wait_fut = ex.submit(compile_wait) if with_test else None
+        var_futs = {n: ex.submit(compile_variant, n) for n in VARIANT_LIBS} if with_variants else {}
         objs = [f.result() for f in futs]
-        if wait_fut is not None:
-            wait_fut.result()
+        var_objs = {n: f.result() for n, f in var_futs.items()}
     link(objs, out)
-    if with_test:
-        link([wait_obj if os.path.basename(o) == "attn_fwd_bf16.o" else o for o in objs],
-             os.path.join(os.path.dirname(out), RING_WAIT_TEST_LIB))
+    for name, vobj in var_objs.items():
+        link([vobj if os.path.basename(o) == "attn_fwd_bf16.o" else o for o in objs],
+             os.path.join(os.path.dirname(out), name))
     return out
 
 

@@ -101,11 +101,23 @@
 #ifndef CP_FWD_SEQ
 #define CP_FWD_SEQ 1  // rings of 2+ blocks on the 8-wave shape: one launch, blocks in turn per workgroup
 #endif
+#ifndef CP_FWD_PHASE_TRACE
+#define CP_FWD_PHASE_TRACE 0  // diagnostic builds only: cycle sums of the one-block launch's tile-loop intervals
+#endif
 #ifndef CP_FWD_LAZY
 #define CP_FWD_LAZY 8.0f  // rescale threshold on the row maximum, log2 units
 #endif
 
 namespace cpattn {
+#if CP_FWD_PHASE_TRACE
+// Diagnostic builds: for each of the first kPhaseWg workgroups of a one-block launch and each
+// wave, core-clock cycles of the tile loop's barrier intervals (the first three left out),
+// summed by interval parity: [parity][work, wait at the barrier (tile loads, LDS accesses and
+// the other waves)], then the number of intervals summed. Each launch overwrites the entries of
+// the workgroups it runs.
+constexpr int kPhaseWg = 1024, kPhaseVals = 8;
+__device__ unsigned long long g_phase[kPhaseWg * 8 * kPhaseVals];
+#endif
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -671,14 +683,45 @@ seq_next_block:
   // its `pending` most recent global->LDS loads have landed (loads complete in
   // issue order). The memory clobbers keep the compiler from moving LDS
   // accesses across it.
+#if CP_FWD_PHASE_TRACE
+  // The core clock (s_memtime, waited for in the same statement: each reading is a scalar
+  // memory round trip that the wave waits for, which the cycle counts include), read before and
+  // after each barrier's waits; sums (see g_phase) of the work up to the wait, and of the wait for
+  // tile loads and LDS accesses plus the barrier wait. 32-bit: differences of the counter's low
+  // word, and sums over a launch, stay far below 2^32.
+  constexpr bool TRACE = !RING && !SEQ;
+  auto clock_now = [] {
+    unsigned long long t;
+    asm volatile("s_memtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t));
+    return (uint32_t)t;
+  };
+  uint32_t ph_prev = TRACE ? clock_now() : 0;
+  uint32_t ph_sum[2][2] = {{0, 0}, {0, 0}};
+  int ph_i = 0;
+#endif
   auto sync = [&](auto pending_tag) {
     constexpr int PENDING = decltype(pending_tag)::value;  // 63: no wait on loads
     static_assert(PENDING >= 0 && PENDING < 64, "vmcnt field");
+#if CP_FWD_PHASE_TRACE
+    uint32_t t1 = 0;
+    if constexpr (TRACE) t1 = clock_now();
+#endif
     // s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
     __builtin_amdgcn_s_waitcnt(0x0070 | (PENDING & 15) | ((PENDING >> 4) << 14));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+#if CP_FWD_PHASE_TRACE
+    if constexpr (TRACE) {
+      const uint32_t t2 = clock_now();
+      if (ph_i >= 3) {
+        ph_sum[ph_i & 1][0] += t1 - ph_prev;
+        ph_sum[ph_i & 1][1] += t2 - t1;
+      }
+      ph_prev = t2;
+      ++ph_i;
+    }
+#endif
   };
   using Pend0 = std::integral_constant<int, 0>;
   using PendAll = std::integral_constant<int, 63>;
@@ -839,6 +882,17 @@ seq_next_block:
       step(Last{}, C0{}, j);
     }
   }
+
+#if CP_FWD_PHASE_TRACE
+  if constexpr (TRACE) {
+    if (blockIdx.x < kPhaseWg && lane == 0) {
+      unsigned long long* d = g_phase + (blockIdx.x * 8 + wave) * kPhaseVals;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = ph_sum[i / 2][i % 2];
+      d[4] = (unsigned long long)(ph_i > 3 ? ph_i - 3 : 0);
+    }
+  }
+#endif
 
   // ---- epilogue: normalise, LSE, optional merge into the accumulator
   // RING: block 0 writes, later blocks merge, each after the previous block's
@@ -1295,6 +1349,15 @@ hipError_t launch_ring_bf16(const FwdArgs& a, const RingBlocks& rb, int* ws, hip
   }
   return hipErrorInvalidValue;
 }
+
+#if CP_FWD_PHASE_TRACE
+// Diagnostic builds only (not part of the C ABI header): copy the first n values of g_phase.
+extern "C" int cp_debug_phase_trace(unsigned long long* host, long n) {
+  const long total = (long)kPhaseWg * 8 * kPhaseVals;
+  if (host == nullptr || n < 0 || n > total) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase), (size_t)n * 8, 0, hipMemcpyDeviceToHost);
+}
+#endif
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.D == 128) return launch_dn<128>(a, stream);

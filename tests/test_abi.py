@@ -34,6 +34,25 @@ def test_exports_every_declared_symbol(lib):
     assert lib.cp_abi_version() == _lib.ABI_VERSION
 
 
+def test_phase_trace_only_in_the_diagnostic_library(lib):
+    """The tile-loop cycle trace (bench.py --phase-trace) lives in its own library; the main one
+    has neither the symbol nor the instrumentation's device buffer."""
+    from context_attention_dits_amd.build import PHASE_TRACE_LIB
+    assert not hasattr(lib, "cp_debug_phase_trace")
+    path = os.path.join(os.path.dirname(_lib.DEFAULT_PATH), PHASE_TRACE_LIB)
+    if _lib.library_path() != _lib.DEFAULT_PATH or not os.path.exists(path):
+        pytest.skip("diagnostic library not built next to the default one")
+    diag = ctypes.CDLL(path)
+    assert hasattr(diag, "cp_debug_phase_trace")
+    diag.cp_debug_phase_trace.argtypes = [ctypes.c_void_p, ctypes.c_long]
+    diag.cp_debug_phase_trace.restype = ctypes.c_int
+    # argument checks only (no copy is attempted, so no GPU is needed)
+    assert diag.cp_debug_phase_trace(None, 8) != 0
+    buf = (ctypes.c_ulonglong * 1)()
+    assert diag.cp_debug_phase_trace(ctypes.addressof(buf), -1) != 0
+    assert diag.cp_debug_phase_trace(ctypes.addressof(buf), 1 << 40) != 0
+
+
 def _block(lib, dtype=1, B=1, H=2, D=128, Sq=8, Skv=8, scale=0.1, flags=0, q=FAKE, k=FAKE, v=FAKE,
            out=FAKE, lse=FAKE, qs=None, kvs=None, os_=None):
     return lib.cp_attn_block_fwd(q, qs, k, v, kvs, dtype, B, H, D, Sq, Skv, scale, flags, out, os_, lse, None)
