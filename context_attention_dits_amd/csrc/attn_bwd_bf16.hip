@@ -17,8 +17,9 @@
 // single-pass gradients.
 //
 // Design (reusing the forward's layouts, see attn_fwd_bf16.hip):
-//   * bwd_prep: one 16- or 8-lane group per (b, s, h) row computes D_i and
-//     writes dO rounded to bf16, the MFMA operand of both kernels.
+//   * bwd_prep: one 16- or 8-lane group per (b, s, h) row writes dO rounded
+//     to bf16, the MFMA operand of both kernels, and computes D_i from that
+//     rounded dO (so that dP - D is exact for the dO the products use).
 //   * dq kernel, one lane per query as in the forward: S^T = K Q^T and
 //     dP^T = V dO^T on v_mfma_f32_32x32x16_bf16 with Q and dO in registers,
 //     K and V fragments from LDS; P^T and dS^T stay in the accumulator
@@ -539,7 +540,7 @@ attn_bwd_dkv_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ prep
 
-// D_i = sum_d dO_id O_id and dO rounded to bf16 (contiguous [B, Sq, H, D]).
+// dO rounded to bf16 (contiguous [B, Sq, H, D]) and D_i = sum_d dO_id O_id of that rounded dO.
 // G = D / 8 lanes per (b, s, h) row, 8 elements each.
 template <int D>
 __global__ void __launch_bounds__(256)
@@ -558,13 +559,16 @@ attn_bwd_prep_kernel(const float* __restrict__ out, Strides os, const float* __r
     const float* dp = dout + b * ds.b + (int64_t)s * ds.s + h * ds.h + c * 8;
     const f32x4 o0 = *reinterpret_cast<const f32x4*>(op), o1 = *reinterpret_cast<const f32x4*>(op + 4);
     const f32x4 d0 = *reinterpret_cast<const f32x4*>(dp), d1 = *reinterpret_cast<const f32x4*>(dp + 4);
+    // D from dO as rounded for the products (dP = dO V^T takes the bfloat16 dO): then
+    // dP - D is the exact difference for that dO, and cancels where it should (one key:
+    // P = 1, O = v, dS = 0) instead of leaving dO's rounding error times |dO| |v|.
     bf16x8 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc = fmaf(o0[e], d0[e], acc);
-      acc = fmaf(o1[e], d1[e], acc);
       w[e] = (__bf16)d0[e];
       w[4 + e] = (__bf16)d1[e];
+      acc = fmaf(o0[e], (float)w[e], acc);
+      acc = fmaf(o1[e], (float)w[4 + e], acc);
     }
     *reinterpret_cast<bf16x8*>(dob + (int64_t)row * D + c * 8) = w;
   }

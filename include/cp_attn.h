@@ -386,7 +386,9 @@ cp_status_t cp_ulysses_concat_seq(const void* in, void* out, int elem_bytes, int
  *   dQ_i  = scale sum_j dS_ij k_j                (sum over every block's keys)
  * the derivative of softmax attention; per block, j runs over that block's
  * keys. The MFMA operands dO and P, dS are rounded to bfloat16, D_i, the
- * exponent and every accumulation are float32.
+ * exponent and every accumulation are float32; D_i is summed from the same
+ * bfloat16 dO the products use, so dP - D is exact for that dO (with one key,
+ * P = 1 and O = v give dS = 0, as they should).
  *
  * Workspace (caller-owned, 256-byte aligned): dO rounded to bfloat16
  * ([B, Sq, H, D], contiguous) and D ([B, H, Sq] float32), written by

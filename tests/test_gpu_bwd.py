@@ -8,9 +8,11 @@ Tolerance, derived from the kernels' arithmetic (no tolerance for gradients
 is fixed elsewhere). With u = 2^-8 the unit roundoff of bfloat16 (8
 significant bits) and, per (b, h), P = exp(scale QK^T - LSE), dP = dO V^T,
 dS = P (dP - D):
-  * dO is rounded to bfloat16, so dP_ij carries at most u A_ij with
-    A = |dO| |V|^T; dS_ij is rounded to bfloat16 (u |dS_ij|). Its error is at
-    most u W_ij with W = |dS| + P A.
+  * dO is rounded to bfloat16 and both dP = dO V^T and D = rowsum(dO O)
+    take the rounded dO, so dP_ij - D_i carries at most u (A_ij + a_i) with
+    A = |dO| |V|^T and a_i = sum_d |dO_id| |O_id|; dS_ij is rounded to
+    bfloat16 (u |dS_ij|). Its error is at most u W_ij with
+    W = |dS| + P (A + a).
   * dQ = scale dS K and dK = scale dS^T Q take K and Q exactly (they are
     bfloat16 inputs): |err dQ| <= scale (u + n 2^-24) W |K|, |err dK| <=
     scale (u + n 2^-24) W^T |Q|, the n 2^-24 term bounding float32
@@ -68,6 +70,7 @@ def _bounds(q, k_blocks, v_blocks, o, lse, do, scale):
             qh = q[b, :, h].astype(np.float64)
             doh = do[b, :, h].astype(np.float64)
             dlt = np.sum(doh * o[b, :, h], axis=1)
+            dlt_abs = np.sum(np.abs(doh) * np.abs(o[b, :, h]), axis=1)
             for i, (kb, vb) in enumerate(zip(k_blocks, v_blocks)):
                 if kb.shape[1] == 0:
                     continue
@@ -75,7 +78,7 @@ def _bounds(q, k_blocks, v_blocks, o, lse, do, scale):
                 vh = vb[b, :, h].astype(np.float64)
                 p = np.exp(scale * (qh @ kh.T) - lse[b, h][:, None])
                 ds = p * (doh @ vh.T - dlt[:, None])
-                w = np.abs(ds) + p * (np.abs(doh) @ np.abs(vh).T)
+                w = np.abs(ds) + p * (np.abs(doh) @ np.abs(vh).T + dlt_abs[:, None])
                 bq[b, :, h] += scale * (U + n_total * EPS32) * (w @ np.abs(kh))
                 bks[i][b, :, h] = scale * (U + Sq * EPS32) * (w.T @ np.abs(qh))
                 bvs[i][b, :, h] = (2 * U + Sq * EPS32) * (p.T @ np.abs(doh))
@@ -170,6 +173,37 @@ def test_bwd_peaked_softmax(cp):
     o, lse = _fwd_oracle(inp, scale)
     got = _run(cp, inp, do, o, lse, scale)
     _check_all("bwd peaked", inp, do, scale, got)
+
+
+@pytest.mark.parametrize("D,Sq,lens", [(128, 300, (1,)), (64, 489, (0, 1)), (128, 97, (1, 0, 0))])
+def test_bwd_single_key_gradients_vanish(cp, D, Sq, lens):
+    """One key in the whole ring: every row's softmax is the constant 1, so O = v and the exact
+    dQ and dK are zero (dS = P (dP - D) = dO.v - dO.v). The kernels take dP and D from the same
+    bfloat16 dO, so what remains is float32 accumulation order, bounded per row by
+    2 D 2^-24 sum_d |dO_id| |v_d| for dS_i; a D computed from a differently rounded dO would
+    leave u |dO_i| |v| (128 times more at D = 128)."""
+    B, H = 1, 3
+    say("bwd single key", D, Sq, lens)
+    inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=41 + D + Sq)
+    scale = 1.0 / np.sqrt(D)
+    do = workloads.grad_out((B, Sq, H, D), 41)
+    o, lse = _fwd_oracle(inp, scale)
+    o32, lse32 = o.astype(np.float32), lse.astype(np.float32)
+    dq, dks, dvs = _run(cp, inp, do, o32, lse32, scale)
+    i = [j for j, L in enumerate(lens) if L == 1][0]
+    k1 = inp.k_block(i)[:, 0].astype(np.float64)  # [B, H, D]
+    v1 = inp.v_block(i)[:, 0].astype(np.float64)
+    dob = do.astype(np.float64)
+    b_ds = 2 * D * EPS32 * np.einsum("bshd,bhd->bsh", np.abs(dob), np.abs(v1))  # [B, Sq, H]
+    bound_dq = 1.25 * scale * (1 + U) * b_ds[..., None] * np.abs(k1)[:, None] + 1e-7
+    bound_dk = 1.25 * scale * (1 + U) * np.einsum("bsh,bshd->bhd", b_ds, np.abs(inp.q.astype(np.float64))) + 1e-7
+    say(f"max|dq|={np.abs(dq).max():.3e} (bound {bound_dq.max():.3e}), max|dk|={np.abs(dks[i]).max():.3e} "
+        f"(bound {bound_dk.max():.3e})")
+    assert np.all(np.abs(dq) <= bound_dq), "dQ of a one-key softmax is not zero to float32 rounding"
+    assert np.all(np.abs(dks[i][:, 0]) <= bound_dk), "dK of a one-key softmax is not zero to float32 rounding"
+    # dV of the one key is sum_i dO_i (P = 1); the other, empty blocks have no rows
+    dv_ref = dob.sum(axis=1)
+    _compare("single key dv", dvs[i][:, 0], dv_ref, (2 * U + Sq * EPS32) * np.abs(dob).sum(axis=1))
 
 
 def test_bwd_block_api_and_strided_views(cp):
