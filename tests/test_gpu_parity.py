@@ -534,6 +534,55 @@ def test_short_blocks_many_seeds(cp, waves):
             assert_close("lse", lse.cpu().numpy(), l_ref, TOL["bf16"]["lse"])
 
 
+# ---------------------------------------------------- random shapes ---
+
+def _random_cases(n, seed):
+    """Seeded shapes spanning the API's combinations: dtype, head dim, batch, heads, ragged query
+    counts, 1-5 blocks of equal or uneven (possibly empty) lengths, packed V, the workgroup
+    shape, a separate merge and a non-default scale."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dt = "f32" if rng.random() < 0.25 else "bf16"
+        D = int(rng.choice([64, 128, 128]))
+        B, H = int(rng.choice([1, 1, 2, 3])), int(rng.integers(1, 5))
+        Sq = int(rng.choice([1, 2, 31, 33, 63, 65, 127, 129, 255, 257, int(rng.integers(1, 400))]))
+        nb = int(rng.integers(1, 6))
+        if rng.random() < 0.5:
+            lens = [int(rng.choice([1, 31, 64, 65, 128, 191, int(rng.integers(1, 400))]))] * nb
+        else:
+            lens = [int(rng.choice([0, 1, 17, 64, 129, int(rng.integers(0, 400))])) for _ in range(nb)]
+        if sum(lens) == 0:
+            lens[0] = 1
+        packed = dt == "bf16" and rng.random() < 0.5
+        waves = int(rng.choice([0, 0, 4, 8])) if dt == "bf16" else 0
+        sep = bool(rng.random() < 0.2)
+        scale = 1.0 / math.sqrt(D) if rng.random() < 0.8 else float(rng.uniform(0.02, 0.2))
+        cases.append((i, dt, D, B, H, Sq, tuple(lens), packed, waves, sep, scale, int(rng.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(40, 2026), ids=lambda c: f"r{c[0]}")
+def test_random_shapes(cp, case):
+    """Every element of out and LSE against the oracle's full attention over the concatenated
+    blocks (a full ring equals full attention), on seeded N(0,1) inputs of random shapes."""
+    i, dt, D, B, H, Sq, lens, packed, waves, sep, scale, seed = case
+    say(f"random#{i} {dt} B{B} H{H} D{D} Sq{Sq} lens{list(lens)} packed{int(packed)} waves{waves} "
+        f"sep{int(sep)} scale{scale:.4f}")
+    inp = workloads.make_custom(B, H, D, Sq, lens, dt, seed=seed)
+    q, k, v = dev(inp.q, dt), dev(inp.k, dt), dev(inp.v, dt)
+    offs = workloads.block_offsets(lens)
+    kb = [k[:, a:a + L] for a, L in zip(offs, lens)]
+    vb = [v[:, a:a + L] for a, L in zip(offs, lens)]
+    if packed:
+        vb = [cp.pack_v(x.contiguous()) for x in vb]
+    out, lse = cp.ring_attention(q, kb, vb, scale=scale, separate_merge=sep, waves=waves)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, scale)
+    assert_close("out", out.cpu().numpy(), o_ref, TOL[dt]["o"])
+    assert_close("lse", lse.cpu().numpy(), l_ref, TOL[dt]["lse"])
+
+
 # ------------------------------------------------------- graph capture ---
 
 def test_ring_and_backward_replay_in_a_graph(cp):
