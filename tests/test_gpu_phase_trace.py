@@ -1,0 +1,35 @@
+"""The tile-loop cycle accounting (bench.py --phase-trace, the diagnostic library) runs and
+reports a consistent breakdown: every wave of the 216 workgroups of the Ulysses-2 share's launch
+recorded its intervals, and a step takes at least the 64 MFMAs' 2048 cycles a SIMD issues in it."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_phase_trace_reports_every_interval():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from context_attention_dits_amd.build import PHASE_TRACE_LIB
+    if not os.path.exists(os.path.join(ROOT, "context_attention_dits_amd", PHASE_TRACE_LIB)):
+        pytest.skip("diagnostic library not built")
+    print("[case] bench.py --phase-trace (child process)", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--phase-trace"], capture_output=True,
+                       text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    rec = json.loads(r.stdout.strip().splitlines()[-1])["phase_trace"]
+    assert rec["workload"] == "flux1024_ulysses2_bf16" and rec["workgroups"] == 216
+    # 72 key tiles: 2 * 72 barriers per wave, the first three left out
+    assert rec["intervals_per_wave"] == 2 * 72 - 3
+    assert rec["cycles_per_step"] >= rec["mfma_cycles_per_simd_step"]
+    for k in rec["intervals"]:
+        for g in ("A", "B"):
+            assert k[g]["work"] > 0 and k[g]["wait"] >= 0
+            assert k[g]["work"] + k[g]["wait"] <= 1.5 * k["cycles"]
