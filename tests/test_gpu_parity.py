@@ -432,6 +432,71 @@ def test_concat_seq_bit_exact(cp, B, counts, Hg, D, dt):
     assert torch.equal(back, tb)
 
 
+def _random_layout_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = "f32" if rng.random() < 0.3 else "bf16"
+        D = int(rng.choice([8, 64, 128]))
+        B = int(rng.integers(1, 4))
+        P = int(rng.integers(1, 6))
+        S_l = int(rng.integers(1, 300))
+        Hg = int(rng.integers(1, 5))
+        counts = [int(c) for c in rng.integers(0, 6, size=P)]
+        if sum(counts) == 0:
+            counts[0] = 1
+        out.append((i, dt, D, B, P, S_l, Hg, tuple(counts), int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_layout_cases(24, 4242), ids=lambda c: f"r{c[0]}")
+def test_random_layouts_bit_exact(cp, case):
+    """Seeded random shapes for the three permutations (even regroup, uneven head packs, uneven
+    sequence joins), both directions, bit for bit against the oracle's index maps."""
+    i, dt, D, B, P, S_l, Hg, counts, seed = case
+    say(f"layouts#{i} {dt} D{D} B{B} P{P} S_l{S_l} Hg{Hg} counts{list(counts)}")
+    rng = np.random.default_rng(seed)
+    # even regroup: [B, S_l, P*Hg, D] <-> [B, P*S_l, Hg, D]
+    x = rng.standard_normal((B, S_l, P * Hg, D)).astype(np.float32)
+    if dt == "bf16":
+        x = workloads.round_to_bf16(x)
+    t = dev(x, dt)
+    y = torch.empty(B, P * S_l, Hg, D, dtype=t.dtype, device="cuda")
+    cp.cp_ulysses_regroup(t, y, P, cp.CP_REGROUP_SEQ_TO_HEAD)
+    back = torch.full_like(t, float("nan"))
+    cp.cp_ulysses_regroup(y, back, P, cp.CP_REGROUP_HEAD_TO_SEQ)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(y.float().cpu().numpy()), _bits(oracle.ulysses_regroup(x, P)))
+    assert torch.equal(back, t)
+    # uneven head packs: [B, S_l, sum(counts), D] <-> pieces of counts[g] heads
+    H = sum(counts)
+    x = rng.standard_normal((B, S_l, H, D)).astype(np.float32)
+    if dt == "bf16":
+        x = workloads.round_to_bf16(x)
+    t = dev(x, dt)
+    buf = torch.empty(t.numel(), dtype=t.dtype, device="cuda")
+    cp.cp_ulysses_pack_heads(t, buf, list(counts), cp.CP_REGROUP_SEQ_TO_HEAD)
+    back = torch.full_like(t, float("nan"))
+    cp.cp_ulysses_pack_heads(buf, back, list(counts), cp.CP_REGROUP_HEAD_TO_SEQ)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(buf.float().cpu().numpy()), _bits(oracle.ulysses_pack_heads(x, list(counts))))
+    assert torch.equal(back, t)
+    # uneven sequence joins: pieces of counts[r] tokens <-> [B, sum(counts), Hg, D]
+    S = sum(counts)
+    flat = rng.standard_normal(B * S * Hg * D).astype(np.float32)
+    if dt == "bf16":
+        flat = workloads.round_to_bf16(flat)
+    tb = dev(flat, dt)
+    yy = torch.empty((B, S, Hg, D), dtype=tb.dtype, device="cuda")
+    cp.cp_ulysses_concat_seq(tb, yy, list(counts), cp.CP_REGROUP_SEQ_TO_HEAD)
+    back = torch.full_like(tb, float("nan"))
+    cp.cp_ulysses_concat_seq(yy, back, list(counts), cp.CP_REGROUP_HEAD_TO_SEQ)
+    torch.cuda.synchronize()
+    want = oracle.ulysses_concat_seq(flat, B, list(counts), Hg, D)
+    assert np.array_equal(_bits(yy.float().cpu().numpy()), _bits(want))
+    assert torch.equal(back, tb)
+
+
 def _anything_gpu(cp, q, k, v, seq, heads, scale):
     """Every rank of an uneven Ulysses group on one GPU: the packs and the attention in the
     library, the two exchanges as device copies between the ranks' buffers (test scaffolding)."""
