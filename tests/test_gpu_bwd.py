@@ -163,6 +163,36 @@ def test_bwd_small_full_compare(cp, B, H, D, Sq, lens, seed):
     _check_all(f"bwd B{B} H{H} D{D} Sq{Sq}", inp, do, scale, got)
 
 
+def _random_bwd_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([64, 128, 128]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        Sq = int(rng.choice([1, 31, 33, 64, 97, 129, int(rng.integers(1, 320))]))
+        nb = int(rng.integers(1, 5))
+        lens = [int(rng.choice([0, 1, 32, 33, 100, int(rng.integers(0, 320))])) for _ in range(nb)]
+        if sum(lens) == 0:
+            lens[0] = 7
+        q_scale = float(rng.choice([1.0, 1.0, 3.0]))
+        cases.append((i, B, H, D, Sq, tuple(lens), q_scale, int(rng.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_bwd_cases(12, 777), ids=lambda c: f"r{c[0]}")
+def test_bwd_random_shapes(cp, case):
+    """Seeded random shapes (ragged, empty and one-key blocks, D = 64 and 128, some with Q scaled
+    by 3) against the oracle's gradients, every element within the derived bound."""
+    i, B, H, D, Sq, lens, q_scale, seed = case
+    say(f"bwd random#{i} B={B} H={H} D={D} Sq={Sq} blocks={list(lens)} q_scale={q_scale}")
+    inp = workloads.make_custom(B, H, D, Sq, lens, "bf16", seed=seed % 100000, q_scale=q_scale)
+    scale = 1.0 / np.sqrt(D)
+    do = workloads.grad_out((B, Sq, H, D), seed % 100000)
+    o, lse = _fwd_oracle(inp, scale)
+    got = _run(cp, inp, do, o, lse, scale)
+    _check_all(f"bwd random#{i}", inp, do, scale, got)
+
+
 def test_bwd_peaked_softmax(cp):
     """Q scaled by 4: rows dominated by a few keys (P near 0 and 1)."""
     B, H, D, Sq, lens = 1, 2, 128, 160, (96, 96)
