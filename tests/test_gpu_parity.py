@@ -186,6 +186,27 @@ def test_zero_length_blocks(cp):
     assert torch.all(out == 0).item() and torch.all(torch.isneginf(lse)).item()
 
 
+@pytest.mark.parametrize("dt,packed,lens", [("bf16", True, (64,) * 18), ("bf16", False, (40, 0, 130) * 6 + (7,)),
+                                             ("f32", False, (16,) * 20), ("bf16", True, (300,) * 17)])
+def test_rings_beyond_sixteen_blocks(cp, dt, packed, lens):
+    """Rings longer than the one-launch forms take (16 blocks) run block by block and still equal
+    full attention over every block's keys."""
+    B, H, D, Sq = 1, 3, 128, 200
+    say(f"ring of {len(lens)} blocks, {dt}, packed {packed}")
+    inp = workloads.make_custom(B, H, D, Sq, lens, dt, seed=90 + len(lens))
+    q, k, v = dev(inp.q, dt), dev(inp.k, dt), dev(inp.v, dt)
+    offs = workloads.block_offsets(lens)
+    kb = [k[:, a:a + L] for a, L in zip(offs, lens)]
+    vb = [v[:, a:a + L] for a, L in zip(offs, lens)]
+    if packed:
+        vb = [cp.pack_v(x.contiguous()) for x in vb]
+    out, lse = cp.ring_attention(q, kb, vb, scale=inp.workload.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(inp.q, inp.k, inp.v, inp.workload.scale)
+    assert_close("out", out.cpu().numpy(), o_ref, TOL[dt]["o"])
+    assert_close("lse", lse.cpu().numpy(), l_ref, TOL[dt]["lse"])
+
+
 @pytest.mark.parametrize("waves", SHAPES)
 def test_strided_views(cp, waves):
     """Q, K/V and out as non-contiguous views (heads interleaved in wider buffers)."""
