@@ -89,7 +89,8 @@ def parse():
     ap.add_argument("--phase-trace", action="store_true",
                     help="instead of the benchmark: load the diagnostic library (libcpattn_phase.so) and "
                          "print the core-clock cycles of the block kernel's tile-loop intervals for the "
-                         "workload's one-block launch (8-wave shape)")
+                         "workload's one-block launch (8-wave shape), and those of a synthetic ping-pong "
+                         "with the loop's instruction mix")
     return ap.parse_args()
 
 
@@ -613,7 +614,31 @@ def phase_trace(prob, warm_seconds: float = 0.5) -> dict:
     step = sum(k["cycles"] for k in kinds)
     return {"workload": w.name, "traced_launch_us": round(e0.elapsed_time(e1) * 1e3, 2), "workgroups": n_wg,
             "intervals_per_wave": int(np.median(count)), "cycles_per_step": step,
-            "mfma_cycles_per_simd_step": 64 * 32, "intervals": kinds}
+            "mfma_cycles_per_simd_step": 64 * 32, "intervals": kinds, "synthetic_mix": mix_probe(lib)}
+
+
+MIX_VARIANTS = ("as_the_loop", "mfma_16x16x32", "fragments_in_registers", "groups_in_phase")
+
+
+def mix_probe(lib, iters: int = 4000) -> dict:
+    """The diagnostic library's synthetic ping-pong (cp_debug_mix_probe): the tile loop's interval
+    structure and instruction mix on random bf16 with no memory traffic, 8 waves on each of the 256
+    compute units. Per variant, the mean core-clock cycles of one interval (one group's matrix half,
+    the other's softmax half, one barrier) and the milliseconds of the timed launch of `iters`
+    intervals. Variants: as the loop does it; the same flops as twice as many 16x16x32 MFMAs; the
+    fragments taken from registers instead of LDS; both groups in the same phase."""
+    import ctypes
+    lib.cp_debug_mix_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_double)]
+    lib.cp_debug_mix_probe.restype = ctypes.c_int
+    res = {}
+    for v, name in enumerate(MIX_VARIANTS):
+        cyc, ms = ctypes.c_double(), ctypes.c_double()
+        st = lib.cp_debug_mix_probe(v, iters, ctypes.byref(cyc), ctypes.byref(ms))
+        if st != 0:
+            raise SystemExit(f"cp_debug_mix_probe({v}) failed ({st})")
+        res[name] = {"cycles_per_interval": round(cyc.value, 1), "ms": round(ms.value, 3)}
+    return res
 
 
 def main():

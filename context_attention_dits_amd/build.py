@@ -47,12 +47,15 @@ def hipcc() -> str:
 RING_WAIT_TEST_LIB = "libcpattn_ringwait_test.so"
 RING_WAIT_TEST_DEFINES = {"CP_RING_TEST_NEVER_READY": "1"}
 # A diagnostic library: the block kernel's one-block launch also records the core-clock cycles of
-# its tile-loop intervals (work, wait for tile loads, barrier wait; cp_debug_phase_trace, which the
-# C ABI header does not declare). bench.py --phase-trace loads it.
+# its tile-loop intervals (work, wait for tile loads, barrier wait; cp_debug_phase_trace), and a
+# synthetic ping-pong with the tile loop's instruction mix and no memory traffic is added
+# (cp_debug_mix_probe); the C ABI header declares neither. bench.py --phase-trace loads it.
 PHASE_TRACE_LIB = "libcpattn_phase.so"
 PHASE_TRACE_DEFINES = {"CP_FWD_PHASE_TRACE": "1"}
 # Libraries built next to the main one with only the forward kernel recompiled: name -> defines.
 VARIANT_LIBS = {RING_WAIT_TEST_LIB: RING_WAIT_TEST_DEFINES, PHASE_TRACE_LIB: PHASE_TRACE_DEFINES}
+# Sources only a variant library links in: name -> sources.
+VARIANT_EXTRA_SOURCES = {PHASE_TRACE_LIB: ["diag_mix.hip"]}
 
 
 def build(out: Optional[str] = None, defines: Optional[Dict[str, str]] = None,
@@ -91,16 +94,20 @@ def build(out: Optional[str] = None, defines: Optional[Dict[str, str]] = None,
     # the variant libraries need only the forward kernel recompiled with their defines
     with_variants = test_libs and not defines
 
-    def compile_variant(name: str) -> str:
+    def compile_variant(name: str) -> List[str]:
+        """The variant's forward kernel object, then its extra sources' objects."""
         vdir = os.path.join(PKG, "_build", name.replace(".so", ""))
         os.makedirs(vdir, exist_ok=True)
-        obj = os.path.join(vdir, "attn_fwd_bf16.o")
         df = [f"-D{k}={v}" for k, v in sorted(VARIANT_LIBS[name].items())]
-        cmd = [cc, *HIPCC_FLAGS, *df, "-c", os.path.join(CSRC, "attn_fwd_bf16.hip"), "-o", obj]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed for attn_fwd_bf16.hip ({name} build):\n{r.stderr}")
-        return obj
+        objs = []
+        for src in ["attn_fwd_bf16.hip", *VARIANT_EXTRA_SOURCES.get(name, [])]:
+            obj = os.path.join(vdir, src.replace(".hip", ".o"))
+            cmd = [cc, *HIPCC_FLAGS, *df, "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {src} ({name} build):\n{r.stderr}")
+            objs.append(obj)
+        return objs
 
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + len(VARIANT_LIBS), os.cpu_count() or 4)) as ex:
         futs = [ex.submit(compile_one, src) for src in SOURCES]
@@ -108,8 +115,8 @@ def build(out: Optional[str] = None, defines: Optional[Dict[str, str]] = None,
         objs = [f.result() for f in futs]
         var_objs = {n: f.result() for n, f in var_futs.items()}
     link(objs, out)
-    for name, vobj in var_objs.items():
-        link([vobj if os.path.basename(o) == "attn_fwd_bf16.o" else o for o in objs],
+    for name, vobjs in var_objs.items():
+        link([vobjs[0] if os.path.basename(o) == "attn_fwd_bf16.o" else o for o in objs] + vobjs[1:],
              os.path.join(os.path.dirname(out), name))
     return out
 

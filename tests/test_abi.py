@@ -35,8 +35,9 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_phase_trace_only_in_the_diagnostic_library(lib):
-    """The tile-loop cycle trace (bench.py --phase-trace) lives in its own library; the main one
-    has neither the symbol nor the instrumentation's device buffer."""
+    """The tile-loop cycle trace (bench.py --phase-trace) and the synthetic ping-pong beside it
+    live in their own library; the main one has neither the symbols nor the instrumentation's
+    device buffer."""
     from context_attention_dits_amd.build import PHASE_TRACE_LIB
     assert not hasattr(lib, "cp_debug_phase_trace")
     path = os.path.join(os.path.dirname(_lib.DEFAULT_PATH), PHASE_TRACE_LIB)
@@ -51,6 +52,15 @@ def test_phase_trace_only_in_the_diagnostic_library(lib):
     buf = (ctypes.c_ulonglong * 1)()
     assert diag.cp_debug_phase_trace(ctypes.addressof(buf), -1) != 0
     assert diag.cp_debug_phase_trace(ctypes.addressof(buf), 1 << 40) != 0
+    # the synthetic ping-pong beside it: argument checks only
+    assert not hasattr(lib, "cp_debug_mix_probe")
+    diag.cp_debug_mix_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    diag.cp_debug_mix_probe.restype = ctypes.c_int
+    cyc, ms = ctypes.c_double(), ctypes.c_double()
+    for v, it, a, b in ((4, 100, cyc, ms), (-1, 100, cyc, ms), (0, 1, cyc, ms), (0, 1 << 21, cyc, ms)):
+        assert diag.cp_debug_mix_probe(v, it, ctypes.addressof(a), ctypes.addressof(b)) != 0
+    assert diag.cp_debug_mix_probe(0, 100, None, ctypes.addressof(ms)) != 0
+    assert diag.cp_debug_mix_probe(0, 100, ctypes.addressof(cyc), None) != 0
 
 
 def _block(lib, dtype=1, B=1, H=2, D=128, Sq=8, Skv=8, scale=0.1, flags=0, q=FAKE, k=FAKE, v=FAKE,
