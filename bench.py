@@ -617,7 +617,8 @@ def phase_trace(prob, warm_seconds: float = 0.5) -> dict:
             "mfma_cycles_per_simd_step": 64 * 32, "intervals": kinds, "synthetic_mix": mix_probe(lib)}
 
 
-MIX_VARIANTS = ("as_the_loop", "mfma_16x16x32", "fragments_in_registers", "groups_in_phase")
+MIX_VARIANTS = ("as_the_loop", "mfma_16x16x32", "fragments_in_registers", "groups_in_phase",
+                "fragment_reads_only", "fragment_reads_only_all_waves")
 
 
 def mix_probe(lib, iters: int = 4000) -> dict:
@@ -626,7 +627,9 @@ def mix_probe(lib, iters: int = 4000) -> dict:
     compute units. Per variant, the mean core-clock cycles of one interval (one group's matrix half,
     the other's softmax half, one barrier) and the milliseconds of the timed launch of `iters`
     intervals. Variants: as the loop does it; the same flops as twice as many 16x16x32 MFMAs; the
-    fragments taken from registers instead of LDS; both groups in the same phase."""
+    fragments taken from registers instead of LDS; both groups in the same phase; the matrix
+    half's 32 LDS fragment reads alone (no MFMAs, the other group idle); those reads by all 8
+    waves in every interval."""
     import ctypes
     lib.cp_debug_mix_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_double)]

@@ -8,7 +8,9 @@
 // other group a softmax half over 32 values per lane (maxima, FMA, exp2, sums, bf16
 // conversion); then a workgroup barrier. Variants: 0 as described; 1 the same flops as twice as
 // many 16x16x32 MFMAs; 2 fragments taken from registers instead of LDS; 3 both groups in the
-// same phase instead of ping-pong.
+// same phase instead of ping-pong; 4 the matrix half's 32 fragment reads alone (all issued
+// before their results are used, no MFMAs; the other group idles); 5 as 4 with all 8 waves
+// reading in every interval.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -18,6 +20,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWgs = 256, kThreads = 512, kFrags = 32;
 
@@ -37,13 +40,23 @@ __global__ void __launch_bounds__(kThreads) mix_kernel(const bf16x8* __restrict_
   float x[32];
   for (int i = 0; i < 32; ++i) x[i] = (float)mine[(tid * 7 + i) % (kFrags * 64)][i & 7];
   __syncthreads();
-  const int grp = VARIANT == 3 ? 0 : (wave >> 2);
+  const int grp = (VARIANT == 3 || VARIANT == 5) ? 0 : (wave >> 2);
+  u32x4 rd = {0u, 0u, 0u, 0u};
   f32x16 o32[4] = {}, s32[2] = {};
   f32x4 o16[16] = {}, s16[8] = {};
   float m = 0.f, l = 0.f;
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
   for (int it = 0; it < iters; ++it) {
-    if (((it + grp) & 1) == 0) {
+    if (VARIANT >= 4) {
+      if (VARIANT == 5 || ((it + grp) & 1) == 0) {
+        const int rot = (it & 7) * 64;  // the addresses move a little from one interval to the next
+        bf16x8 r[kFrags];
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) r[f] = frag[((f * 64 + rot) & (kFrags * 64 - 1)) + lane];
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) rd ^= __builtin_bit_cast(u32x4, r[f]);
+      }
+    } else if (((it + grp) & 1) == 0) {
       if (VARIANT == 1) {
 #pragma unroll
         for (int f = 0; f < 16; ++f) {
@@ -98,7 +111,7 @@ __global__ void __launch_bounds__(kThreads) mix_kernel(const bf16x8* __restrict_
     __syncthreads();
   }
   const unsigned long long t1 = __builtin_amdgcn_s_memtime();
-  float sink = l + m;
+  float sink = l + m + (float)(rd[0] ^ rd[1] ^ rd[2] ^ rd[3]);
   for (int i = 0; i < 16; ++i) sink += VARIANT == 1 ? o16[i][0] + o16[i][3] : o32[i >> 2][i & 15] + o32[3][i];
   pad[tid] = (char)sink;
   __syncthreads();
@@ -108,11 +121,11 @@ __global__ void __launch_bounds__(kThreads) mix_kernel(const bf16x8* __restrict_
 
 }  // namespace
 
-// Runs variant `variant` (0-3, see above) for `iters` intervals after one untimed launch and
+// Runs variant `variant` (0-5, see above) for `iters` intervals after one untimed launch and
 // returns the mean core-clock cycles per interval (s_memtime, every wave) and the timed
 // launch's milliseconds. Allocates and frees its own device buffers; blocks until done.
 extern "C" int cp_debug_mix_probe(int variant, int iters, double* cycles_per_interval, double* ms) {
-  if (variant < 0 || variant > 3 || iters < 2 || iters > (1 << 20) || !cycles_per_interval || !ms)
+  if (variant < 0 || variant > 5 || iters < 2 || iters > (1 << 20) || !cycles_per_interval || !ms)
     return (int)hipErrorInvalidValue;
   const size_t n_src = (size_t)kWgs * kFrags * 64;
   bf16x8* src = nullptr;
@@ -144,7 +157,9 @@ extern "C" int cp_debug_mix_probe(int variant, int iters, double* cycles_per_int
       case 0: hipLaunchKernelGGL(mix_kernel<0>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
       case 1: hipLaunchKernelGGL(mix_kernel<1>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
       case 2: hipLaunchKernelGGL(mix_kernel<2>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
-      default: hipLaunchKernelGGL(mix_kernel<3>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
+      case 3: hipLaunchKernelGGL(mix_kernel<3>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
+      case 4: hipLaunchKernelGGL(mix_kernel<4>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
+      default: hipLaunchKernelGGL(mix_kernel<5>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
     }
     e = hipGetLastError();
     if (e == hipSuccess) e = hipEventRecord(e1, 0);

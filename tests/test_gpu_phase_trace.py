@@ -1,8 +1,8 @@
 """The tile-loop cycle accounting (bench.py --phase-trace, the diagnostic library) runs and
 reports a consistent breakdown: every wave of the 216 workgroups of the Ulysses-2 share's launch
 recorded its intervals, and a step takes at least the 64 MFMAs' 2048 cycles a SIMD issues in it.
-The synthetic ping-pong beside it reports each variant, every interval again at least the 32 MFMAs'
-1024 cycles a SIMD issues per interval on average."""
+The synthetic ping-pong beside it reports each variant, every interval with MFMAs again at least
+the 32 MFMAs' 1024 cycles a SIMD issues per interval on average."""
 import json
 import os
 import subprocess
@@ -36,6 +36,11 @@ def test_phase_trace_reports_every_interval():
             assert k[g]["work"] > 0 and k[g]["wait"] >= 0
             assert k[g]["work"] + k[g]["wait"] <= 1.5 * k["cycles"]
     mix = rec["synthetic_mix"]
-    assert set(mix) == {"as_the_loop", "mfma_16x16x32", "fragments_in_registers", "groups_in_phase"}
-    for v in mix.values():
-        assert v["cycles_per_interval"] >= 1024 and v["ms"] > 0
+    assert set(mix) == {"as_the_loop", "mfma_16x16x32", "fragments_in_registers", "groups_in_phase",
+                        "fragment_reads_only", "fragment_reads_only_all_waves"}
+    for name, v in mix.items():
+        assert v["ms"] > 0
+        if "reads_only" not in name:
+            assert v["cycles_per_interval"] >= 1024
+    # the reads of all 8 waves take longer than those of 4
+    assert mix["fragment_reads_only_all_waves"]["cycles_per_interval"] > mix["fragment_reads_only"]["cycles_per_interval"]
