@@ -618,7 +618,8 @@ def phase_trace(prob, warm_seconds: float = 0.5) -> dict:
 
 
 MIX_VARIANTS = ("as_the_loop", "mfma_16x16x32", "fragments_in_registers", "groups_in_phase",
-                "fragment_reads_only", "fragment_reads_only_all_waves")
+                "fragment_reads_only", "fragment_reads_only_all_waves", "8_reads_one_half_early",
+                "16_reads_one_half_early")
 
 
 def mix_probe(lib, iters: int = 4000) -> dict:
@@ -629,7 +630,8 @@ def mix_probe(lib, iters: int = 4000) -> dict:
     intervals. Variants: as the loop does it; the same flops as twice as many 16x16x32 MFMAs; the
     fragments taken from registers instead of LDS; both groups in the same phase; the matrix
     half's 32 LDS fragment reads alone (no MFMAs, the other group idle); those reads by all 8
-    waves in every interval."""
+    waves in every interval; as the loop with 8 or 16 of a matrix half's fragment reads issued
+    during the wave's preceding softmax half (into registers the loop does not have to spare)."""
     import ctypes
     lib.cp_debug_mix_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_double)]

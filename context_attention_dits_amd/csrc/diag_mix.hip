@@ -10,7 +10,8 @@
 // many 16x16x32 MFMAs; 2 fragments taken from registers instead of LDS; 3 both groups in the
 // same phase instead of ping-pong; 4 the matrix half's 32 fragment reads alone (all issued
 // before their results are used, no MFMAs; the other group idles); 5 as 4 with all 8 waves
-// reading in every interval.
+// reading in every interval; 6 and 7 as 0 with the first 8 or 16 of a matrix half's fragment
+// reads issued by the wave during its preceding softmax half, into registers it keeps for them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -44,10 +45,13 @@ __global__ void __launch_bounds__(kThreads) mix_kernel(const bf16x8* __restrict_
   u32x4 rd = {0u, 0u, 0u, 0u};
   f32x16 o32[4] = {}, s32[2] = {};
   f32x4 o16[16] = {}, s16[8] = {};
+  constexpr int R = VARIANT == 6 ? 8 : VARIANT == 7 ? 16 : 0;  // fragments read one half early
+  bf16x8 early[R > 0 ? R : 1];
+  for (int i = 0; i < (R > 0 ? R : 1); ++i) early[i] = q[i & 3];
   float m = 0.f, l = 0.f;
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
   for (int it = 0; it < iters; ++it) {
-    if (VARIANT >= 4) {
+    if (VARIANT == 4 || VARIANT == 5) {
       if (VARIANT == 5 || ((it + grp) & 1) == 0) {
         const int rot = (it & 7) * 64;  // the addresses move a little from one interval to the next
         bf16x8 r[kFrags];
@@ -75,16 +79,20 @@ __global__ void __launch_bounds__(kThreads) mix_kernel(const bf16x8* __restrict_
       } else {
 #pragma unroll
         for (int f = 0; f < 16; ++f) {
-          const bf16x8 a = VARIANT == 2 ? q[(f + 1) & 3] : frag[f * 64 + lane];
+          const bf16x8 a = VARIANT == 2 ? q[(f + 1) & 3] : f < R ? early[f < R ? f : 0] : frag[f * 64 + lane];
           s32[f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[f & 3], s32[f & 1], 0, 0, 0);
         }
 #pragma unroll
         for (int f = 0; f < 16; ++f) {
-          const bf16x8 a = VARIANT == 2 ? q[(f + 2) & 3] : frag[(16 + f) * 64 + lane];
+          const bf16x8 a = VARIANT == 2 ? q[(f + 2) & 3]
+                           : 16 + f < R ? early[16 + f < R ? 16 + f : 0] : frag[(16 + f) * 64 + lane];
           o32[f >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[f & 3], o32[f >> 2], 0, 0, 0);
         }
       }
     } else {
+      const int rot = (it & 7) * 64;
+#pragma unroll
+      for (int f = 0; f < R; ++f) early[f] = frag[((f * 64 + rot) & (kFrags * 64 - 1)) + lane];
       float mx0 = x[0], mx1 = x[1];
 #pragma unroll
       for (int i = 2; i < 32; i += 2) {
@@ -112,6 +120,7 @@ __global__ void __launch_bounds__(kThreads) mix_kernel(const bf16x8* __restrict_
   }
   const unsigned long long t1 = __builtin_amdgcn_s_memtime();
   float sink = l + m + (float)(rd[0] ^ rd[1] ^ rd[2] ^ rd[3]);
+  for (int i = 0; i < (R > 0 ? R : 1); ++i) sink += (float)early[i][i & 7];
   for (int i = 0; i < 16; ++i) sink += VARIANT == 1 ? o16[i][0] + o16[i][3] : o32[i >> 2][i & 15] + o32[3][i];
   pad[tid] = (char)sink;
   __syncthreads();
@@ -121,11 +130,11 @@ __global__ void __launch_bounds__(kThreads) mix_kernel(const bf16x8* __restrict_
 
 }  // namespace
 
-// Runs variant `variant` (0-5, see above) for `iters` intervals after one untimed launch and
+// Runs variant `variant` (0-7, see above) for `iters` intervals after one untimed launch and
 // returns the mean core-clock cycles per interval (s_memtime, every wave) and the timed
 // launch's milliseconds. Allocates and frees its own device buffers; blocks until done.
 extern "C" int cp_debug_mix_probe(int variant, int iters, double* cycles_per_interval, double* ms) {
-  if (variant < 0 || variant > 5 || iters < 2 || iters > (1 << 20) || !cycles_per_interval || !ms)
+  if (variant < 0 || variant > 7 || iters < 2 || iters > (1 << 20) || !cycles_per_interval || !ms)
     return (int)hipErrorInvalidValue;
   const size_t n_src = (size_t)kWgs * kFrags * 64;
   bf16x8* src = nullptr;
@@ -159,7 +168,9 @@ extern "C" int cp_debug_mix_probe(int variant, int iters, double* cycles_per_int
       case 2: hipLaunchKernelGGL(mix_kernel<2>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
       case 3: hipLaunchKernelGGL(mix_kernel<3>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
       case 4: hipLaunchKernelGGL(mix_kernel<4>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
-      default: hipLaunchKernelGGL(mix_kernel<5>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
+      case 5: hipLaunchKernelGGL(mix_kernel<5>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
+      case 6: hipLaunchKernelGGL(mix_kernel<6>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
+      default: hipLaunchKernelGGL(mix_kernel<7>, dim3(kWgs), dim3(kThreads), 0, 0, src, out, iters, ticks); break;
     }
     e = hipGetLastError();
     if (e == hipSuccess) e = hipEventRecord(e1, 0);

@@ -57,7 +57,7 @@ def test_phase_trace_only_in_the_diagnostic_library(lib):
     diag.cp_debug_mix_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     diag.cp_debug_mix_probe.restype = ctypes.c_int
     cyc, ms = ctypes.c_double(), ctypes.c_double()
-    for v, it, a, b in ((6, 100, cyc, ms), (-1, 100, cyc, ms), (0, 1, cyc, ms), (0, 1 << 21, cyc, ms)):
+    for v, it, a, b in ((8, 100, cyc, ms), (-1, 100, cyc, ms), (0, 1, cyc, ms), (0, 1 << 21, cyc, ms)):
         assert diag.cp_debug_mix_probe(v, it, ctypes.addressof(a), ctypes.addressof(b)) != 0
     assert diag.cp_debug_mix_probe(0, 100, None, ctypes.addressof(ms)) != 0
     assert diag.cp_debug_mix_probe(0, 100, ctypes.addressof(cyc), None) != 0

@@ -37,7 +37,8 @@ def test_phase_trace_reports_every_interval():
             assert k[g]["work"] + k[g]["wait"] <= 1.5 * k["cycles"]
     mix = rec["synthetic_mix"]
     assert set(mix) == {"as_the_loop", "mfma_16x16x32", "fragments_in_registers", "groups_in_phase",
-                        "fragment_reads_only", "fragment_reads_only_all_waves"}
+                        "fragment_reads_only", "fragment_reads_only_all_waves", "8_reads_one_half_early",
+                        "16_reads_one_half_early"}
     for name, v in mix.items():
         assert v["ms"] > 0
         if "reads_only" not in name:
